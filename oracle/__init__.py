@@ -1,0 +1,176 @@
+"""fp64 CPU oracle for split-K paged-attention decode (ctypes over liboracle.so).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the product path (the HIP library
+and its Python binding) never does, and shares no code with it.
+
+Every function follows a definition stated in oracle.c's header:
+  build_page_table  -- sglang fused metadata kernel docstring (page_table,
+                       cache_seqlens, cu_seqlens_k by definition);
+  paged_attention   -- plain softmax attention of one query token over the
+                       paged KV cache (lmdeploy's split-K decode computes this
+                       exactly, split-K being a reformulation);
+  split_partials    -- per-split (max, sum, unnormalised accumulator) state;
+  split_merge       -- log-sum-exp merge of that state.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+KV_BF16 = 0
+KV_INT8 = 1
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_F32 = ctypes.c_float
+_INT = ctypes.c_int
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _b
+        _b.build(verbose=False)
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.oracle_build_page_table.argtypes = [_P, _I64, _P, _P, _I32, _I32, _I32, _I32, _P, _I64,
+                                            _P, _P]
+    lib.oracle_build_page_table.restype = _INT
+    att = [_P, _P, _P, _P, _P, _INT, _P, _I64, _P, _INT, _INT, _INT, _INT, _INT, _F32]
+    lib.oracle_paged_attention.argtypes = att + [_P, _P]
+    lib.oracle_paged_attention.restype = _INT
+    lib.oracle_split_partials.argtypes = att + [_INT, _P, _P, _P]
+    lib.oracle_split_partials.restype = _INT
+    lib.oracle_split_merge.argtypes = [_P, _P, _P, _INT, _INT, _INT, _INT, _P, _P]
+    lib.oracle_split_merge.restype = _INT
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def build_page_table(req_to_token, req_pool_indices, seq_lens, page_size, max_seq_pages,
+                     seqlen_offset=0, page_table=None):
+    """Returns (page_table [bs, stride] int32, cache_seqlens [bs], cu_seqlens_k [bs+1]).
+
+    If ``page_table`` is given it is updated in place (columns >= max_seq_pages
+    are left as they are) and its row stride is used."""
+    lib = _load()
+    r2t = _c(req_to_token, np.int32)
+    rpi = _c(req_pool_indices, np.int32)
+    sl = _c(seq_lens, np.int32)
+    bs = int(rpi.shape[0])
+    if page_table is None:
+        page_table = np.full((bs, max(1, max_seq_pages)), -0x5A5A5A5A, dtype=np.int32)
+    assert page_table.dtype == np.int32 and page_table.flags.c_contiguous
+    # poisoned so that an unwritten output entry shows up
+    cache = np.full(bs, -0x5A5A5A5A, dtype=np.int32)
+    cu = np.full(bs + 1, -0x5A5A5A5A, dtype=np.int32)
+    rc = lib.oracle_build_page_table(_ptr(r2t), r2t.shape[1], _ptr(rpi), _ptr(sl), bs,
+                                     int(seqlen_offset), int(page_size), int(max_seq_pages),
+                                     _ptr(page_table), page_table.shape[1], _ptr(cache), _ptr(cu))
+    if rc != 0:
+        raise ValueError("oracle_build_page_table: invalid arguments")
+    return page_table, cache, cu
+
+
+def _att_args(q, k_pages, v_pages, k_scales, v_scales, kv_dtype, page_table, seq_lens,
+              num_kv_heads, page_size, scale):
+    q = _c(q, np.uint16)
+    B, Hq, D = q.shape
+    if kv_dtype in ("bf16", KV_BF16):
+        kd = KV_BF16
+        k = _c(k_pages, np.uint16)
+        v = _c(v_pages, np.uint16)
+        ks = vs = None
+    else:
+        kd = KV_INT8
+        k = _c(k_pages, np.int8)
+        v = _c(v_pages, np.int8)
+        ks = _c(k_scales, np.float32)
+        vs = _c(v_scales, np.float32)
+    pt = _c(page_table, np.int32)
+    sl = _c(seq_lens, np.int32)
+    keep = (q, k, v, ks, vs, pt, sl)
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(ks), _ptr(vs), kd, _ptr(pt), pt.shape[1], _ptr(sl),
+            B, Hq, int(num_kv_heads), D, int(page_size), float(np.float32(scale))]
+    return keep, args, (B, Hq, D)
+
+
+def paged_attention(q, k_pages, v_pages, page_table, seq_lens, *, num_kv_heads, page_size,
+                    scale, kv_dtype="bf16", k_scales=None, v_scales=None):
+    """fp64 out [B, Hq, D] and lse [B, Hq] by the plain definition."""
+    lib = _load()
+    keep, args, (B, Hq, D) = _att_args(q, k_pages, v_pages, k_scales, v_scales, kv_dtype,
+                                       page_table, seq_lens, num_kv_heads, page_size, scale)
+    out = np.full((B, Hq, D), np.nan, dtype=np.float64)
+    lse = np.full((B, Hq), np.nan, dtype=np.float64)
+    rc = lib.oracle_paged_attention(*args, _ptr(out), _ptr(lse))
+    del keep
+    if rc != 0:
+        raise ValueError("oracle_paged_attention: invalid arguments")
+    return out, lse
+
+
+def split_partials(q, k_pages, v_pages, page_table, seq_lens, *, num_kv_heads, page_size,
+                   scale, num_splits, kv_dtype="bf16", k_scales=None, v_scales=None):
+    """fp64 per-split state: acc [B, Hq, S, D], m [B, Hq, S], l [B, Hq, S]."""
+    lib = _load()
+    keep, args, (B, Hq, D) = _att_args(q, k_pages, v_pages, k_scales, v_scales, kv_dtype,
+                                       page_table, seq_lens, num_kv_heads, page_size, scale)
+    S = int(num_splits)
+    acc = np.full((B, Hq, S, D), np.nan, dtype=np.float64)
+    m = np.full((B, Hq, S), np.nan, dtype=np.float64)
+    l = np.full((B, Hq, S), np.nan, dtype=np.float64)
+    rc = lib.oracle_split_partials(*args, S, _ptr(acc), _ptr(m), _ptr(l))
+    del keep
+    if rc != 0:
+        raise ValueError("oracle_split_partials: invalid arguments")
+    return acc, m, l
+
+
+def split_merge(acc, m, l):
+    """Log-sum-exp merge; inputs acc [B, Hq, S, D], m/l [B, Hq, S] (any float dtype)."""
+    lib = _load()
+    acc = _c(acc, np.float64)
+    m = _c(m, np.float64)
+    l = _c(l, np.float64)
+    B, Hq, S, D = acc.shape
+    out = np.full((B, Hq, D), np.nan, dtype=np.float64)
+    lse = np.full((B, Hq), np.nan, dtype=np.float64)
+    rc = lib.oracle_split_merge(_ptr(acc), _ptr(m), _ptr(l), B, Hq, D, S, _ptr(out), _ptr(lse))
+    if rc != 0:
+        raise ValueError("oracle_split_merge: invalid arguments")
+    return out, lse
+
+
+def case_attention(case, page_table=None):
+    """Oracle attention for a workloads.DecodeCase.  Uses the case's own page
+    placement unless a page table is given."""
+    pt = case.page_list if page_table is None else page_table
+    return paged_attention(case.q, case.k_pages, case.v_pages, pt, case.seq_lens,
+                           num_kv_heads=case.num_kv_heads, page_size=case.page_size,
+                           scale=case.scale, kv_dtype=case.kv_dtype,
+                           k_scales=case.k_scales, v_scales=case.v_scales)
+
+
+def case_page_table(case, max_seq_pages=None, seqlen_offset=None):
+    msp = case.max_seq_pages if max_seq_pages is None else max_seq_pages
+    off = case.seqlen_offset if seqlen_offset is None else seqlen_offset
+    return build_page_table(case.req_to_token, case.req_pool_indices, case.seq_lens,
+                            case.page_size, msp, seqlen_offset=off)

@@ -1,0 +1,38 @@
+"""Dense numpy brute force used to pin the oracle.
+
+It works on the generator's LOGICAL rows (DecodeCase.dense_kv: the rows in
+token order, from the generator's own page placement), so it never touches a
+page table or does any page arithmetic, and it uses numpy matrix products
+and scipy's logsumexp/softmax instead of the oracle's loops."""
+import numpy as np
+from scipy.special import logsumexp, softmax
+
+from workloads import bf16_bits_to_f32
+
+
+def dequant_rows(k, ks):
+    if ks is None:
+        return bf16_bits_to_f32(k).astype(np.float64)
+    return k.astype(np.float64) * ks.astype(np.float64)[..., None]
+
+
+def dense_attention(case):
+    B, Hq, D = case.q.shape
+    G = case.group
+    out = np.zeros((B, Hq, D))
+    lse = np.zeros((B, Hq))
+    qf = bf16_bits_to_f32(case.q).astype(np.float64)
+    for b in range(B):
+        k, v, ks, vs = case.dense_kv(b)
+        K = dequant_rows(k, ks)   # [L, Hkv, D]
+        V = dequant_rows(v, vs)
+        L = K.shape[0]
+        for h in range(Hq):
+            if L == 0:
+                lse[b, h] = -np.inf
+                continue
+            s = float(case.scale) * (K[:, h // G, :] @ qf[b, h])
+            w = softmax(s)
+            out[b, h] = w @ V[:, h // G, :]
+            lse[b, h] = logsumexp(s)
+    return out, lse

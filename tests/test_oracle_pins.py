@@ -1,0 +1,315 @@
+"""Pins for the fp64 oracle (CPU only).
+
+Each test ties the oracle to something other than itself: hand-worked
+closed forms (tests/golden), a dense numpy/scipy brute force that never uses
+a page table, exact special cases, and invariances the mathematics fixes
+(split count, physical page placement, key order, GQA grouping)."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from tests.brute import dense_attention
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _bits(x):
+    return W.f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+def _ev(expr):
+    return eval(expr, {"e": math.e, "log": math.log, "__builtins__": {}})
+
+
+# ---------------------------------------------------------------- metadata
+
+def test_metadata_golden_hand_example():
+    g = json.load(open(os.path.join(GOLDEN, "metadata_tiny.json")))
+    pt = np.array(g["page_table_preset"], dtype=np.int32)
+    pt, cache, cu = oracle.build_page_table(
+        np.array(g["req_to_token"], np.int32), np.array(g["req_pool_indices"], np.int32),
+        np.array(g["seq_lens"], np.int32), g["page_size"], g["max_seq_pages"],
+        seqlen_offset=g["seqlen_offset"], page_table=pt)
+    assert pt.tolist() == g["expect_page_table"]
+    assert cache.tolist() == g["expect_cache_seqlens"]
+    assert cu.tolist() == g["expect_cu_seqlens_k"]
+
+
+def test_metadata_bs0_is_noop():
+    pt, cache, cu = oracle.build_page_table(np.zeros((1, 8), np.int32), np.zeros(0, np.int32),
+                                            np.zeros(0, np.int32), 4, 2)
+    # the launcher returns before writing anything when bs == 0
+    assert pt.shape[0] == 0 and cache.shape == (0,) and cu.tolist() == [-0x5A5A5A5A]
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_metadata_inverts_generator_placement(cfg):
+    """For page-aligned maps, page_table[i, t // P] * P + t % P must give back
+    req_to_token[rpi[i], t] for every t < L_i, and used columns must equal the
+    generator's own page placement (which built req_to_token the other way)."""
+    c = W.make_config(cfg)
+    pt, cache, cu = oracle.case_page_table(c)
+    P = c.page_size
+    for i in range(c.batch):
+        L = int(c.seq_lens[i])
+        t = np.arange(L)
+        back = pt[i, t // P].astype(np.int64) * P + t % P
+        assert np.array_equal(back, c.req_to_token[c.req_pool_indices[i], :L].astype(np.int64))
+        npg = -(-L // P)
+        assert np.array_equal(pt[i, :npg], c.page_list[i, :npg])
+        # columns past the request's own pages come from the filler slots
+        assert np.all((pt[i] >= 0) & (pt[i] < c.num_pages))
+    assert np.array_equal(cache, c.seq_lens)
+    assert cu[0] == 0 and np.array_equal(np.diff(cu), cache)
+    assert cu[-1] == int(np.sum(c.seq_lens.astype(np.int64)))
+
+
+def test_metadata_offset_and_cumsum_wrap_int32():
+    r2t = np.arange(16, dtype=np.int32).reshape(2, 8)
+    rpi = np.array([1, 0], np.int32)
+    sl = np.array([2**31 - 10, 5], np.int32)
+    pt, cache, cu = oracle.build_page_table(r2t, rpi, sl, 4, 2, seqlen_offset=3)
+    assert cache.tolist() == [2**31 - 7, 8]
+    # int32 cumsum wraps like the int32 scan it defines
+    assert cu.tolist() == [0, 2**31 - 7, np.int32(np.int64(2**31 - 7 + 8) - 2**32)]
+    assert pt.tolist() == [[2, 3], [0, 1]]
+
+
+# ---------------------------------------------------------------- attention: golden
+
+def _golden_case(c, int8=False):
+    Hq, Hkv, D, P = c["num_q_heads"], c["num_kv_heads"], c["head_dim"], c["page_size"]
+    q = _bits(c["q"]).reshape(1, Hq, D)
+    pt = np.array([c["page_table"]], np.int32)
+    sl = np.array([c["seq_len"]], np.int32)
+    if int8:
+        k = np.array(c["k_pool_q8"], np.int8)
+        v = np.array(c["v_pool_q8"], np.int8)
+        ks = np.array(c["k_scales"], np.float32).reshape(k.shape[:3])
+        vs = np.array(c["v_scales"], np.float32).reshape(v.shape[:3])
+        return oracle.paged_attention(q, k, v, pt, sl, num_kv_heads=Hkv, page_size=P,
+                                      scale=c["scale"], kv_dtype="int8", k_scales=ks,
+                                      v_scales=vs)
+    k = _bits(c["k_pool"])
+    v = _bits(c["v_pool"])
+    return oracle.paged_attention(q, k, v, pt, sl, num_kv_heads=Hkv, page_size=P,
+                                  scale=c["scale"])
+
+
+@pytest.mark.parametrize("idx", range(3))
+def test_attention_golden_closed_forms(idx):
+    c = json.load(open(os.path.join(GOLDEN, "attention_tiny.json")))["cases"][idx]
+    out, lse = _golden_case(c)
+    want_o = np.array([[_ev(x) for x in row] for row in c["expect_out"]])
+    want_l = np.array([_ev(x) for x in c["expect_lse"]])
+    np.testing.assert_allclose(out[0], want_o, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse[0], want_l, rtol=0, atol=1e-14)
+
+
+def test_attention_golden_int8():
+    c = json.load(open(os.path.join(GOLDEN, "attention_tiny.json")))["int8_cases"][0]
+    out, lse = _golden_case(c, int8=True)
+    want_o = np.array([[_ev(x) for x in row] for row in c["expect_out"]])
+    np.testing.assert_allclose(out[0], want_o, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse[0], [_ev(c["expect_lse"][0])], rtol=0, atol=1e-14)
+
+
+# ---------------------------------------------------------------- attention: brute force
+
+SMALL = [
+    # (seq_lens, Hq, Hkv, D, P, num_pages)
+    ([1], 4, 1, 8, 4, 8),
+    ([2, 63], 8, 2, 8, 4, 24),
+    ([64, 65], 32, 8, 128, 64, 8),
+    ([130], 8, 2, 128, 64, 5),
+    ([63, 1], 32, 8, 128, 64, 4),
+    ([5, 9, 17], 4, 1, 8, 4, 12),
+]
+
+
+@pytest.mark.parametrize("kv", ["bf16", "int8"])
+@pytest.mark.parametrize("shape", SMALL)
+def test_attention_matches_dense_brute_force(shape, kv):
+    lens, Hq, Hkv, D, P, npg = shape
+    msp = max(-(-L // P) for L in lens) + 1
+    c = W.make_case(seed=11, seq_lens=lens, num_pages=npg, num_splits=2, kv_dtype=kv,
+                    num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=P,
+                    req_pool_rows=4, req_to_token_stride=msp * P, max_seq_pages=msp)
+    out, lse = oracle.case_attention(c)
+    bo, bl = dense_attention(c)
+    np.testing.assert_allclose(out, bo, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, bl, rtol=0, atol=1e-12)
+
+
+def test_attention_config1_matches_brute_force():
+    c = W.make_config(1)
+    out, lse = oracle.case_attention(c)
+    bo, bl = dense_attention(c)
+    np.testing.assert_allclose(out, bo, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, bl, rtol=0, atol=1e-12)
+
+
+def test_attention_via_metadata_page_table_equals_generator_placement():
+    c = W.make_config(3)
+    pt, _, _ = oracle.case_page_table(c)
+    a = oracle.case_attention(c, page_table=pt)
+    b = oracle.case_attention(c)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ---------------------------------------------------------------- special cases
+
+def _small(lens, **kw):
+    base = dict(seed=5, seq_lens=lens, num_pages=16, num_splits=4, num_q_heads=8,
+                num_kv_heads=2, head_dim=16, page_size=8, req_pool_rows=4,
+                req_to_token_stride=256, max_seq_pages=16)
+    base.update(kw)
+    return W.make_case(**base)
+
+
+def test_single_token_returns_its_value_row():
+    c = _small([1, 1])
+    out, lse = oracle.case_attention(c)
+    qf = W.bf16_bits_to_f32(c.q).astype(np.float64)
+    for b in range(c.batch):
+        k, v, _, _ = c.dense_kv(b)
+        kf = W.bf16_bits_to_f32(k).astype(np.float64)
+        vf = W.bf16_bits_to_f32(v).astype(np.float64)
+        for h in range(c.num_q_heads):
+            g = h // c.group
+            assert np.array_equal(out[b, h], vf[0, g])
+            assert lse[b, h] == pytest.approx(float(c.scale) * float(qf[b, h] @ kf[0, g]),
+                                              abs=1e-12)
+
+
+def test_zero_query_gives_mean_of_values():
+    c = _small([37, 8], q_override=np.zeros((2, 8, 16), np.uint16))
+    out, lse = oracle.case_attention(c)
+    for b in range(c.batch):
+        _, v, _, _ = c.dense_kv(b)
+        vf = W.bf16_bits_to_f32(v).astype(np.float64)
+        L = vf.shape[0]
+        for h in range(c.num_q_heads):
+            np.testing.assert_allclose(out[b, h], vf[:, h // c.group].mean(0), atol=1e-14)
+            assert lse[b, h] == pytest.approx(math.log(L), abs=1e-14)
+
+
+def test_constant_value_rows_give_that_constant():
+    c = _small([29])
+    c.v_pages[...] = _bits(np.float32(0.375))
+    out, _ = oracle.case_attention(c)
+    assert np.all(np.abs(out - 0.375) < 1e-15)
+
+
+def test_large_logits_no_overflow():
+    qf = np.random.default_rng(3).standard_normal((1, 8, 16)).astype(np.float32) * 30
+    c = _small([100], q_override=_bits(qf))
+    out, lse = oracle.case_attention(c)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    bo, bl = dense_attention(c)
+    np.testing.assert_allclose(out, bo, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, bl, rtol=1e-14, atol=1e-12)
+
+
+def test_empty_request_gives_zero_and_minus_inf():
+    c = _small([0, 3])
+    out, lse = oracle.case_attention(c)
+    assert np.all(out[0] == 0) and np.all(lse[0] == -np.inf)
+    assert np.all(np.isfinite(lse[1]))
+
+
+# ---------------------------------------------------------------- invariances
+
+@pytest.mark.parametrize("S", [1, 2, 3, 4, 16, 128])
+def test_split_merge_equals_direct(S):
+    c = _small([1, 8, 9, 100], num_pages=40, req_pool_rows=8)
+    out, lse = oracle.case_attention(c)
+    acc, m, l = oracle.split_partials(c.q, c.k_pages, c.v_pages, c.page_list, c.seq_lens,
+                                      num_kv_heads=c.num_kv_heads, page_size=c.page_size,
+                                      scale=c.scale, num_splits=S)
+    mo, ml = oracle.split_merge(acc, m, l)
+    np.testing.assert_allclose(mo, out, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(ml, lse, rtol=0, atol=1e-13)
+
+
+def test_split_partial_contract_single_split_and_empty_splits():
+    c = _small([8], num_pages=4)
+    acc, m, l = oracle.split_partials(c.q, c.k_pages, c.v_pages, c.page_list, c.seq_lens,
+                                      num_kv_heads=2, page_size=8, scale=c.scale, num_splits=3)
+    # one page, three splits: split 0 holds everything, splits 1 and 2 are empty
+    assert np.all(m[:, :, 1:] == -np.inf) and np.all(l[:, :, 1:] == 0) and np.all(acc[:, :, 1:] == 0)
+    out, lse = oracle.case_attention(c)
+    np.testing.assert_allclose(acc[:, :, 0] / l[:, :, 0, None], out, atol=1e-15)
+    np.testing.assert_allclose(m[:, :, 0] + np.log(l[:, :, 0]), lse, atol=1e-14)
+
+
+def _repermute(c, seed):
+    """Move every physical page to a new slot and update the placement; the
+    logical data are unchanged."""
+    rng = np.random.default_rng(seed)
+    sigma = rng.permutation(c.num_pages)          # old page p -> new page sigma[p]
+    k = np.empty_like(c.k_pages); k[sigma] = c.k_pages
+    v = np.empty_like(c.v_pages); v[sigma] = c.v_pages
+    pl = np.where(c.page_list >= 0, sigma[np.maximum(c.page_list, 0)], -1).astype(np.int32)
+    kw = {}
+    if c.k_scales is not None:
+        ks = np.empty_like(c.k_scales); ks[sigma] = c.k_scales
+        vs = np.empty_like(c.v_scales); vs[sigma] = c.v_scales
+        kw = dict(k_scales=ks, v_scales=vs)
+    return k, v, pl, kw
+
+
+@pytest.mark.parametrize("kv", ["bf16", "int8"])
+def test_physical_page_permutation_is_bit_identical(kv):
+    c = _small([50, 3, 17], num_pages=30, kv_dtype=kv)
+    out, lse = oracle.case_attention(c)
+    k, v, pl, kw = _repermute(c, 1)
+    o2, l2 = oracle.paged_attention(c.q, k, v, pl, c.seq_lens, num_kv_heads=2, page_size=8,
+                                    scale=c.scale, kv_dtype=kv, **kw)
+    assert np.array_equal(out, o2) and np.array_equal(lse, l2)
+
+
+def test_logical_key_order_permutation():
+    c = _small([40], num_pages=5)
+    out, lse = oracle.case_attention(c)
+    P = c.page_size
+    pages = c.page_list[0, :5]
+    rows = np.arange(40)
+    perm = np.random.default_rng(2).permutation(40)
+    k = c.k_pages.copy(); v = c.v_pages.copy()
+    src_k = c.k_pages[pages].reshape(40, 2, 16)
+    src_v = c.v_pages[pages].reshape(40, 2, 16)
+    k[pages] = src_k[perm].reshape(5, P, 2, 16)
+    v[pages] = src_v[perm].reshape(5, P, 2, 16)
+    o2, l2 = oracle.paged_attention(c.q, k, v, c.page_list, c.seq_lens, num_kv_heads=2,
+                                    page_size=P, scale=c.scale)
+    np.testing.assert_allclose(o2, out, atol=1e-14)
+    np.testing.assert_allclose(l2, lse, atol=1e-13)
+    assert rows.size == 40
+
+
+def test_gqa_identical_queries_in_group_give_identical_outputs():
+    c = _small([33])
+    q = c.q.copy()
+    q[:, 1:4] = q[:, 0:1]     # heads 0..3 form KV group 0 (group size 4)
+    o, l = oracle.paged_attention(q, c.k_pages, c.v_pages, c.page_list, c.seq_lens,
+                                  num_kv_heads=2, page_size=8, scale=c.scale)
+    for h in range(1, 4):
+        assert np.array_equal(o[:, h], o[:, 0]) and np.array_equal(l[:, h], l[:, 0])
+    assert not np.array_equal(o[:, 4], o[:, 0])
+
+
+def test_int8_dequantisation_is_exact_product():
+    c = _small([20], kv_dtype="int8")
+    k, v, ks, vs = c.dense_kv(0)
+    # sigma * q8 with |q8| <= 127 is exact in fp64; the brute force agrees
+    out, lse = oracle.case_attention(c)
+    bo, bl = dense_attention(c)
+    np.testing.assert_allclose(out, bo, atol=1e-12)
+    np.testing.assert_allclose(lse, bl, atol=1e-12)
+    assert np.max(np.abs(k.astype(np.int32))) <= 127
