@@ -1,0 +1,175 @@
+/*
+ * spa.h -- C ABI of libspa.so: split-K paged-attention decode and its
+ * page-table / cu_seqlens metadata build, for AMD Instinct MI355X (gfx950).
+ *
+ * Every pointer argument is a DEVICE pointer (memory the caller allocated
+ * with hipMalloc, or a PyTorch tensor's data pointer) unless stated
+ * otherwise; every size is in elements unless stated otherwise.  The caller
+ * owns every buffer, the workspace included; the library allocates nothing
+ * and keeps no state between calls.  All calls are asynchronous on the
+ * given stream, perform no host synchronisation and no memset, and may be
+ * captured into a HIP graph.
+ *
+ * Error behaviour.  Arguments are checked on the host BEFORE anything is
+ * launched: a rejected call returns a status and writes nothing.  A launch
+ * failure returns SPA_ERR_HIP (spa_last_hip_error() gives the hipError_t).
+ * Contract violations that only the device data could reveal -- a page id
+ * outside [0, num_pages), a req_pool_indices entry outside the pool, a
+ * seq_len larger than the page-table row covers -- are NOT checked and give
+ * undefined results (possibly a memory fault), as in the source kernels.
+ */
+#ifndef SPA_H_
+#define SPA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum spa_status {
+    SPA_OK = 0,
+    SPA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, negative size, bad stride/alignment */
+    SPA_ERR_UNSUPPORTED = 2,        /* shape/dtype outside the compiled set */
+    SPA_ERR_WORKSPACE_TOO_SMALL = 3,
+    SPA_ERR_HIP = 4                 /* a HIP runtime call or kernel launch failed */
+} spa_status;
+
+typedef enum spa_kv_dtype {
+    SPA_KV_BF16 = 0,   /* K/V pages hold bf16 values */
+    SPA_KV_INT8 = 1    /* K/V pages hold int8 codes; value = code * fp32 scale per (token, kv head) */
+} spa_kv_dtype;
+
+/* flags for spa_paged_decode_attention */
+#define SPA_DECODE_SEPARATE_MERGE 0x1u  /* producer and merge as two launches (default: one) */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *spa_status_string(spa_status status);
+
+/* hipError_t of the last call on this host thread that returned SPA_ERR_HIP. */
+int spa_last_hip_error(void);
+
+/* ABI revision of this header; bumped on any signature change. */
+int spa_abi_version(void);
+
+/*
+ * Page table, cache_seqlens and cu_seqlens_k in ONE launch.
+ *
+ * Defined by the fused CUDA-graph metadata update of sglang's TRTLLM MHA
+ * backend ("trtllm_mha_graph_metadata.py": module docstring, kernel row and
+ * cumsum branches, launcher), which replaces about 25 small host-dispatched
+ * ops per graph replay.  For i < bs and p < max_seq_pages:
+ *   cache_seqlens[i]  = seq_lens[i] + seqlen_offset                (int32)
+ *   cu_seqlens_k[0]   = 0;  cu_seqlens_k[i+1] = sum_{i'<=i} cache_seqlens[i']  (int32, wraps)
+ *   page_table[i*page_table_stride + p]
+ *        = floor(req_to_token[req_pool_indices[i]*req_to_token_stride + p*page_size] / page_size)
+ * using floor division (so slot -1 maps to page -1).  Columns
+ * p >= max_seq_pages of page_table are not touched.
+ *
+ *   req_to_token      [pool_size, req_to_token_stride] int32, row-major
+ *   req_pool_indices  [bs] int32, each in [0, pool_size)
+ *   seq_lens          [bs] int32
+ *   page_table        [bs, page_table_stride] int32 (output)
+ *   cache_seqlens     [bs] int32 (output);  cu_seqlens_k [bs + 1] int32 (output)
+ *
+ * bs == 0 returns SPA_OK without launching (the source launcher's early
+ * return).  Requires page_size >= 1, 0 <= max_seq_pages <= page_table_stride
+ * and (max_seq_pages - 1) * page_size < req_to_token_stride.
+ */
+spa_status spa_build_page_table(const int32_t *req_to_token, int64_t req_to_token_stride,
+                                int32_t pool_size, const int32_t *req_pool_indices,
+                                const int32_t *seq_lens, int32_t bs, int32_t seqlen_offset,
+                                int32_t page_size, int32_t max_seq_pages, int32_t *page_table,
+                                int64_t page_table_stride, int32_t *cache_seqlens,
+                                int32_t *cu_seqlens_k, hipStream_t stream);
+
+/*
+ * Bytes of workspace spa_paged_decode_attention needs: the per-split partial
+ * state (fp32 accumulator [B, Hq, S, D], fp32 max and sum [B, Hq, S]) plus
+ * one int32 arrival counter per (batch row, kv head).  0 for invalid sizes.
+ */
+size_t spa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t num_splits);
+
+/*
+ * Zero a workspace with a fill kernel (capture-safe; no hipMemset).  A new
+ * workspace must be zeroed once before its first use; every successful
+ * attention call leaves the counters at zero again, so no reset is needed
+ * between calls.  bytes must be a multiple of 4.
+ */
+spa_status spa_workspace_reset(void *workspace, size_t bytes, hipStream_t stream);
+
+/*
+ * Split-K paged-attention decode: one query token per request attends over
+ * its seq_lens[b] cached tokens, which live in fixed-size pages named by
+ * page_table (lmdeploy PR "use PDL for paged attention", Summary and Changes:
+ * a split-K producer writes per-split scratch, a reducer merges it).
+ *
+ *   q           [batch, num_q_heads, head_dim] bf16, contiguous, 16-byte aligned
+ *   k_pages,
+ *   v_pages     [num_pages, page_size, num_kv_heads, head_dim], bf16 or int8
+ *               codes, contiguous, 16-byte aligned; token t of request b is
+ *               row (page_table[b*page_table_stride + t/page_size], t % page_size)
+ *   k_scales,
+ *   v_scales    [num_pages, page_size, num_kv_heads] fp32 (SPA_KV_INT8 only,
+ *               else ignored; may be NULL for bf16)
+ *   page_table  [batch, page_table_stride] int32 physical page ids
+ *   seq_lens    [batch] int32, each in [0, page_table_stride * page_size]
+ *   out         [batch, num_q_heads, head_dim] bf16 (output)
+ *   lse         [batch, num_q_heads] fp32 (output, may be NULL):
+ *               ln(sum_t exp(s_t)) with s_t = scale * q . k_t
+ *
+ * Query head h reads kv head h / (num_q_heads / num_kv_heads).  Request b's
+ * ceil(L/page_size) pages are cut into num_splits splits of
+ * ceil(pages/num_splits) pages each (trailing splits may be empty).  Each
+ * split computes (max, sum, unnormalised accumulator); the splits are merged
+ * by log-sum-exp in split order.  By default the merge runs inside the same
+ * launch, in the last split workgroup to arrive; SPA_DECODE_SEPARATE_MERGE
+ * runs it as a second launch (same arithmetic, bit-identical output).
+ * L == 0 gives out = 0 and lse = -inf.
+ *
+ * Supported: head_dim 128, page_size 64, num_q_heads == 4 * num_kv_heads,
+ * kv_dtype bf16 or int8, 1 <= num_splits <= 1024; otherwise
+ * SPA_ERR_UNSUPPORTED.  workspace: spa_decode_workspace_bytes(...) bytes,
+ * 16-byte aligned, zeroed before first use (see spa_workspace_reset);
+ * concurrent calls must not share a workspace.  batch == 0 returns SPA_OK
+ * without launching.
+ */
+spa_status spa_paged_decode_attention(const void *q, const void *k_pages, const void *v_pages,
+                                      const float *k_scales, const float *v_scales,
+                                      const int32_t *page_table, int64_t page_table_stride,
+                                      const int32_t *seq_lens, int32_t batch,
+                                      int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t page_size, int32_t num_pages,
+                                      int32_t num_splits, float scale, spa_kv_dtype kv_dtype,
+                                      uint32_t flags, void *workspace, size_t workspace_bytes,
+                                      void *out, float *lse, hipStream_t stream);
+
+/*
+ * Log-sum-exp merge of per-split partial softmax state (the reducer of the
+ * lmdeploy split-K decode).  For each (b, h), with j = 0..num_splits-1 in order:
+ *   M = max_j m_j;  w_j = exp(m_j - M), or 0 where m_j = -inf (an empty split)
+ *   out[b,h,:] = sum_j w_j acc_j / sum_j w_j l_j   (bf16, round to nearest even)
+ *   lse[b,h]   = M + ln(sum_j w_j l_j)
+ * and out = 0, lse = -inf where sum_j w_j l_j == 0.
+ *
+ *   partial_acc [batch, num_q_heads, num_splits, head_dim] fp32, unnormalised
+ *   partial_max [batch, num_q_heads, num_splits] fp32, natural-log units of s
+ *   partial_sum [batch, num_q_heads, num_splits] fp32
+ *   out         [batch, num_q_heads, head_dim] bf16;  lse [batch, num_q_heads] fp32 (may be NULL)
+ *
+ * Any head_dim in [1, 4096] and num_splits in [1, 1024]; batch == 0 is a no-op.
+ */
+spa_status spa_split_merge(const float *partial_acc, const float *partial_max,
+                           const float *partial_sum, int32_t batch, int32_t num_q_heads,
+                           int32_t head_dim, int32_t num_splits, void *out, float *lse,
+                           hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPA_H_ */

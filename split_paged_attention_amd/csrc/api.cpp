@@ -1,0 +1,172 @@
+// C ABI of libspa.so: host-side argument checks, workspace layout and
+// dispatch to the kernels.  Every check runs before any HIP call, so a
+// rejected call launches nothing and writes nothing.
+#include <math.h>
+
+#include "../../include/spa.h"
+#include "internal.h"
+
+namespace spa {
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+WorkspaceLayout workspace_layout(int64_t batch, int64_t hq, int64_t hkv, int64_t head_dim,
+                                 int64_t splits) {
+    WorkspaceLayout w{};
+    const size_t rows = (size_t)batch * (size_t)hq * (size_t)splits;
+    w.acc_off = 0;
+    w.max_off = align256(w.acc_off + rows * (size_t)head_dim * sizeof(float));
+    w.sum_off = align256(w.max_off + rows * sizeof(float));
+    w.cnt_off = align256(w.sum_off + rows * sizeof(float));
+    w.total = align256(w.cnt_off + (size_t)batch * (size_t)hkv * sizeof(int32_t));
+    if (w.total == 0) w.total = 256;   // a valid request never needs 0 bytes
+    return w;
+}
+
+}  // namespace spa
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+spa_status hip_status(hipError_t e) {
+    if (e == hipSuccess) return SPA_OK;
+    g_last_hip_error = (int)e;
+    return SPA_ERR_HIP;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char *spa_status_string(spa_status status) {
+    switch (status) {
+        case SPA_OK: return "SPA_OK";
+        case SPA_ERR_INVALID_ARGUMENT: return "SPA_ERR_INVALID_ARGUMENT";
+        case SPA_ERR_UNSUPPORTED: return "SPA_ERR_UNSUPPORTED";
+        case SPA_ERR_WORKSPACE_TOO_SMALL: return "SPA_ERR_WORKSPACE_TOO_SMALL";
+        case SPA_ERR_HIP: return "SPA_ERR_HIP";
+    }
+    return "SPA_ERR_UNKNOWN";
+}
+
+int spa_last_hip_error(void) { return g_last_hip_error; }
+
+int spa_abi_version(void) { return 1; }
+
+spa_status spa_build_page_table(const int32_t *req_to_token, int64_t req_to_token_stride,
+                                int32_t pool_size, const int32_t *req_pool_indices,
+                                const int32_t *seq_lens, int32_t bs, int32_t seqlen_offset,
+                                int32_t page_size, int32_t max_seq_pages, int32_t *page_table,
+                                int64_t page_table_stride, int32_t *cache_seqlens,
+                                int32_t *cu_seqlens_k, hipStream_t stream) {
+    if (bs < 0 || page_size < 1 || max_seq_pages < 0 || pool_size < 1 ||
+        page_table_stride < max_seq_pages || page_table_stride < 1 || req_to_token_stride < 1)
+        return SPA_ERR_INVALID_ARGUMENT;
+    if (max_seq_pages > 0 && (int64_t)(max_seq_pages - 1) * page_size >= req_to_token_stride)
+        return SPA_ERR_INVALID_ARGUMENT;
+    if (bs == 0) return SPA_OK;
+    if (!req_to_token || !req_pool_indices || !seq_lens || !page_table || !cache_seqlens ||
+        !cu_seqlens_k)
+        return SPA_ERR_INVALID_ARGUMENT;
+    if (bs == INT32_MAX) return SPA_ERR_INVALID_ARGUMENT;   // grid is bs + 1
+    return hip_status(spa::launch_build_page_table(
+        req_to_token, req_to_token_stride, req_pool_indices, seq_lens, bs, seqlen_offset,
+        page_size, max_seq_pages, page_table, page_table_stride, cache_seqlens, cu_seqlens_k,
+        stream));
+}
+
+size_t spa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t num_splits) {
+    if (batch < 0 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 || num_splits < 1)
+        return 0;
+    return spa::workspace_layout(batch, num_q_heads, num_kv_heads, head_dim, num_splits).total;
+}
+
+spa_status spa_workspace_reset(void *workspace, size_t bytes, hipStream_t stream) {
+    if (bytes == 0) return SPA_OK;
+    if (!workspace || bytes % 4 != 0 || !aligned(workspace, 4)) return SPA_ERR_INVALID_ARGUMENT;
+    return hip_status(spa::launch_fill_zero(workspace, bytes / 4, stream));
+}
+
+spa_status spa_paged_decode_attention(const void *q, const void *k_pages, const void *v_pages,
+                                      const float *k_scales, const float *v_scales,
+                                      const int32_t *page_table, int64_t page_table_stride,
+                                      const int32_t *seq_lens, int32_t batch,
+                                      int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t page_size, int32_t num_pages,
+                                      int32_t num_splits, float scale, spa_kv_dtype kv_dtype,
+                                      uint32_t flags, void *workspace, size_t workspace_bytes,
+                                      void *out, float *lse, hipStream_t stream) {
+    if (batch < 0 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 || page_size < 1 ||
+        num_pages < 1 || num_splits < 1 || page_table_stride < 1)
+        return SPA_ERR_INVALID_ARGUMENT;
+    if (num_q_heads % num_kv_heads != 0) return SPA_ERR_INVALID_ARGUMENT;
+    if (kv_dtype != SPA_KV_BF16 && kv_dtype != SPA_KV_INT8) return SPA_ERR_INVALID_ARGUMENT;
+    if ((flags & ~SPA_DECODE_SEPARATE_MERGE) != 0) return SPA_ERR_INVALID_ARGUMENT;
+    if (!isfinite(scale)) return SPA_ERR_INVALID_ARGUMENT;
+    if (head_dim != spa::kHeadDim || page_size != spa::kPageSize ||
+        num_q_heads != spa::kGroup * num_kv_heads || num_splits > 1024)
+        return SPA_ERR_UNSUPPORTED;
+    // grid = batch * kv_heads * splits workgroups must fit a 32-bit grid
+    if ((int64_t)batch * num_kv_heads * num_splits > (int64_t)INT32_MAX)
+        return SPA_ERR_UNSUPPORTED;
+    if (batch == 0) return SPA_OK;
+    if (!q || !k_pages || !v_pages || !page_table || !seq_lens || !out || !workspace)
+        return SPA_ERR_INVALID_ARGUMENT;
+    if (kv_dtype == SPA_KV_INT8 && (!k_scales || !v_scales)) return SPA_ERR_INVALID_ARGUMENT;
+    if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) ||
+        !aligned(workspace, 16) || !aligned(out, 2) || !aligned(page_table, 4) ||
+        !aligned(seq_lens, 4) || (lse && !aligned(lse, 4)) ||
+        (kv_dtype == SPA_KV_INT8 && (!aligned(k_scales, 4) || !aligned(v_scales, 4))))
+        return SPA_ERR_INVALID_ARGUMENT;
+    const spa::WorkspaceLayout w =
+        spa::workspace_layout(batch, num_q_heads, num_kv_heads, head_dim, num_splits);
+    if (workspace_bytes < w.total) return SPA_ERR_WORKSPACE_TOO_SMALL;
+
+    char *ws = static_cast<char *>(workspace);
+    spa::DecodeParams p{};
+    p.q = q;
+    p.k_pages = k_pages;
+    p.v_pages = v_pages;
+    p.k_scales = k_scales;
+    p.v_scales = v_scales;
+    p.page_table = page_table;
+    p.pt_stride = page_table_stride;
+    p.seq_lens = seq_lens;
+    p.batch = batch;
+    p.hq = num_q_heads;
+    p.hkv = num_kv_heads;
+    p.splits = num_splits;
+    p.qk_scale_log2 = scale * 1.4426950408889634f;
+    p.part_acc = reinterpret_cast<float *>(ws + w.acc_off);
+    p.part_max = reinterpret_cast<float *>(ws + w.max_off);
+    p.part_sum = reinterpret_cast<float *>(ws + w.sum_off);
+    p.counters = reinterpret_cast<int32_t *>(ws + w.cnt_off);
+    p.out = static_cast<uint16_t *>(out);
+    p.lse = lse;
+    const bool fused = (flags & SPA_DECODE_SEPARATE_MERGE) == 0;
+    return hip_status(spa::launch_decode(p, kv_dtype == SPA_KV_INT8 ? 1 : 0, fused, stream));
+}
+
+spa_status spa_split_merge(const float *partial_acc, const float *partial_max,
+                           const float *partial_sum, int32_t batch, int32_t num_q_heads,
+                           int32_t head_dim, int32_t num_splits, void *out, float *lse,
+                           hipStream_t stream) {
+    if (batch < 0 || num_q_heads < 1 || head_dim < 1 || head_dim > 4096 || num_splits < 1 ||
+        num_splits > 1024)
+        return SPA_ERR_INVALID_ARGUMENT;
+    if ((int64_t)batch * num_q_heads > (int64_t)INT32_MAX) return SPA_ERR_UNSUPPORTED;
+    if (batch == 0) return SPA_OK;
+    if (!partial_acc || !partial_max || !partial_sum || !out) return SPA_ERR_INVALID_ARGUMENT;
+    if (!aligned(partial_acc, 4) || !aligned(partial_max, 4) || !aligned(partial_sum, 4) ||
+        !aligned(out, 2) || (lse && !aligned(lse, 4)))
+        return SPA_ERR_INVALID_ARGUMENT;
+    return hip_status(spa::launch_split_merge(partial_acc, partial_max, partial_sum,
+                                              batch * num_q_heads, head_dim, num_splits,
+                                              static_cast<uint16_t *>(out), lse, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,151 @@
+"""C-ABI boundary tests that need no GPU: the library loads, exports every
+function include/spa.h declares, and rejects bad arguments on the host
+before launching anything (fake non-null pointers are never dereferenced)."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import split_paged_attention_amd as spa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spa.h")
+
+FAKE = ctypes.c_void_p(0x100000)       # aligned, never dereferenced
+FAKE_ODD = ctypes.c_void_p(0x100002)   # misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["spa_build_page_table", "spa_paged_decode_attention", "spa_split_merge",
+              "spa_decode_workspace_bytes", "spa_workspace_reset", "spa_status_string"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", spa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    L = spa.lib()
+    for n in declared_functions():
+        assert n in exported, n
+        assert hasattr(L, n)
+    assert L.spa_abi_version() == 1
+
+
+def test_status_strings():
+    assert spa.status_string(0) == "SPA_OK"
+    assert spa.status_string(3) == "SPA_ERR_WORKSPACE_TOO_SMALL"
+    assert spa.status_string(99) == "SPA_ERR_UNKNOWN"
+
+
+def _attn(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ks=None, vs=None, pt=FAKE, pts=128, sl=FAKE, B=1, Hq=32,
+             Hkv=8, D=128, P=64, npg=16, S=4, scale=0.088, kvd=0, flags=0, ws=FAKE,
+             wsb=1 << 30, out=FAKE, lse=FAKE)
+    a.update(kw)
+    return spa.lib().spa_paged_decode_attention(
+        a["q"], a["k"], a["v"], a["ks"], a["vs"], a["pt"], a["pts"], a["sl"], a["B"], a["Hq"],
+        a["Hkv"], a["D"], a["P"], a["npg"], a["S"], a["scale"], a["kvd"], a["flags"], a["ws"],
+        a["wsb"], a["out"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(Hq=30), spa.SPA_ERR_INVALID_ARGUMENT),            # Hq % Hkv != 0
+    (dict(S=0), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(kvd=7), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(flags=2), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(scale=math.nan), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(scale=math.inf), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(pts=0), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(q=None), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(out=None), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(ws=None), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(kvd=1), spa.SPA_ERR_INVALID_ARGUMENT),            # int8 without scales
+    (dict(q=FAKE_ODD), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(k=FAKE_ODD), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(D=64), spa.SPA_ERR_UNSUPPORTED),
+    (dict(P=32), spa.SPA_ERR_UNSUPPORTED),
+    (dict(Hq=64), spa.SPA_ERR_UNSUPPORTED),                 # group 8
+    (dict(Hq=8, Hkv=8), spa.SPA_ERR_UNSUPPORTED),           # group 1
+    (dict(S=1025), spa.SPA_ERR_UNSUPPORTED),
+    (dict(wsb=1024), spa.SPA_ERR_WORKSPACE_TOO_SMALL),
+    (dict(B=0), spa.SPA_OK),                                # no launch
+    (dict(B=0, q=None, out=None), spa.SPA_OK),
+])
+def test_attention_argument_checks(kw, code):
+    assert _attn(**kw) == code
+
+
+def test_workspace_bytes():
+    f = spa.decode_workspace_bytes
+    assert f(0, 32, 8, 128, 16) > 0
+    n = f(32, 32, 8, 128, 16)
+    rows = 32 * 32 * 16
+    assert n >= rows * 128 * 4 + 2 * rows * 4 + 32 * 8 * 4
+    assert n % 256 == 0
+    assert f(-1, 32, 8, 128, 4) == 0 and f(1, 32, 8, 128, 0) == 0 and f(1, 0, 8, 128, 4) == 0
+    assert _attn(wsb=n - 1, B=32, S=16) == spa.SPA_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_workspace_reset_checks():
+    L = spa.lib()
+    assert L.spa_workspace_reset(None, 0, None) == spa.SPA_OK
+    assert L.spa_workspace_reset(None, 16, None) == spa.SPA_ERR_INVALID_ARGUMENT
+    assert L.spa_workspace_reset(FAKE, 6, None) == spa.SPA_ERR_INVALID_ARGUMENT
+
+
+def _meta(**kw):
+    a = dict(r2t=FAKE, r2ts=8192, pool=64, rpi=FAKE, sl=FAKE, bs=4, off=0, P=64, msp=128,
+             pt=FAKE, pts=128, cache=FAKE, cu=FAKE)
+    a.update(kw)
+    return spa.lib().spa_build_page_table(a["r2t"], a["r2ts"], a["pool"], a["rpi"], a["sl"],
+                                          a["bs"], a["off"], a["P"], a["msp"], a["pt"], a["pts"],
+                                          a["cache"], a["cu"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bs=-1), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(P=0), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(msp=-1), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(pts=100), spa.SPA_ERR_INVALID_ARGUMENT),          # stride < max_seq_pages
+    (dict(r2ts=127 * 64), spa.SPA_ERR_INVALID_ARGUMENT),    # last column past the row
+    (dict(pool=0), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(r2t=None), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(cu=None), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(bs=2**31 - 1), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(bs=0), spa.SPA_OK),
+    (dict(bs=0, r2t=None, cu=None), spa.SPA_OK),
+])
+def test_page_table_argument_checks(kw, code):
+    assert _meta(**kw) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((FAKE, FAKE, FAKE, 1, 32, 128, 0, FAKE, FAKE), spa.SPA_ERR_INVALID_ARGUMENT),
+    ((FAKE, FAKE, FAKE, 1, 32, 0, 4, FAKE, FAKE), spa.SPA_ERR_INVALID_ARGUMENT),
+    ((FAKE, FAKE, FAKE, 1, 32, 5000, 4, FAKE, FAKE), spa.SPA_ERR_INVALID_ARGUMENT),
+    ((FAKE, FAKE, FAKE, -1, 32, 128, 4, FAKE, FAKE), spa.SPA_ERR_INVALID_ARGUMENT),
+    ((None, FAKE, FAKE, 1, 32, 128, 4, FAKE, FAKE), spa.SPA_ERR_INVALID_ARGUMENT),
+    ((FAKE, FAKE, FAKE, 1, 32, 128, 4, None, FAKE), spa.SPA_ERR_INVALID_ARGUMENT),
+    ((None, None, None, 0, 32, 128, 4, None, None), spa.SPA_OK),
+])
+def test_split_merge_argument_checks(args, code):
+    assert spa.lib().spa_split_merge(*args, None) == code
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(spa, "_lib", None)
+    monkeypatch.setattr(spa, "LIB_PATH", "/nonexistent/libspa.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        spa.lib()

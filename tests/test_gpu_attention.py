@@ -1,0 +1,307 @@
+"""GPU parity for split-K paged-attention decode against the fp64 oracle,
+through the C ABI.  Tolerances: bf16 output max-abs 1e-2, LSE max-abs 1e-3
+(tests/gpu_util.py); structural properties (one-token context, fused vs
+two-launch, repeat, page permutation, GQA grouping) are checked bit-exactly."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import split_paged_attention_amd as spa
+import workloads as W
+from tests.gpu_util import (DevCase, bf16_dev, bits_host, compare_attention, config_case,
+                            counters_view)
+
+pytestmark = pytest.mark.gpu
+
+
+def small_case(lens, kv="bf16", S=4, seed=21, num_pages=None, q_override=None, Hkv=8):
+    P = 64
+    need = sum(-(-L // P) for L in lens)
+    msp = max(1, max(-(-L // P) for L in lens))
+    return W.make_case(seed=seed, seq_lens=lens, num_pages=num_pages or need + 3, num_splits=S,
+                       kv_dtype=kv, num_q_heads=4 * Hkv, num_kv_heads=Hkv, head_dim=128,
+                       page_size=P, req_pool_rows=max(4, len(lens)),
+                       req_to_token_stride=msp * P, max_seq_pages=msp, q_override=q_override,
+                       name=f"lens{lens}_{kv}_S{S}")
+
+
+# ---------------------------------------------------------------- configs
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 5])
+def test_config_parity_full(cfg):
+    c = config_case(cfg)
+    print(f"[case] attention config {cfg} ({c.name}) full parity", flush=True)
+    d = DevCase(c)
+    pt, _, _ = d.page_table()
+    out, lse = d.attention(page_table=pt)
+    pt_o, _, _ = oracle.case_page_table(c)
+    o_ref, l_ref = oracle.case_attention(c, page_table=pt_o)
+    compare_attention(out, lse, o_ref, l_ref, label=c.name)
+
+
+def test_config4_headline_parity():
+    """Batch 32 / context 8K in the launch configuration the benchmark times,
+    every output checked (the oracle finishes it in seconds)."""
+    c = config_case(4)
+    print(f"[case] attention config 4 ({c.name}) full parity", flush=True)
+    d = DevCase(c)
+    pt, _, _ = d.page_table()
+    out, lse = d.attention(page_table=pt)
+    o_ref, l_ref = oracle.case_attention(c)
+    compare_attention(out, lse, o_ref, l_ref, label=c.name)
+
+
+# ---------------------------------------------------------------- ragged / edges
+
+@pytest.mark.parametrize("kv", ["bf16", "int8"])
+@pytest.mark.parametrize("lens,S", [
+    ([1, 63, 64, 65], 1),
+    ([127, 128, 129, 1000], 3),
+    ([1, 2, 3, 700], 16),           # splits with no pages
+    ([4096, 5, 64, 191], 64),       # many empty splits
+    ([8192, 8191, 1], 16),
+])
+def test_ragged_parity(lens, S, kv):
+    c = small_case(lens, kv=kv, S=S)
+    print(f"[case] ragged {c.name}", flush=True)
+    out, lse = DevCase(c).attention()
+    o_ref, l_ref = oracle.case_attention(c)
+    compare_attention(out, lse, o_ref, l_ref, label=c.name)
+
+
+def test_zero_length_request():
+    c = small_case([0, 70, 0], S=4)
+    print("[case] zero-length requests", flush=True)
+    out, lse = DevCase(c).attention()
+    o_ref, l_ref = oracle.case_attention(c)
+    compare_attention(out, lse, o_ref, l_ref, label="L=0")
+    o = bits_host(out)
+    assert np.all(o[0] == 0) and np.all(o[2] == 0)
+    assert torch.all(torch.isneginf(lse[0])) and torch.all(torch.isneginf(lse[2]))
+
+
+@pytest.mark.parametrize("kv", ["bf16", "int8"])
+def test_single_token_returns_value_row_bit_exact(kv):
+    c = small_case([1, 1, 1], kv=kv, S=4)
+    print(f"[case] one-token context {kv}", flush=True)
+    out, lse = DevCase(c).attention()
+    o_ref, l_ref = oracle.case_attention(c)
+    compare_attention(out, lse, o_ref, l_ref, label=f"L=1 {kv}")
+    if kv != "bf16":
+        return   # int8: the value scale is folded into the bf16 probability, so within tolerance
+    got = bits_host(out)
+    for b in range(c.batch):
+        k, v, _, _ = c.dense_kv(b)
+        for h in range(c.num_q_heads):
+            assert np.array_equal(got[b, h], v[0, h // c.group])
+
+
+def test_large_logits():
+    qf = np.random.default_rng(4).standard_normal((2, 32, 128)).astype(np.float32) * 30
+    c = small_case([900, 77], S=4, q_override=W.f32_to_bf16_bits(qf))
+    print("[case] large logits", flush=True)
+    out, lse = DevCase(c).attention()
+    assert torch.isfinite(lse).all()
+    o_ref, l_ref = oracle.case_attention(c)
+    compare_attention(out, lse, o_ref, l_ref, label="q*30")
+
+
+# ---------------------------------------------------------------- structure
+
+@pytest.mark.parametrize("kv", ["bf16", "int8"])
+def test_fused_equals_two_launch_bit_exact(kv):
+    c = small_case([3000, 64, 1, 777], kv=kv, S=16)
+    print(f"[case] fused vs separate merge {kv}", flush=True)
+    d = DevCase(c)
+    o1, l1 = d.attention()
+    o2, l2 = d.attention(separate_merge=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+
+
+def test_repeat_bit_identical_and_counters_return_to_zero():
+    c = config_case(3)
+    print("[case] repeat x20 + counters", flush=True)
+    d = DevCase(c)
+    B, Hq, D, S = c.batch, c.num_q_heads, c.head_dim, c.num_splits
+    ws = spa.new_workspace(B, Hq, c.num_kv_heads, D, S)
+    o0, l0 = d.attention(workspace=ws)
+    for _ in range(20):
+        o, l = d.attention(workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o0.view(torch.int16)) and torch.equal(l, l0)
+    assert int(counters_view(ws, B, Hq, c.num_kv_heads, D, S).abs().sum()) == 0
+
+
+def test_alternating_inputs_share_one_workspace():
+    """Two different batches of the same shape alternate on one workspace: a
+    merge that read partial state left by the previous call (instead of this
+    call's) would give the other batch's answer."""
+    ca = small_case([3000, 700, 65, 1], S=16, seed=31)
+    cb = small_case([3000, 700, 65, 1], S=16, seed=32)
+    print("[case] alternating inputs on one workspace", flush=True)
+    da, db = DevCase(ca), DevCase(cb)
+    ref_a = da.attention(separate_merge=True)
+    ref_b = db.attention(separate_merge=True)
+    ws = spa.new_workspace(4, 32, 8, 128, 16)
+    for it in range(6):
+        d, ref = (da, ref_a) if it % 2 == 0 else (db, ref_b)
+        o, l = d.attention(workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), ref[0].view(torch.int16)), it
+        assert torch.equal(l, ref[1]), it
+
+
+def test_nan_poisoned_partials_region_is_never_read_before_write():
+    c = small_case([1500, 2, 640], S=8)
+    print("[case] NaN-poisoned workspace", flush=True)
+    d = DevCase(c)
+    B, Hq, D, S = c.batch, c.num_q_heads, c.head_dim, c.num_splits
+    ws = spa.new_workspace(B, Hq, c.num_kv_heads, D, S)
+    cnt = counters_view(ws, B, Hq, c.num_kv_heads, D, S)
+    nbytes = cnt.data_ptr() - ws.data_ptr()
+    ws[:nbytes].view(torch.float32).fill_(float("nan"))
+    out, lse = d.attention(workspace=ws)
+    o_ref, l_ref = oracle.case_attention(c)
+    compare_attention(out, lse, o_ref, l_ref, label="poisoned")
+
+
+def test_physical_page_permutation_bit_identical():
+    c = small_case([900, 130, 64, 1], S=4, num_pages=40)
+    print("[case] physical page permutation", flush=True)
+    d = DevCase(c)
+    o1, l1 = d.attention()
+    sigma = np.random.default_rng(9).permutation(c.num_pages)
+    k = np.empty_like(c.k_pages); k[sigma] = c.k_pages
+    v = np.empty_like(c.v_pages); v[sigma] = c.v_pages
+    pl = np.where(c.page_list >= 0, sigma[np.maximum(c.page_list, 0)], -1).astype(np.int32)
+    o2, l2 = spa.paged_decode_attention(d.q, bf16_dev(k), bf16_dev(v),
+                                        torch.from_numpy(pl).cuda(), d.seq_lens, c.num_splits,
+                                        float(c.scale))
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_gqa_identical_queries_identical_outputs():
+    q = np.random.default_rng(5).standard_normal((2, 32, 128)).astype(np.float32)
+    q = q.reshape(2, 8, 4, 128)
+    q[:, :, 1:] = q[:, :, :1]
+    c = small_case([500, 64], S=4, q_override=W.f32_to_bf16_bits(q.reshape(2, 32, 128)))
+    print("[case] GQA identical queries", flush=True)
+    out, lse = DevCase(c).attention()
+    o = bits_host(out).reshape(2, 8, 4, 128)
+    l = lse.cpu().numpy().reshape(2, 8, 4)
+    for r in range(1, 4):
+        assert np.array_equal(o[:, :, r], o[:, :, 0]) and np.array_equal(l[:, :, r], l[:, :, 0])
+
+
+def test_split_count_changes_little():
+    c = small_case([6000, 300], S=1)
+    print("[case] split count sweep", flush=True)
+    d = DevCase(c)
+    o_ref, l_ref = oracle.case_attention(c)
+    for S in [1, 2, 5, 16, 94, 128, 1024]:
+        out, lse = d.attention(num_splits=S)
+        compare_attention(out, lse, o_ref, l_ref, label=f"S={S}")
+
+
+def test_split_merge_entry_point():
+    c = small_case([2000, 1, 300], S=7)
+    print("[case] split-merge entry point", flush=True)
+    acc, m, l = oracle.split_partials(c.q, c.k_pages, c.v_pages, c.page_list, c.seq_lens,
+                                      num_kv_heads=8, page_size=64, scale=c.scale, num_splits=7)
+    acc32, m32, l32 = acc.astype(np.float32), m.astype(np.float32), l.astype(np.float32)
+    o_ref, l_ref = oracle.split_merge(acc32, m32, l32)
+    out, lse = spa.split_merge(torch.from_numpy(acc32).cuda(), torch.from_numpy(m32).cuda(),
+                               torch.from_numpy(l32).cuda())
+    torch.cuda.synchronize()
+    from tests.gpu_util import bf16_to_f64
+    o = bf16_to_f64(out)
+    # bf16 rounding of the output (half an ulp) plus fp32 arithmetic
+    assert np.all(np.abs(o - o_ref) <= np.abs(o_ref) * 2.0 ** -8 + 1e-6)
+    fin = np.isfinite(l_ref)
+    assert np.array_equal(np.isfinite(lse.cpu().numpy()), fin)
+    assert np.max(np.abs(lse.cpu().numpy()[fin] - l_ref[fin])) <= 1e-5
+
+
+def test_split_merge_generic_head_dim():
+    rng = np.random.default_rng(3)
+    print("[case] split-merge head_dim 72, 33 splits, empty splits", flush=True)
+    B, Hq, S, D = 3, 5, 33, 72
+    acc = rng.standard_normal((B, Hq, S, D)).astype(np.float32)
+    m = rng.standard_normal((B, Hq, S)).astype(np.float32) * 5
+    l = rng.uniform(0.5, 3, (B, Hq, S)).astype(np.float32)
+    m[0, 0, ::2] = -np.inf; l[0, 0, ::2] = 0; acc[0, 0, ::2] = 0
+    m[1, 1, :] = -np.inf; l[1, 1, :] = 0; acc[1, 1, :] = 0
+    o_ref, l_ref = oracle.split_merge(acc, m, l)
+    out, lse = spa.split_merge(torch.from_numpy(acc).cuda(), torch.from_numpy(m).cuda(),
+                               torch.from_numpy(l).cuda())
+    torch.cuda.synchronize()
+    from tests.gpu_util import bf16_to_f64
+    o = bf16_to_f64(out)
+    assert np.all(np.abs(o - o_ref) <= np.abs(o_ref) * 2.0 ** -8 + 1e-6)
+    ln = lse.cpu().numpy()
+    assert np.isneginf(ln[1, 1]) and np.all(o[1, 1] == 0)
+    fin = np.isfinite(l_ref)
+    assert np.max(np.abs(ln[fin] - l_ref[fin])) <= 1e-5
+
+
+# ---------------------------------------------------------------- full step + graphs
+
+def test_full_step_config5_metadata_then_attention():
+    """The whole hot path on the ragged int8 batch: page table, cache_seqlens
+    and cu_seqlens_k built on the device (bit-exact) feed the attention."""
+    c = config_case(5)
+    print("[case] full step config 5", flush=True)
+    d = DevCase(c)
+    pt, cache, cu = d.page_table()
+    pt_o, cache_o, cu_o = oracle.case_page_table(c)
+    torch.cuda.synchronize()
+    assert np.array_equal(pt.cpu().numpy(), pt_o)
+    assert np.array_equal(cache.cpu().numpy(), cache_o)
+    assert np.array_equal(cu.cpu().numpy(), cu_o)
+    out, lse = d.attention(page_table=pt)
+    o_ref, l_ref = oracle.case_attention(c, page_table=pt_o)
+    compare_attention(out, lse, o_ref, l_ref, label="config 5 step")
+
+
+def test_hip_graph_replay_matches_eager():
+    c = config_case(3)
+    print("[case] HIP graph capture of the decode step", flush=True)
+    d = DevCase(c)
+    B, Hq, D, S = c.batch, c.num_q_heads, c.head_dim, c.num_splits
+    ws = spa.new_workspace(B, Hq, c.num_kv_heads, D, S)
+    pt = torch.empty((B, c.max_seq_pages), dtype=torch.int32, device="cuda")
+    cache = torch.empty((B,), dtype=torch.int32, device="cuda")
+    cu = torch.empty((B + 1,), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+
+    def step():
+        spa.build_page_table(d.r2t, d.rpi, d.seq_lens, c.page_size, c.max_seq_pages,
+                             page_table=pt, cache_seqlens=cache, cu_seqlens_k=cu)
+        d.attention(page_table=pt, workspace=ws, out=out, lse=lse)
+
+    step()
+    torch.cuda.synchronize()
+    o_eager, l_eager = out.clone(), lse.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(4):
+        out.zero_(); lse.zero_(); pt.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), o_eager.view(torch.int16))
+        assert torch.equal(lse, l_eager)
+        step()   # eager work between replays
+        torch.cuda.synchronize()
+    assert int(counters_view(ws, B, Hq, c.num_kv_heads, D, S).abs().sum()) == 0
