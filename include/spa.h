@@ -43,8 +43,13 @@ typedef enum spa_kv_dtype {
     SPA_KV_INT8 = 1    /* K/V pages hold int8 codes; value = code * fp32 scale per (token, kv head) */
 } spa_kv_dtype;
 
-/* flags for spa_paged_decode_attention */
-#define SPA_DECODE_SEPARATE_MERGE 0x1u  /* producer and merge as two launches (default: one) */
+/* flags for spa_paged_decode_attention (0 = the library chooses).  None of
+ * them changes what is computed; the producer shape changes the rounding of
+ * the in-workgroup combination, the merge placement changes nothing. */
+#define SPA_DECODE_SEPARATE_MERGE 0x1u  /* merge as a second launch */
+#define SPA_DECODE_FUSED_MERGE 0x2u     /* merge in the last split workgroup (one launch) */
+#define SPA_DECODE_HEAD_GROUPED 0x4u    /* producer: 2 kv heads per workgroup, waves walk all pages */
+#define SPA_DECODE_PAGE_SPLIT 0x8u      /* producer: 1 kv head per workgroup, 4 waves share pages */
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *spa_status_string(spa_status status);
@@ -126,14 +131,17 @@ spa_status spa_workspace_reset(void *workspace, size_t bytes, hipStream_t stream
  * ceil(L/page_size) pages are cut into num_splits splits of
  * ceil(pages/num_splits) pages each (trailing splits may be empty).  Each
  * split computes (max, sum, unnormalised accumulator); the splits are merged
- * by log-sum-exp in split order.  By default the merge runs inside the same
- * launch, in the last split workgroup to arrive; SPA_DECODE_SEPARATE_MERGE
- * runs it as a second launch (same arithmetic, bit-identical output).
- * L == 0 gives out = 0 and lse = -inf.
+ * by log-sum-exp in split order, either inside the producer launch by the
+ * last split workgroup to arrive, or by a second launch -- same arithmetic,
+ * bit-identical output.  With flags == 0 the library picks the producer
+ * shape from batch * num_kv_heads * num_splits (the same sizes always give
+ * the same choice, so results are reproducible) and the merge placement that
+ * is faster for it.  L == 0 gives out = 0 and lse = -inf.  Contradictory
+ * flags (both merges, both producers) are SPA_ERR_INVALID_ARGUMENT.
  *
  * Supported: head_dim 128, page_size 64, num_q_heads == 4 * num_kv_heads,
- * kv_dtype bf16 or int8, 1 <= num_splits <= 1024; otherwise
- * SPA_ERR_UNSUPPORTED.  workspace: spa_decode_workspace_bytes(...) bytes,
+ * kv_dtype bf16 or int8, 1 <= num_splits <= 1024 (SPA_DECODE_HEAD_GROUPED
+ * also needs an even num_kv_heads); otherwise SPA_ERR_UNSUPPORTED.  workspace: spa_decode_workspace_bytes(...) bytes,
  * 16-byte aligned, zeroed before first use (see spa_workspace_reset);
  * concurrent calls must not share a workspace.  batch == 0 returns SPA_OK
  * without launching.

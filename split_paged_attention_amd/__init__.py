@@ -20,7 +20,8 @@ __all__ = [
     "workspace_reset", "new_workspace", "paged_decode_attention", "split_merge",
     "SPA_OK", "SPA_ERR_INVALID_ARGUMENT", "SPA_ERR_UNSUPPORTED",
     "SPA_ERR_WORKSPACE_TOO_SMALL", "SPA_ERR_HIP", "SPA_KV_BF16", "SPA_KV_INT8",
-    "SPA_DECODE_SEPARATE_MERGE",
+    "SPA_DECODE_SEPARATE_MERGE", "SPA_DECODE_FUSED_MERGE", "SPA_DECODE_HEAD_GROUPED",
+    "SPA_DECODE_PAGE_SPLIT",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspa.so")
@@ -33,6 +34,9 @@ SPA_ERR_HIP = 4
 SPA_KV_BF16 = 0
 SPA_KV_INT8 = 1
 SPA_DECODE_SEPARATE_MERGE = 0x1
+SPA_DECODE_FUSED_MERGE = 0x2
+SPA_DECODE_HEAD_GROUPED = 0x4
+SPA_DECODE_PAGE_SPLIT = 0x8
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
@@ -191,11 +195,16 @@ def paged_decode_attention(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torc
                            out: Optional[torch.Tensor] = None,
                            lse: Optional[torch.Tensor] = None,
                            separate_merge: bool = False,
+                           merge: Optional[str] = None,
+                           producer: Optional[str] = None,
                            stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """spa_paged_decode_attention.  q [B, Hq, D] bf16; k/v_pages
     [num_pages, P, Hkv, D] bf16 or int8; k/v_scales [num_pages, P, Hkv] fp32
     for int8; page_table [B, stride] int32; seq_lens [B] int32.
-    Returns (out [B, Hq, D] bf16, lse [B, Hq] fp32)."""
+    Returns (out [B, Hq, D] bf16, lse [B, Hq] fp32).
+
+    merge: None (library default), "fused" or "separate" (``separate_merge=True``
+    is the same as "separate"); producer: None, "head_grouped" or "page_split"."""
     _need(q, "q", torch.bfloat16)
     if q.dim() != 3:
         raise ValueError("q must be [batch, num_q_heads, head_dim]")
@@ -233,7 +242,13 @@ def paged_decode_attention(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torc
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     _need(out, "out", torch.bfloat16)
     _need(lse, "lse", torch.float32)
-    flags = SPA_DECODE_SEPARATE_MERGE if separate_merge else 0
+    if separate_merge:
+        if merge not in (None, "separate"):
+            raise ValueError("separate_merge=True contradicts merge=" + repr(merge))
+        merge = "separate"
+    flags = {None: 0, "fused": SPA_DECODE_FUSED_MERGE, "separate": SPA_DECODE_SEPARATE_MERGE}[merge]
+    flags |= {None: 0, "head_grouped": SPA_DECODE_HEAD_GROUPED,
+              "page_split": SPA_DECODE_PAGE_SPLIT}[producer]
     st = lib().spa_paged_decode_attention(
         _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(k_scales), _ptr(v_scales), _ptr(page_table),
         page_table.stride(0), _ptr(seq_lens), B, Hq, Hkv, D, P, num_pages, int(num_splits),

@@ -105,7 +105,13 @@ spa_status spa_paged_decode_attention(const void *q, const void *k_pages, const 
         return SPA_ERR_INVALID_ARGUMENT;
     if (num_q_heads % num_kv_heads != 0) return SPA_ERR_INVALID_ARGUMENT;
     if (kv_dtype != SPA_KV_BF16 && kv_dtype != SPA_KV_INT8) return SPA_ERR_INVALID_ARGUMENT;
-    if ((flags & ~SPA_DECODE_SEPARATE_MERGE) != 0) return SPA_ERR_INVALID_ARGUMENT;
+    const uint32_t known = SPA_DECODE_SEPARATE_MERGE | SPA_DECODE_FUSED_MERGE |
+                           SPA_DECODE_HEAD_GROUPED | SPA_DECODE_PAGE_SPLIT;
+    if ((flags & ~known) != 0) return SPA_ERR_INVALID_ARGUMENT;
+    if ((flags & SPA_DECODE_SEPARATE_MERGE) && (flags & SPA_DECODE_FUSED_MERGE))
+        return SPA_ERR_INVALID_ARGUMENT;
+    if ((flags & SPA_DECODE_HEAD_GROUPED) && (flags & SPA_DECODE_PAGE_SPLIT))
+        return SPA_ERR_INVALID_ARGUMENT;
     if (!isfinite(scale)) return SPA_ERR_INVALID_ARGUMENT;
     if (head_dim != spa::kHeadDim || page_size != spa::kPageSize ||
         num_q_heads != spa::kGroup * num_kv_heads || num_splits > 1024)
@@ -147,8 +153,18 @@ spa_status spa_paged_decode_attention(const void *q, const void *k_pages, const 
     p.counters = reinterpret_cast<int32_t *>(ws + w.cnt_off);
     p.out = static_cast<uint16_t *>(out);
     p.lse = lse;
-    const bool fused = (flags & SPA_DECODE_SEPARATE_MERGE) == 0;
-    return hip_status(spa::launch_decode(p, kv_dtype == SPA_KV_INT8 ? 1 : 0, fused, stream));
+    spa::DecodeMode mode = spa::default_mode(batch, num_kv_heads, num_splits);
+    if (flags & SPA_DECODE_HEAD_GROUPED) mode = spa::DecodeMode::kHeadGrouped;
+    if (flags & SPA_DECODE_PAGE_SPLIT) mode = spa::DecodeMode::kPageSplit;
+    if (!spa::mode_supported(mode, num_kv_heads)) return SPA_ERR_UNSUPPORTED;
+    // Default merge: fused into the producer launch for page-split grids;
+    // a second launch after head-grouped grids, whose splits all finish
+    // together, so a merge inside the launch would run after every split.
+    bool fused = mode == spa::DecodeMode::kPageSplit;
+    if (flags & SPA_DECODE_SEPARATE_MERGE) fused = false;
+    if (flags & SPA_DECODE_FUSED_MERGE) fused = true;
+    return hip_status(
+        spa::launch_decode(p, kv_dtype == SPA_KV_INT8 ? 1 : 0, mode, fused, stream));
 }
 
 spa_status spa_split_merge(const float *partial_acc, const float *partial_max,

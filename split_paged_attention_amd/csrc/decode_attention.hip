@@ -43,6 +43,37 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));   // store operand type
+
+// Cache-policy immediate of buffer accesses for system-scope coherence
+// (sc0 sc1): stores write through to memory, loads bypass the caches.
+constexpr int kSysCoherent = 17;
+
+// Raw buffer loads, bit-cast to plain structs at once: reading lanes of the
+// builtins' vector results through a local vector variable was seen to
+// compile to a single-dword load whose value fills every lane.
+template <int AUX = 0>
+__device__ __forceinline__ void buf_st16(uint4 v, __amdgpu_buffer_rsrc_t r, int off) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, off, 0, AUX);
+}
+// AUX is the cache-policy immediate.
+template <int AUX = 0>
+__device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, int off, int soff) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, AUX));
+}
+template <int AUX = 0>
+__device__ __forceinline__ uint2 buf_ld8(__amdgpu_buffer_rsrc_t r, int off, int soff) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, AUX));
+}
+template <int AUX = 0>
+__device__ __forceinline__ float buf_ldf(__amdgpu_buffer_rsrc_t r, int off, int soff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, AUX));
+}
+
+// Word 3 of a gfx9 buffer resource for raw (untyped, unswizzled) access:
+// data format field = 32-bit, so dword loads of any width are range checked
+// against the descriptor's byte size.
+constexpr int kBufferWord3 = 0x00020000;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -118,24 +149,33 @@ __device__ __forceinline__ uint32_t i8_pair_f16(uint32_t wb, uint32_t wa) {
 }
 
 // ---------------------------------------------------------------------------
-// The log-sum-exp merge of one output element.  Shared, unchanged, by the
-// fused tail and by the separate merge kernel, so both give the same bits.
-// SYS_LOADS: read through to memory (system scope, no cached copy), used by
-// the fused tail, which reads state other workgroups published in this launch.
-template <bool SYS_LOADS>
-__device__ __forceinline__ float ld(const float *p) {
-    if constexpr (SYS_LOADS)
-        return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    else
-        return *p;
-}
-// Store that is written through to memory (system scope): visible to every
-// XCD once the issuing wave's store counter drains, with no L2 writeback.
-__device__ __forceinline__ void st_sys(float *p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+// The log-sum-exp merge.  Both merge paths (the fused tail and the separate
+// kernel) apply exactly the same per-element operations, in split order
+// j = 0..S-1, so they give the same bits:
+//   M = max_j m_j;  for each non-empty j: w = 2^((m_j - M) log2 e),
+//   l = fma(w, l_j, l),  o = fma(w, acc_j, o);  out = bf16(o / l), lse = M + ln l.
+// Loads are issued CH splits at a time so that their latencies overlap.
+constexpr int kMergeChunk = 8;
+
+template <int VEC>
+__device__ __forceinline__ void merge_step(float mj, float lj, const float (&aj)[VEC], float M,
+                                           float &l, float (&o)[VEC]) {
+    if (mj == kNegInf) return;   // empty split: weight 0
+    const float w = exp2_fast((mj - M) * kLog2e);
+    l = __builtin_fmaf(w, lj, l);
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) o[v] = __builtin_fmaf(w, aj[v], o[v]);
 }
 
-template <bool SYS_LOADS>
+template <int VEC>
+__device__ __forceinline__ void merge_finish(float M, float l, const float (&o)[VEC],
+                                             uint16_t *out, float *lse, bool write_lse) {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) out[v] = to_bf16_bits(l > 0.f ? o[v] / l : 0.f);
+    if (write_lse) *lse = l > 0.f ? M + __builtin_amdgcn_logf(l) * kLn2 : kNegInf;
+}
+
+// One output element of row (b, h), plain loads (separate merge kernel).
 __device__ __forceinline__ void merge_element(const float *__restrict__ acc,
                                               const float *__restrict__ mx,
                                               const float *__restrict__ sum, int splits,
@@ -145,48 +185,111 @@ __device__ __forceinline__ void merge_element(const float *__restrict__ acc,
     const float *mrow = mx + row * splits;
     const float *lrow = sum + row * splits;
     const float *arow = acc + row * splits * (int64_t)head_dim + d;
-    // Splits are visited in order j = 0..splits-1; loads are issued CH at a
-    // time (clamped indices, masked values) so their latencies overlap.
-    constexpr int CH = 8;
+    constexpr int CH = kMergeChunk;
     float M = kNegInf;
     for (int j0 = 0; j0 < splits; j0 += CH) {
         float mv[CH];
 #pragma unroll
-        for (int u = 0; u < CH; ++u) mv[u] = ld<SYS_LOADS>(mrow + min(j0 + u, splits - 1));
+        for (int u = 0; u < CH; ++u) mv[u] = mrow[min(j0 + u, splits - 1)];
 #pragma unroll
         for (int u = 0; u < CH; ++u) M = fmaxf(M, mv[u]);
     }
-    float l = 0.f, o = 0.f;
+    float l = 0.f, o[1] = {0.f};
     for (int j0 = 0; j0 < splits; j0 += CH) {
-        float mv[CH], lv[CH], av[CH];
+        float mv[CH], lv[CH], av[CH][1];
 #pragma unroll
         for (int u = 0; u < CH; ++u) {
             const int j = min(j0 + u, splits - 1);
-            mv[u] = ld<SYS_LOADS>(mrow + j);
-            lv[u] = ld<SYS_LOADS>(lrow + j);
-            av[u] = ld<SYS_LOADS>(arow + (int64_t)j * head_dim);
+            mv[u] = mrow[j];
+            lv[u] = lrow[j];
+            av[u][0] = arow[(int64_t)j * head_dim];
         }
 #pragma unroll
-        for (int u = 0; u < CH; ++u) {
-            if (j0 + u >= splits || mv[u] == kNegInf) continue;   // past the end / empty split
-            const float w = exp2_fast((mv[u] - M) * kLog2e);
-            l = __builtin_fmaf(w, lv[u], l);
-            o = __builtin_fmaf(w, av[u], o);
-        }
+        for (int u = 0; u < CH; ++u)
+            if (j0 + u < splits) merge_step<1>(mv[u], lv[u], av[u], M, l, o);
     }
-    const float res = l > 0.f ? o / l : 0.f;
-    out[row * head_dim + d] = to_bf16_bits(res);
-    if (lse != nullptr && d == 0)
-        lse[row] = l > 0.f ? M + __builtin_amdgcn_logf(l) * kLn2 : kNegInf;
+    merge_finish<1>(M, l, o, out + row * head_dim + d, lse != nullptr ? lse + row : nullptr,
+                    lse != nullptr && d == 0);
+}
+
+// VEC consecutive elements of one row, reading state that other workgroups
+// published in this launch: system-scope (cache-bypassing) buffer loads
+// through descriptors based at this group's first row (rows of one group
+// are contiguous).  m/l descriptor: [rows][S]; acc descriptor: [rows][S][D].
+template <int VEC>
+__device__ __forceinline__ void merge_vec_sys(__amdgpu_buffer_rsrc_t racc,
+                                              __amdgpu_buffer_rsrc_t rmax,
+                                              __amdgpu_buffer_rsrc_t rsum, int splits,
+                                              int head_dim, int hl, int d0, uint16_t *out,
+                                              float *lse, bool write_lse) {
+    static_assert(VEC == 2 || VEC == 4 || VEC == 8, "vector width");
+    constexpr int CH = kMergeChunk;
+    const int mrow = hl * splits * 4;                       // byte offsets
+    const int arow = (hl * splits * head_dim + d0) * 4;
+    auto ldf = [&](__amdgpu_buffer_rsrc_t r, int off) { return buf_ldf<kSysCoherent>(r, off, 0); };
+    float M = kNegInf;
+    for (int j0 = 0; j0 < splits; j0 += CH) {
+        float mv[CH];
+#pragma unroll
+        for (int u = 0; u < CH; ++u) mv[u] = ldf(rmax, mrow + 4 * min(j0 + u, splits - 1));
+#pragma unroll
+        for (int u = 0; u < CH; ++u) M = fmaxf(M, mv[u]);
+    }
+    float l = 0.f, o[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) o[v] = 0.f;
+    for (int j0 = 0; j0 < splits; j0 += CH) {
+        float mv[CH], lv[CH], av[CH][VEC];
+#pragma unroll
+        for (int u = 0; u < CH; ++u) {
+            const int j = min(j0 + u, splits - 1);
+            mv[u] = ldf(rmax, mrow + 4 * j);
+            lv[u] = ldf(rsum, mrow + 4 * j);
+            const int off = arow + j * head_dim * 4;
+            if constexpr (VEC == 2) {
+                const uint2 w = buf_ld8<kSysCoherent>(racc, off, 0);
+                av[u][0] = __uint_as_float(w.x);
+                av[u][1] = __uint_as_float(w.y);
+            } else {
+#pragma unroll
+                for (int q4 = 0; q4 < VEC / 4; ++q4) {
+                    const uint4 w = buf_ld16<kSysCoherent>(racc, off + 16 * q4, 0);
+                    av[u][4 * q4 + 0] = __uint_as_float(w.x);
+                    av[u][4 * q4 + 1] = __uint_as_float(w.y);
+                    av[u][4 * q4 + 2] = __uint_as_float(w.z);
+                    av[u][4 * q4 + 3] = __uint_as_float(w.w);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < CH; ++u)
+            if (j0 + u < splits) merge_step<VEC>(mv[u], lv[u], av[u], M, l, o);
+    }
+    merge_finish<VEC>(M, l, o, out, lse, write_lse);
+}
+
+// Store that is written through to memory (system scope): visible to every
+// XCD once the issuing wave's store counter drains, with no L2 writeback.
+__device__ __forceinline__ void st_sys(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 // ---------------------------------------------------------------------------
 // Producer (+ fused merge).
-template <int KV_INT8, int NW, bool FUSED>
-__global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
+// HG = false: a workgroup is one (request, kv head, split); its NW waves take
+//             the split's pages round robin and are merged through LDS.
+// HG = true:  a workgroup is one (request, block of NW kv heads, split); wave w
+//             is kv head block*NW + w and walks all the split's pages, so the
+//             NW waves read the same token rows of the same pages together.
+template <int KV_INT8, int NW, bool FUSED, bool HG>
+__global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
+                                                        const int32_t *__restrict__ page_table,
+                                                        const int32_t *__restrict__ seq_lens) {
     constexpr int D = kHeadDim, P = kPageSize;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    // wave index is uniform per wave; say so, so that page ids, buffer
+    // descriptors and loop bounds live in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15, g = lane >> 4;     // QK layout: token n of a 16-block, k-chunk g
     const int vr = lane >> 4, vc = lane & 15;   // PV layout: token phase r, dims 8c..8c+7
 
@@ -194,7 +297,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     // group get ids congruent mod 8 so they land on one XCD (dispatch is round
     // robin over the 8 XCDs) and share its L2 for the merge.
     const int S = p.splits;
-    const int ngroups = p.batch * p.hkv;
+    const int kv_per_grp = HG ? NW : 1;             // kv heads per workgroup
+    const int grp_per_b = p.hkv / kv_per_grp;
+    const int ngroups = p.batch * grp_per_b;
     int grp, j;
     {
         const int bid = blockIdx.x;
@@ -207,8 +312,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
             j = bid % S;
         }
     }
-    const int b = grp / p.hkv, kvh = grp - b * p.hkv;
-    const int L = p.seq_lens[b];
+    const int b = grp / grp_per_b;
+    const int kvh = (grp - b * grp_per_b) * kv_per_grp + (HG ? wave : 0);
+    const int L = seq_lens[b];
     const int pages = (L + P - 1) / P;
     const int pps = (pages + S - 1) / S;
     const int pg0 = min(j * pps, pages);
@@ -240,53 +346,98 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     __shared__ float sm_acc[NW][4][D];
     __shared__ int sm_last;
 
-    const int32_t *pt_row = p.page_table + (int64_t)b * p.pt_stride;
+    const int32_t *pt_row = page_table + (int64_t)b * p.pt_stride;
 
-    for (int pg = pg0 + wave; pg < pg1; pg += NW) {
+    // Tile registers.  K in MFMA B layout: lane (n, g) holds token 16t + n,
+    // dims 32c + 8g .. +8.  V in P.V layout: lane (r, c) holds token 4i + r,
+    // dims 8c .. 8c+7.  One page = 64 tokens per tile.
+    //
+    // Loads go through a buffer resource per (page, kv head) whose range ends
+    // after the page's last valid token row: rows past the context read as 0
+    // without touching memory (so V needs no masking), and a zero range turns
+    // the prefetch past the split's last page into a no-op.
+    constexpr int ES = KV_INT8 ? 1 : 2;                   // bytes per element
+    const int row_bytes = row_stride * ES;
+    const int k_lane = (n * row_stride + 8 * g) * ES;     // byte offsets inside a page
+    const int v_lane = (vr * row_stride + 8 * vc) * ES;
+    const int s_lane = n * p.hkv * 4;
+    uint4 kr[4][4];          // bf16 K
+    uint4 vr16[16];          // bf16 V
+    uint2 kr8[4][4];         // int8 K codes
+    uint2 vr8[16];           // int8 V codes
+    float ksc[4], vsc[4];    // int8 scales of token 16t + n
+    auto rsrc = [&](const void *base, int64_t page, int64_t elem_per_page, int64_t elem_off,
+                    int esize, int nbytes) {
+        const char *ptr = static_cast<const char *>(base) + (page * elem_per_page + elem_off) * esize;
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(ptr), (short)0, nbytes,
+                                                 kBufferWord3);
+    };
+    auto load_k = [&](int64_t page, int valid_rows) {
+        const auto r = rsrc(p.k_pages, page, (int64_t)P * row_stride, (int64_t)kvh * D, ES,
+                            valid_rows * row_bytes);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int off = k_lane + 32 * c * ES;
+                if constexpr (KV_INT8 == 0)
+                    kr[t][c] = buf_ld16(r, off, 16 * t * row_bytes);
+                else
+                    kr8[t][c] = buf_ld8(r, off, 16 * t * row_bytes);
+            }
+        if constexpr (KV_INT8 != 0) {
+            const auto rs = rsrc(p.k_scales, page, (int64_t)P * p.hkv, kvh, 4,
+                                 valid_rows * p.hkv * 4);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                ksc[t] = buf_ldf(rs, s_lane, 16 * t * p.hkv * 4);
+        }
+    };
+    auto load_v = [&](int64_t page, int valid_rows) {
+        const auto r = rsrc(p.v_pages, page, (int64_t)P * row_stride, (int64_t)kvh * D, ES,
+                            valid_rows * row_bytes);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if constexpr (KV_INT8 == 0)
+                vr16[i] = buf_ld16(r, v_lane, 4 * i * row_bytes);
+            else
+                vr8[i] = buf_ld8(r, v_lane, 4 * i * row_bytes);
+        }
+        if constexpr (KV_INT8 != 0) {
+            const auto rs = rsrc(p.v_scales, page, (int64_t)P * p.hkv, kvh, 4,
+                                 valid_rows * p.hkv * 4);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                vsc[t] = buf_ldf(rs, s_lane, 16 * t * p.hkv * 4);
+        }
+    };
+
+    // Software pipeline over this wave's pages: the next page's K loads are
+    // issued as soon as QK^T has consumed the K registers, its V loads as soon
+    // as P.V has consumed the V registers, so loads stay in flight while the
+    // current page is computed.
+    constexpr int PSTEP = HG ? 1 : NW;              // page stride of one wave
+    int pg = HG ? pg0 : pg0 + wave;
+    if (pg < pg1) {
         const int64_t page = pt_row[pg];
-        const int64_t page_elem = page * (int64_t)(P * row_stride) + (int64_t)kvh * D;
-        const int tok0 = pg * P;
-        const int valid = min(P, L - tok0);         // tokens of this page that count
+        const int valid = min(P, L - pg * P);
+        load_k(page, valid);
+        load_v(page, valid);
+    }
+    for (; pg < pg1; pg += PSTEP) {
+        const int nxt = pg + PSTEP;
+        const bool has_next = nxt < pg1;
+        const int64_t page_next = has_next ? (int64_t)pt_row[nxt] : 0;
+        const int valid_next = has_next ? min(P, L - nxt * P) : 0;
+        const int valid = min(P, L - pg * P);       // tokens of this page that count
 
-        // ---- loads: K in MFMA B layout, V in PV layout
         bf16x8_t kb[4][4];
-        uint32_t vw[16][4];      // bf16 V words (bf16 pages)
-        uint2 vraw[16];          // int8 V codes (int8 pages)
-        float ksc[4], vsc[4];
         if constexpr (KV_INT8 == 0) {
-            const uint16_t *kp = reinterpret_cast<const uint16_t *>(p.k_pages) + page_elem;
-            const uint16_t *vp = reinterpret_cast<const uint16_t *>(p.v_pages) + page_elem;
 #pragma unroll
             for (int t = 0; t < 4; ++t)
 #pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    kb[t][c] = *reinterpret_cast<const bf16x8_t *>(
-                        kp + (16 * t + n) * row_stride + 32 * c + 8 * g);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const uint4 w = *reinterpret_cast<const uint4 *>(
-                    vp + (4 * i + vr) * row_stride + 8 * vc);
-                vw[i][0] = w.x; vw[i][1] = w.y; vw[i][2] = w.z; vw[i][3] = w.w;
-            }
+                for (int c = 0; c < 4; ++c) kb[t][c] = __builtin_bit_cast(bf16x8_t, kr[t][c]);
         } else {
-            const int8_t *kp = reinterpret_cast<const int8_t *>(p.k_pages) + page_elem;
-            const int8_t *vp = reinterpret_cast<const int8_t *>(p.v_pages) + page_elem;
-            uint2 kraw[4][4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    kraw[t][c] = *reinterpret_cast<const uint2 *>(
-                        kp + (16 * t + n) * row_stride + 32 * c + 8 * g);
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                vraw[i] = *reinterpret_cast<const uint2 *>(vp + (4 * i + vr) * row_stride + 8 * vc);
-            const int64_t srow = page * (int64_t)(P * p.hkv) + kvh;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                ksc[t] = p.k_scales[srow + (int64_t)(16 * t + n) * p.hkv];
-                vsc[t] = p.v_scales[srow + (int64_t)(16 * t + n) * p.hkv];
-            }
             // int8 -> bf16 (exact)
 #pragma unroll
             for (int t = 0; t < 4; ++t)
@@ -295,12 +446,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
                     uint32_t wds[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const uint32_t src = e < 2 ? kraw[t][c].x : kraw[t][c].y;
+                        const uint32_t src = e < 2 ? kr8[t][c].x : kr8[t][c].y;
                         const int k0 = (e & 1) * 2;
                         wds[e] = pack_hi16(i8_bf16_hi(src, k0), i8_bf16_hi(src, k0 + 1));
                     }
-                    uint4 u = make_uint4(wds[0], wds[1], wds[2], wds[3]);
-                    kb[t][c] = __builtin_bit_cast(bf16x8_t, u);
+                    kb[t][c] = __builtin_bit_cast(bf16x8_t, make_uint4(wds[0], wds[1], wds[2], wds[3]));
                 }
         }
 
@@ -321,6 +471,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
 #pragma unroll
             for (int h = 0; h < 4; ++h) s[t][h] = ok ? sacc[t][h] * f : kNegInf;
         }
+        // keep the prefetch after the last read of the K registers it reuses
+        __builtin_amdgcn_sched_barrier(0);
+        load_k(page_next, valid_next);
+        __builtin_amdgcn_sched_barrier(0);
 
         // ---- online softmax (base 2)
         float alpha[4], pv[4][4];
@@ -343,7 +497,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
         // ---- probabilities for P.V: pair (token 32q + n, token 32q + 16 + n),
         // packed bf16; stored by row 0 of the wave as pbuf[pair u][phase r][h]
         // with u = 4q + n/4, r = n % 4.
-        if (g == 0) {
+        {   // every row g holds the same values, so all lanes may store
 #pragma unroll
             for (int qq = 0; qq < 2; ++qq) {
                 uint4 w;
@@ -382,25 +536,18 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
             if constexpr (KV_INT8 != 0) psum[h] *= alpha[h];
         }
         if constexpr (KV_INT8 == 0) {
-            // rows past the context may hold anything (even NaN): zero them,
-            // their probabilities are already 0
-            if (valid < P) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    if (4 * i + vr >= valid) {
-                        vw[i][0] = 0u; vw[i][1] = 0u; vw[i][2] = 0u; vw[i][3] = 0u;
-                    }
-            }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const uint4 pk = *reinterpret_cast<const uint4 *>(&pbuf[wave][u][vr][0]);
                 const int ia = u < 4 ? u : u + 4;       // token 4*ia + r
                 const int ib = ia + 4;                  // token 4*ia + r + 16
                 const uint32_t ph[4] = {pk.x, pk.y, pk.z, pk.w};
+                const uint32_t wa[4] = {vr16[ia].x, vr16[ia].y, vr16[ia].z, vr16[ia].w};
+                const uint32_t wb[4] = {vr16[ib].x, vr16[ib].y, vr16[ib].z, vr16[ib].w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const uint32_t lo = __builtin_amdgcn_perm(vw[ib][e], vw[ia][e], 0x05040100u);
-                    const uint32_t hi = __builtin_amdgcn_perm(vw[ib][e], vw[ia][e], 0x07060302u);
+                    const uint32_t lo = __builtin_amdgcn_perm(wb[e], wa[e], 0x05040100u);
+                    const uint32_t hi = __builtin_amdgcn_perm(wb[e], wa[e], 0x07060302u);
 #pragma unroll
                     for (int h = 0; h < 4; ++h) {
                         acc[h][2 * e] = dot2(ph[h], lo, acc[h][2 * e]);
@@ -420,14 +567,14 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
 #pragma unroll
                 for (int h = 0; h < 4; ++h) psum[h] = dot2_f16(ph[h], kF16One2, psum[h]);
                 uint32_t vp[8];
-                vp[0] = i8_pair_f16<0>(vraw[ib].x, vraw[ia].x);
-                vp[1] = i8_pair_f16<1>(vraw[ib].x, vraw[ia].x);
-                vp[2] = i8_pair_f16<2>(vraw[ib].x, vraw[ia].x);
-                vp[3] = i8_pair_f16<3>(vraw[ib].x, vraw[ia].x);
-                vp[4] = i8_pair_f16<0>(vraw[ib].y, vraw[ia].y);
-                vp[5] = i8_pair_f16<1>(vraw[ib].y, vraw[ia].y);
-                vp[6] = i8_pair_f16<2>(vraw[ib].y, vraw[ia].y);
-                vp[7] = i8_pair_f16<3>(vraw[ib].y, vraw[ia].y);
+                vp[0] = i8_pair_f16<0>(vr8[ib].x, vr8[ia].x);
+                vp[1] = i8_pair_f16<1>(vr8[ib].x, vr8[ia].x);
+                vp[2] = i8_pair_f16<2>(vr8[ib].x, vr8[ia].x);
+                vp[3] = i8_pair_f16<3>(vr8[ib].x, vr8[ia].x);
+                vp[4] = i8_pair_f16<0>(vr8[ib].y, vr8[ia].y);
+                vp[5] = i8_pair_f16<1>(vr8[ib].y, vr8[ia].y);
+                vp[6] = i8_pair_f16<2>(vr8[ib].y, vr8[ia].y);
+                vp[7] = i8_pair_f16<3>(vr8[ib].y, vr8[ia].y);
 #pragma unroll
                 for (int d = 0; d < 8; ++d)
 #pragma unroll
@@ -435,6 +582,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
             }
         }
         __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        load_v(page_next, valid_next);
+        __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (KV_INT8 != 0) {
         // remove the 1152 bias carried by every f16 value code
@@ -456,50 +606,81 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
             acc[h][d] = x;
         }
     }
-    if (lane == 0) {
+    // Partial-state writes: write-through stores in the fused mode (read back
+    // by another workgroup in this launch), plain stores otherwise.
+    auto put = [&](float *ptr, float v) {
+        if constexpr (FUSED) st_sys(ptr, v);
+        else *ptr = v;
+    };
+    if constexpr (HG) {
+        // One wave = one kv head: write its split state straight from
+        // registers.  After the butterfly every lane holds the reduced sums
+        // for its 8 dims, so lane group r publishes head r: two 16-byte
+        // stores per lane cover the wave's 4 heads x 128 dims.
+        const int64_t idx0 = ((int64_t)b * p.hq + kvh * kGroup) * S + j;
+        float v8[8];
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-            sm_m[wave][h] = m[h];
-            sm_l[wave][h] = lpart[h];
-        }
-    }
-    if (lane < 16) {
-#pragma unroll
-        for (int h = 0; h < 4; ++h)
-#pragma unroll
-            for (int d = 0; d < 8; ++d) sm_acc[wave][h][8 * vc + d] = acc[h][d];
-    }
-    __syncthreads();
-
-    // ---- merge the NW waves (wave order) and write this split's partial state
-    const int64_t head0 = (int64_t)b * p.hq + kvh * kGroup;
-    for (int e = threadIdx.x; e < kGroup * D; e += NW * 64) {
-        const int h = e / D, d = e - h * D;
-        float M = kNegInf;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][h]);
-        float l = 0.f, o = 0.f;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            const float mw = sm_m[w][h];
-            if (mw == kNegInf) continue;
-            const float wt = exp2_fast(mw - M);
-            l = __builtin_fmaf(wt, sm_l[w][h], l);
-            o = __builtin_fmaf(wt, sm_acc[w][h][d], o);
-        }
-        const int64_t idx = (head0 + h) * S + j;
-        const float mnat = M == kNegInf ? kNegInf : M * kLn2;
+        for (int d = 0; d < 8; ++d)
+            v8[d] = vr == 0 ? acc[0][d] : vr == 1 ? acc[1][d] : vr == 2 ? acc[2][d] : acc[3][d];
+        const uint4 lo = make_uint4(__float_as_uint(v8[0]), __float_as_uint(v8[1]),
+                                    __float_as_uint(v8[2]), __float_as_uint(v8[3]));
+        const uint4 hi = make_uint4(__float_as_uint(v8[4]), __float_as_uint(v8[5]),
+                                    __float_as_uint(v8[6]), __float_as_uint(v8[7]));
+        const int off = (vr * S * D + 8 * vc) * 4;   // bytes from this wave's first row
         if constexpr (FUSED) {
-            st_sys(p.part_acc + idx * D + d, o);
-            if (d == 0) {
-                st_sys(p.part_max + idx, mnat);
-                st_sys(p.part_sum + idx, l);
-            }
+            const auto r = __builtin_amdgcn_make_buffer_rsrc(p.part_acc + idx0 * D, (short)0,
+                                                             (3 * S + 1) * D * 4, kBufferWord3);
+            buf_st16<kSysCoherent>(lo, r, off);
+            buf_st16<kSysCoherent>(hi, r, off + 16);
         } else {
-            p.part_acc[idx * D + d] = o;
+            char *base = reinterpret_cast<char *>(p.part_acc + idx0 * D) + off;
+            *reinterpret_cast<uint4 *>(base) = lo;
+            *reinterpret_cast<uint4 *>(base + 16) = hi;
+        }
+        if (lane == 0) {
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                put(p.part_max + idx0 + (int64_t)h * S, m[h] == kNegInf ? kNegInf : m[h] * kLn2);
+                put(p.part_sum + idx0 + (int64_t)h * S, lpart[h]);
+            }
+        }
+    } else {
+        if (lane == 0) {
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                sm_m[wave][h] = m[h];
+                sm_l[wave][h] = lpart[h];
+            }
+        }
+        if (lane < 16) {
+#pragma unroll
+            for (int h = 0; h < 4; ++h)
+#pragma unroll
+                for (int d = 0; d < 8; ++d) sm_acc[wave][h][8 * vc + d] = acc[h][d];
+        }
+        __syncthreads();
+
+        // merge the NW waves (wave order) and write this split's partial state
+        const int64_t head0 = (int64_t)b * p.hq + kvh * kGroup;
+        for (int e = threadIdx.x; e < kGroup * D; e += NW * 64) {
+            const int h = e / D, d = e - h * D;
+            float M = kNegInf;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][h]);
+            float l = 0.f, o = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const float mw = sm_m[w][h];
+                if (mw == kNegInf) continue;
+                const float wt = exp2_fast(mw - M);
+                l = __builtin_fmaf(wt, sm_l[w][h], l);
+                o = __builtin_fmaf(wt, sm_acc[w][h][d], o);
+            }
+            const int64_t idx = (head0 + h) * S + j;
+            put(p.part_acc + idx * D + d, o);
             if (d == 0) {
-                p.part_max[idx] = mnat;
-                p.part_sum[idx] = l;
+                put(p.part_max + idx, M == kNegInf ? kNegInf : M * kLn2);
+                put(p.part_sum + idx, l);
             }
         }
     }
@@ -519,11 +700,24 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
         }
         __syncthreads();
         if (sm_last) {
-            for (int e = threadIdx.x; e < kGroup * D; e += NW * 64) {
-                const int h = e / D, d = e - h * D;
-                merge_element<true>(p.part_acc, p.part_max, p.part_sum, S, D, head0 + h, d,
-                                    p.out, p.lse);
-            }
+            // all query heads of this workgroup's kv heads: HEADS rows of
+            // D outputs, VEC consecutive outputs per thread
+            constexpr int HEADS = (HG ? NW : 1) * kGroup;
+            constexpr int VEC = HEADS * D / (NW * 64);
+            static_assert(VEC * NW * 64 == HEADS * D, "merge tiling");
+            const int64_t mhead0 = (int64_t)b * p.hq + (grp - b * grp_per_b) * kv_per_grp * kGroup;
+            const int rows_bytes = HEADS * S * 4;
+            const auto racc = __builtin_amdgcn_make_buffer_rsrc(p.part_acc + mhead0 * S * D, (short)0,
+                                                                rows_bytes * D, kBufferWord3);
+            const auto rmax = __builtin_amdgcn_make_buffer_rsrc(p.part_max + mhead0 * S, (short)0,
+                                                                rows_bytes, kBufferWord3);
+            const auto rsum = __builtin_amdgcn_make_buffer_rsrc(p.part_sum + mhead0 * S, (short)0,
+                                                                rows_bytes, kBufferWord3);
+            const int e0 = threadIdx.x * VEC;
+            const int hl = e0 / D, d0 = e0 - hl * D;
+            merge_vec_sys<VEC>(racc, rmax, rsum, S, D, hl, d0, p.out + (mhead0 + hl) * D + d0,
+                               p.lse != nullptr ? p.lse + (mhead0 + hl) : nullptr,
+                               p.lse != nullptr && d0 == 0);
             if (threadIdx.x == 0)
                 __hip_atomic_store(p.counters + grp, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         }
@@ -539,7 +733,7 @@ __global__ __launch_bounds__(128) void split_merge_kernel(const float *__restric
                                                           float *__restrict__ lse) {
     const int64_t row = blockIdx.x;
     for (int d = threadIdx.x; d < head_dim; d += blockDim.x)
-        merge_element<false>(acc, mx, sum, splits, head_dim, row, d, out, lse);
+        merge_element(acc, mx, sum, splits, head_dim, row, d, out, lse);
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t *__restrict__ ptr, size_t words) {
@@ -548,23 +742,53 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t *__restrict__ p
         ptr[i] = 0u;
 }
 
-template <int KV, int NW>
+template <int KV, int NW, bool HG>
 hipError_t launch_nw(const DecodeParams &p, bool fused, hipStream_t stream) {
-    const unsigned grid = (unsigned)(p.batch * p.hkv * p.splits);
+    const int kv_per_grp = HG ? NW : 1;
+    const unsigned grid = (unsigned)(p.batch * (p.hkv / kv_per_grp) * p.splits);
     if (fused)
-        hipLaunchKernelGGL((decode_kernel<KV, NW, true>), dim3(grid), dim3(NW * 64), 0, stream, p);
+        hipLaunchKernelGGL((decode_kernel<KV, NW, true, HG>), dim3(grid), dim3(NW * 64), 0, stream,
+                           p, p.page_table, p.seq_lens);
     else
-        hipLaunchKernelGGL((decode_kernel<KV, NW, false>), dim3(grid), dim3(NW * 64), 0, stream, p);
+        hipLaunchKernelGGL((decode_kernel<KV, NW, false, HG>), dim3(grid), dim3(NW * 64), 0, stream,
+                           p, p.page_table, p.seq_lens);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeParams &p, int kv_int8, bool fused, hipStream_t stream) {
-    hipError_t err = kv_int8 ? launch_nw<1, 4>(p, fused, stream) : launch_nw<0, 4>(p, fused, stream);
+// Producer shapes.  Head-grouped: 2 kv heads per workgroup, each wave walks
+// all pages of its split (long per-wave streams, row-aligned reads).
+// Page-split: one kv head per workgroup, 4 waves sharing its pages (4x the
+// waves, for grids too small to fill the GPU otherwise).
+constexpr int kNwHeadGrouped = 2;
+constexpr int kNwPageSplit = 4;
+// One wave per (request, kv head, split) fills 2 waves per SIMD from here on.
+constexpr int64_t kHeadGroupedMinWaves = 2048;
+
+hipError_t launch_decode(const DecodeParams &p, int kv_int8, DecodeMode mode, bool fused,
+                         hipStream_t stream) {
+    const bool hg = mode == DecodeMode::kHeadGrouped;
+    hipError_t err;
+    if (hg)
+        err = kv_int8 ? launch_nw<1, kNwHeadGrouped, true>(p, fused, stream)
+                      : launch_nw<0, kNwHeadGrouped, true>(p, fused, stream);
+    else
+        err = kv_int8 ? launch_nw<1, kNwPageSplit, false>(p, fused, stream)
+                      : launch_nw<0, kNwPageSplit, false>(p, fused, stream);
     if (err != hipSuccess || fused) return err;
     return launch_split_merge(p.part_acc, p.part_max, p.part_sum, p.batch * p.hq, kHeadDim,
                               p.splits, p.out, p.lse, stream);
+}
+
+DecodeMode default_mode(int batch, int hkv, int splits) {
+    const int64_t waves = (int64_t)batch * hkv * splits;
+    if (hkv % kNwHeadGrouped == 0 && waves >= kHeadGroupedMinWaves) return DecodeMode::kHeadGrouped;
+    return DecodeMode::kPageSplit;
+}
+
+bool mode_supported(DecodeMode mode, int hkv) {
+    return mode == DecodeMode::kPageSplit || hkv % kNwHeadGrouped == 0;
 }
 
 hipError_t launch_split_merge(const float *acc, const float *mx, const float *sum,

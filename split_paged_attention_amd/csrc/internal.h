@@ -47,9 +47,16 @@ hipError_t launch_build_page_table(const int32_t *req_to_token, int64_t req_to_t
                                    int64_t page_table_stride, int32_t *cache_seqlens,
                                    int32_t *cu_seqlens_k, hipStream_t stream);
 
+// Producer workgroup shape (same arithmetic per split, different rounding of
+// the in-workgroup combination, so one shape always uses one mode).
+enum class DecodeMode { kPageSplit, kHeadGrouped };
+DecodeMode default_mode(int batch, int hkv, int splits);
+bool mode_supported(DecodeMode mode, int hkv);
+
 // kv_int8: 0 = bf16 pages, 1 = int8 pages.  fused: merge in the last split
-// workgroup; otherwise only the partial state is written.
-hipError_t launch_decode(const DecodeParams &p, int kv_int8, bool fused, hipStream_t stream);
+// workgroup; otherwise a separate merge launch follows the producer.
+hipError_t launch_decode(const DecodeParams &p, int kv_int8, DecodeMode mode, bool fused,
+                         hipStream_t stream);
 
 hipError_t launch_split_merge(const float *acc, const float *mx, const float *sum,
                               int32_t rows, int32_t head_dim, int32_t splits, uint16_t *out,

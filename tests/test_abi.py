@@ -64,7 +64,11 @@ def _attn(**kw):
     (dict(Hq=30), spa.SPA_ERR_INVALID_ARGUMENT),            # Hq % Hkv != 0
     (dict(S=0), spa.SPA_ERR_INVALID_ARGUMENT),
     (dict(kvd=7), spa.SPA_ERR_INVALID_ARGUMENT),
-    (dict(flags=2), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(flags=16), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(flags=3), spa.SPA_ERR_INVALID_ARGUMENT),            # both merge placements
+    (dict(flags=12), spa.SPA_ERR_INVALID_ARGUMENT),           # both producer shapes
+    (dict(Hq=12, Hkv=3, flags=4), spa.SPA_ERR_UNSUPPORTED),   # head-grouped needs even Hkv
+    (dict(B=0, flags=2 | 4), spa.SPA_OK),
     (dict(scale=math.nan), spa.SPA_ERR_INVALID_ARGUMENT),
     (dict(scale=math.inf), spa.SPA_ERR_INVALID_ARGUMENT),
     (dict(pts=0), spa.SPA_ERR_INVALID_ARGUMENT),

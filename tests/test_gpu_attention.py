@@ -14,6 +14,8 @@ from tests.gpu_util import (DevCase, bf16_dev, bits_host, compare_attention, con
 
 pytestmark = pytest.mark.gpu
 
+PRODUCERS = ["page_split", "head_grouped"]
+
 
 def small_case(lens, kv="bf16", S=4, seed=21, num_pages=None, q_override=None, Hkv=8):
     P = 64
@@ -41,8 +43,9 @@ def test_config_parity_full(cfg):
 
 
 def test_config4_headline_parity():
-    """Batch 32 / context 8K in the launch configuration the benchmark times,
-    every output checked (the oracle finishes it in seconds)."""
+    """Batch 32 / context 8K in the launch configuration the benchmark times
+    (library defaults), every output checked (the oracle finishes it in
+    seconds); then both producers with both merges, bit-identical per producer."""
     c = config_case(4)
     print(f"[case] attention config 4 ({c.name}) full parity", flush=True)
     d = DevCase(c)
@@ -50,10 +53,17 @@ def test_config4_headline_parity():
     out, lse = d.attention(page_table=pt)
     o_ref, l_ref = oracle.case_attention(c)
     compare_attention(out, lse, o_ref, l_ref, label=c.name)
+    for producer in PRODUCERS:
+        o1, l1 = d.attention(page_table=pt, producer=producer, merge="fused")
+        compare_attention(o1, l1, o_ref, l_ref, label=f"{c.name} {producer} fused")
+        o2, l2 = d.attention(page_table=pt, producer=producer, merge="separate")
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
 
 
 # ---------------------------------------------------------------- ragged / edges
 
+@pytest.mark.parametrize("producer", PRODUCERS)
 @pytest.mark.parametrize("kv", ["bf16", "int8"])
 @pytest.mark.parametrize("lens,S", [
     ([1, 63, 64, 65], 1),
@@ -62,10 +72,10 @@ def test_config4_headline_parity():
     ([4096, 5, 64, 191], 64),       # many empty splits
     ([8192, 8191, 1], 16),
 ])
-def test_ragged_parity(lens, S, kv):
+def test_ragged_parity(lens, S, kv, producer):
     c = small_case(lens, kv=kv, S=S)
-    print(f"[case] ragged {c.name}", flush=True)
-    out, lse = DevCase(c).attention()
+    print(f"[case] ragged {c.name} {producer}", flush=True)
+    out, lse = DevCase(c).attention(producer=producer)
     o_ref, l_ref = oracle.case_attention(c)
     compare_attention(out, lse, o_ref, l_ref, label=c.name)
 
@@ -109,13 +119,14 @@ def test_large_logits():
 
 # ---------------------------------------------------------------- structure
 
+@pytest.mark.parametrize("producer", PRODUCERS)
 @pytest.mark.parametrize("kv", ["bf16", "int8"])
-def test_fused_equals_two_launch_bit_exact(kv):
+def test_fused_equals_two_launch_bit_exact(kv, producer):
     c = small_case([3000, 64, 1, 777], kv=kv, S=16)
-    print(f"[case] fused vs separate merge {kv}", flush=True)
+    print(f"[case] fused vs separate merge {kv} {producer}", flush=True)
     d = DevCase(c)
-    o1, l1 = d.attention()
-    o2, l2 = d.attention(separate_merge=True)
+    o1, l1 = d.attention(merge="fused", producer=producer)
+    o2, l2 = d.attention(merge="separate", producer=producer)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(l1, l2)
