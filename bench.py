@@ -1,19 +1,23 @@
 """Benchmark of the split-K paged-attention decode step on one MI355X.
 
 One step = the whole hot path on one batch: the page table / cache_seqlens /
-cu_seqlens_k build (one launch) followed by split-K paged-attention decode
-(one launch, producer + fused log-sum-exp merge).  Default workload: batch 32,
-context 8192, 32 query / 8 KV heads, head_dim 128, bf16 K/V in 64-token pages
-scattered over a 4096-page pool, 16 splits -- lmdeploy's headline H200 shape.
+cu_seqlens_k build (one launch) followed by one split-K paged-attention decode
+call with the library's default choices (producer plus log-sum-exp merge; at
+the default workload the head-grouped producer and a second, merge launch).
+Default workload: batch 32, context 8192, 32 query / 8 KV heads, head_dim 128,
+bf16 K/V in 64-token pages scattered over a 4096-page pool, 16 splits --
+lmdeploy's headline H200 shape.
 
 Timing: W untimed warm-up steps, then exactly K steps between two device
 synchronisations; HIP events on the launch stream bracket every attention
-launch, giving the attention kernel's average duration.  Two copies of the KV
-pool alternate so that consecutive steps do not read the same addresses.  A
-HIP-graph replay of the step is timed as well (the pages quote CUDA-graph
-latency).  The fp64 CPU oracle is timed on the host beside it.
+call, giving its average duration (both launches of the call, and the gap
+between them, fall inside).  Two copies of the KV pool alternate so that
+consecutive steps do not read the same addresses.  A HIP-graph replay of the
+step is timed as well (the pages quote CUDA-graph latency).  The fp64 CPU
+oracle is timed on the host beside it.
 
-Prints ONE JSON line.
+Prints ONE JSON line.  --summarize-pmc turns two rocprofv3 counter runs
+(FETCH_SIZE, WRITE_SIZE) into the HBM-traffic record the bench reports.
 """
 import argparse
 import json
@@ -25,6 +29,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0   # MI355X HBM3E peak, GB/s
+
+# Context only (another machine): split-K paged-attention CUDA-graph latency on
+# H200 before PDL, from the lmdeploy PR "use PDL for paged attention",
+# Performance table.  Not a target and not used for vs_baseline, whose unit
+# (GB/s) the page does not report.
+H200_GRAPH_US = {"b1_ctx1k_s4_bf16": 12.096, "b1_ctx8k_s16_bf16": 22.080,
+                 "b8_ctx1k_s4_bf16": 21.376, "b32_ctx8k_s16_bf16": 260.384}
 
 
 def _traffic_for(kernel_file: str, workload: str):
@@ -44,6 +55,70 @@ def _traffic_for(kernel_file: str, workload: str):
         return None
 
 
+def _pmc_rows(d: str):
+    """Rows of every rocprofv3 counter_collection.csv under directory d."""
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _per_dispatch(rows, counter: str, match) -> list:
+    """Counter value per dispatch (summed over its dimension rows) for kernels
+    whose name satisfies match()."""
+    acc = {}
+    for r in rows:
+        if r.get("Counter_Name") != counter or not match(r.get("Kernel_Name", "")):
+            continue
+        key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+        acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
+    return list(acc.values())
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str, out_path: str, copy_mib: int, workload: str,
+                  commands: list) -> dict:
+    """HBM bytes per decode call from two rocprofv3 --pmc runs (FETCH_SIZE, then
+    WRITE_SIZE, both in KiB per dispatch), each scaled by what the same counter
+    reads for a device copy of copy_mib MiB (which moves exactly that many bytes
+    each way)."""
+    import hashlib
+    import statistics
+    fr, wr = _pmc_rows(fetch_dir), _pmc_rows(write_dir)
+    is_copy = lambda k: "copyBuffer" in k or "elementwise" in k or "copy" in k.lower()
+    rec = {"workload": workload, "commands": commands, "copy_reference_bytes": copy_mib << 20,
+           "kernels": {}}
+    nbytes = copy_mib << 20
+    cf = [v for v in _per_dispatch(fr, "FETCH_SIZE", is_copy) if v > 0]
+    cw = [v for v in _per_dispatch(wr, "WRITE_SIZE", is_copy) if v > 0]
+    fscale = nbytes / (1024.0 * max(cf)) if cf else None
+    wscale = nbytes / (1024.0 * max(cw)) if cw else None
+    rec["fetch_scale"] = fscale
+    rec["write_scale"] = wscale
+    total = 0.0
+    for short, pat in (("decode", "decode_kernel"), ("split_merge", "split_merge_kernel"),
+                       ("page_table", "build_page_table_kernel")):
+        f = _per_dispatch(fr, "FETCH_SIZE", lambda k, pat=pat: pat in k)
+        w = _per_dispatch(wr, "WRITE_SIZE", lambda k, pat=pat: pat in k)
+        if not f or not w or fscale is None or wscale is None:
+            continue
+        fb = statistics.median(f) * 1024.0 * fscale
+        wb = statistics.median(w) * 1024.0 * wscale
+        rec["kernels"][short] = {"fetch_bytes": round(fb), "write_bytes": round(wb),
+                                 "dispatches": len(f)}
+        if short in ("decode", "split_merge"):
+            total += fb + wb
+    src = open(os.path.join(ROOT, "split_paged_attention_amd", "csrc", "decode_attention.hip"),
+               "rb").read()
+    rec["kernel_source_sha256"] = hashlib.sha256(src).hexdigest()
+    rec["hbm_bytes_per_launch"] = round(total)
+    with open(out_path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    return rec
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -53,12 +128,28 @@ def main() -> int:
     ap.add_argument("--graph-replays", type=int, default=200)
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-ref-mib", type=int, default=0,
+                    help="after timing, run device copies of this size (counter scaling)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc runs into a traffic record and exit")
+    ap.add_argument("--pmc-out", default=None)
+    ap.add_argument("--pmc-commands", nargs="*", default=[])
     args = ap.parse_args()
+
+    if args.summarize_pmc:
+        import workloads as W
+        name = W.CONFIGS[args.config]["name"]
+        out = args.pmc_out or os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+        rec = summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], out,
+                            args.copy_ref_mib or 1024, name, args.pmc_commands)
+        print(json.dumps(rec), flush=True)
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this path has no multi-GPU mode "
-              "(batch rows and KV heads shard with no exchange; see DESIGN.md).", file=sys.stderr)
+        print("bench.py measures one GPU only: this decode path has no multi-GPU mode "
+              "(batch rows and KV heads would shard across GPUs with no exchange).",
+              file=sys.stderr)
         return 2
 
     import numpy as np
@@ -137,34 +228,53 @@ def main() -> int:
     attn_us = [ev_s[i].elapsed_time(ev_e[i]) * 1e3 for i in range(K)]
     attn_us_mean = float(np.mean(attn_us))
 
-    # HIP-graph replay of the whole step (both KV copies, alternating)
-    graphs = []
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
+    if args.copy_ref_mib > 0:
+        # device copies of a known size, for scaling the memory counters
+        src_buf = torch.empty(args.copy_ref_mib << 20, dtype=torch.uint8, device=dev)
+        dst_buf = torch.empty_like(src_buf)
+        for _ in range(2):
+            dst_buf.copy_(src_buf)
+        torch.cuda.synchronize()
+        del src_buf, dst_buf
+
+    # HIP-graph replays: the whole step, and the attention call alone (the
+    # pages quote CUDA-graph latency of the attention), two graphs each over
+    # the two KV copies.  Timed back to back: R replays between two events.
+    def capture(fn):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(2):
+                fn(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        gl = []
         for i in range(2):
-            k1()
-            attn(i)
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    for i in range(2):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            k1()
-            attn(i)
-        graphs.append(g)
-    for i in range(20):
-        graphs[i % 2].replay()
-    torch.cuda.synchronize()
-    R = args.graph_replays
-    gs = [torch.cuda.Event(enable_timing=True) for _ in range(R)]
-    ge = [torch.cuda.Event(enable_timing=True) for _ in range(R)]
-    for i in range(R):
-        gs[i].record()
-        graphs[i % 2].replay()
-        ge[i].record()
-    torch.cuda.synchronize()
-    graph_us = np.array([gs[i].elapsed_time(ge[i]) * 1e3 for i in range(R)])
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn(i)
+            gl.append(g)
+        return gl
+
+    def time_graphs(gl, R):
+        for i in range(20):
+            gl[i % 2].replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(R):
+            gl[i % 2].replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / R
+
+    def step_fn(i):
+        k1()
+        attn(i)
+
+    R = max(1, args.graph_replays)
+    graph_step_us = time_graphs(capture(step_fn), R)
+    graph_attn_us = time_graphs(capture(attn), R)
 
     nbytes = W.algorithmic_bytes(case)
     achieved = nbytes / (attn_us_mean * 1e-6) / 1e9
@@ -205,12 +315,12 @@ def main() -> int:
                    "ragged": bool(np.any(case.seq_lens != case.seq_lens[0])),
                    "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D, "page_size": P,
                    "num_pages": case.num_pages, "num_splits": S, "kv_dtype": case.kv_dtype,
-                   "step": "page-table build + fused split-K decode attention"},
+                   "step": "page-table build + split-K decode attention (library defaults)"},
         "us_per_call": round(attn_us_mean, 3),
         "pct_of_peak": round(100.0 * achieved / PEAK_HBM_GBS, 2),
-        "graph_step_us": {"p10": round(float(np.percentile(graph_us, 10)), 3),
-                          "p50": round(float(np.percentile(graph_us, 50)), 3),
-                          "p90": round(float(np.percentile(graph_us, 90)), 3)},
+        "graph_step_us": round(graph_step_us, 3),
+        "graph_attn_us": round(graph_attn_us, 3),
+        "context_h200_graph_attn_us": H200_GRAPH_US.get(case.name),
         "algorithmic_bytes": int(nbytes),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),

@@ -21,7 +21,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# SPA_ORACLE_LIB lets the mutant test point the pins at a deliberately broken
+# copy of the oracle; nothing else sets it.
+_LIB_PATH = os.environ.get("SPA_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 KV_BF16 = 0
