@@ -312,9 +312,28 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
             j = bid % S;
         }
     }
-    const int b = grp / grp_per_b;
-    const int kvh = (grp - b * grp_per_b) * kv_per_grp + (HG ? wave : 0);
-    const int L = seq_lens[b];
+    // Requests are taken longest first (rank r = r-th longest, ties by
+    // index), so that in a ragged batch the long splits start early instead
+    // of trailing behind the short ones.  Batches of more than 64 requests
+    // keep their natural order.
+    const int r = grp / grp_per_b;
+    const int kvblock = grp - r * grp_per_b;
+    int b, L;
+    if (p.batch <= 64) {
+        const int Li = lane < p.batch ? seq_lens[lane] : INT32_MIN;
+        int rank = 0;
+        for (int k = 0; k < p.batch; ++k) {
+            const int Lk = __builtin_amdgcn_readlane(Li, k);
+            rank += (Lk > Li) || (Lk == Li && k < lane);
+        }
+        const unsigned long long hit = __ballot(lane < p.batch && rank == r);
+        b = __builtin_amdgcn_readfirstlane(__ffsll((long long)hit) - 1);
+        L = __builtin_amdgcn_readlane(Li, b);
+    } else {
+        b = r;
+        L = seq_lens[b];
+    }
+    const int kvh = kvblock * kv_per_grp + (HG ? wave : 0);
     const int pages = (L + P - 1) / P;
     const int pps = (pages + S - 1) / S;
     const int pg0 = min(j * pps, pages);
@@ -393,17 +412,19 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
                 ksc[t] = buf_ldf(rs, s_lane, 16 * t * p.hkv * 4);
         }
     };
-    auto load_v = [&](int64_t page, int valid_rows) {
+    // V in two halves (tokens 0..31, 32..63): P.V consumes the first half's
+    // registers first, so the next page's first half can be requested early.
+    auto load_v_half = [&](int64_t page, int valid_rows, int half) {
         const auto r = rsrc(p.v_pages, page, (int64_t)P * row_stride, (int64_t)kvh * D, ES,
                             valid_rows * row_bytes);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 8 * half; i < 8 * half + 8; ++i) {
             if constexpr (KV_INT8 == 0)
                 vr16[i] = buf_ld16(r, v_lane, 4 * i * row_bytes);
             else
                 vr8[i] = buf_ld8(r, v_lane, 4 * i * row_bytes);
         }
-        if constexpr (KV_INT8 != 0) {
+        if (KV_INT8 != 0 && half == 1) {
             const auto rs = rsrc(p.v_scales, page, (int64_t)P * p.hkv, kvh, 4,
                                  valid_rows * p.hkv * 4);
 #pragma unroll
@@ -413,16 +434,17 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
     };
 
     // Software pipeline over this wave's pages: the next page's K loads are
-    // issued as soon as QK^T has consumed the K registers, its V loads as soon
-    // as P.V has consumed the V registers, so loads stay in flight while the
-    // current page is computed.
+    // issued as soon as QK^T has consumed the K registers, each half of its V
+    // loads as soon as P.V has consumed that half of the V registers, so loads
+    // stay in flight while the current page is computed.
     constexpr int PSTEP = HG ? 1 : NW;              // page stride of one wave
     int pg = HG ? pg0 : pg0 + wave;
     if (pg < pg1) {
         const int64_t page = pt_row[pg];
         const int valid = min(P, L - pg * P);
         load_k(page, valid);
-        load_v(page, valid);
+        load_v_half(page, valid, 0);
+        load_v_half(page, valid, 1);
     }
     for (; pg < pg1; pg += PSTEP) {
         const int nxt = pg + PSTEP;
@@ -538,6 +560,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
         if constexpr (KV_INT8 == 0) {
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
+                if (u == 4) {   // tokens 0..31 done: request the next page's first half
+                    __builtin_amdgcn_sched_barrier(0);
+                    load_v_half(page_next, valid_next, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
                 const uint4 pk = *reinterpret_cast<const uint4 *>(&pbuf[wave][u][vr][0]);
                 const int ia = u < 4 ? u : u + 4;       // token 4*ia + r
                 const int ib = ia + 4;                  // token 4*ia + r + 16
@@ -560,6 +587,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
             // no masking is needed; psum tracks sum(p') for the 1152 bias.
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
+                if (u == 4) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    load_v_half(page_next, valid_next, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
                 const uint4 pk = *reinterpret_cast<const uint4 *>(&pbuf[wave][u][vr][0]);
                 const int ia = u < 4 ? u : u + 4;
                 const int ib = ia + 4;
@@ -583,7 +615,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
         }
         __asm__ volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
-        load_v(page_next, valid_next);
+        load_v_half(page_next, valid_next, 1);
         __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (KV_INT8 != 0) {
@@ -705,7 +737,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
             constexpr int HEADS = (HG ? NW : 1) * kGroup;
             constexpr int VEC = HEADS * D / (NW * 64);
             static_assert(VEC * NW * 64 == HEADS * D, "merge tiling");
-            const int64_t mhead0 = (int64_t)b * p.hq + (grp - b * grp_per_b) * kv_per_grp * kGroup;
+            const int64_t mhead0 = (int64_t)b * p.hq + kvblock * kv_per_grp * kGroup;
             const int rows_bytes = HEADS * S * 4;
             const auto racc = __builtin_amdgcn_make_buffer_rsrc(p.part_acc + mhead0 * S * D, (short)0,
                                                                 rows_bytes * D, kBufferWord3);
