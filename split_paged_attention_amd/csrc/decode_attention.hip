@@ -27,6 +27,9 @@
 //     of one token.  The K tile is read once for all 4 heads.
 //   * online softmax in base 2 (scale * log2 e folded into one multiply),
 //     max across the 16 lanes of a row with DPP;
+//   * int8 KV: key codes become exact f16 values for the f16 matrix cores
+//     (query scaled by a per-head power of two), value codes exact f16
+//     1152 + code for v_dot2_f32_f16, the bias removed once per split;
 //   * P.V on the vector ALUs with v_dot2_f32_bf16: lane (r, c) owns dims
 //     8c..8c+7 of tokens 4i + r (so one V load instruction reads 4 whole
 //     256-byte rows), pairs tokens t and t + 16 in one dot2, and gets the
@@ -115,16 +118,6 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                            __builtin_bit_cast(bf16x2_t, b), c, false);
 }
-// bf16 bit pattern of (float)(signed byte k of w); exact for |x| <= 127.
-__device__ __forceinline__ uint32_t i8_bf16_hi(uint32_t w, int k) {
-    float f = (float)(int32_t)__builtin_amdgcn_sbfe(w, 8 * k, 8);
-    return __float_as_uint(f);
-}
-// Two bf16 (upper halves of two fp32 bit patterns) -> one packed dword.
-__device__ __forceinline__ uint32_t pack_hi16(uint32_t lo_f, uint32_t hi_f) {
-    return __builtin_amdgcn_perm(hi_f, lo_f, 0x07060302u);
-}
-
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
     f16x2_t v;
@@ -136,6 +129,26 @@ __device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b),
                                   c, false);
 }
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+// Eight int8 key codes -> eight exact f16 values.  The sign bits are flipped
+// (code + 128, in 1..255), each code becomes the low mantissa byte under the
+// f16 exponent of 1024 -- one byte permute with a 0x64 constant per pair --
+// reading 1152 + code, and one packed subtract of 1152 leaves the code.
+__device__ __forceinline__ f16x8_t i8x8_to_f16(uint2 w) {
+    const uint32_t x = w.x ^ 0x80808080u, y = w.y ^ 0x80808080u;
+    constexpr uint32_t kExp = 0x64646464u;
+    const uint32_t d0 = __builtin_amdgcn_perm(kExp, x, 0x04010400u);
+    const uint32_t d1 = __builtin_amdgcn_perm(kExp, x, 0x04030402u);
+    const uint32_t d2 = __builtin_amdgcn_perm(kExp, y, 0x04010400u);
+    const uint32_t d3 = __builtin_amdgcn_perm(kExp, y, 0x04030402u);
+    const f16x2_t bias = {(_Float16)1152.f, (_Float16)1152.f};
+    const f16x2_t h0 = __builtin_bit_cast(f16x2_t, d0) - bias;
+    const f16x2_t h1 = __builtin_bit_cast(f16x2_t, d1) - bias;
+    const f16x2_t h2 = __builtin_bit_cast(f16x2_t, d2) - bias;
+    const f16x2_t h3 = __builtin_bit_cast(f16x2_t, d3) - bias;
+    return f16x8_t{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+}
+
 // int8 value codes -> exact f16, biased: byte k of wa (token a) and of wb
 // (token b) become the f16 pair (1152 + a_k, 1152 + b_k).  With its sign bit
 // flipped a code is x + 128 in [1, 255]; placed as the low mantissa byte under
@@ -349,6 +362,30 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
 #pragma unroll
         for (int c = 0; c < 4; ++c) qa[c] = *reinterpret_cast<const bf16x8_t *>(qp + 32 * c);
     }
+    // int8 KV: the scores use the f16 matrix cores with exact f16 key codes,
+    // so the query goes to f16 too, each head scaled by a power of two that
+    // puts its largest |q| in [2^14, 2^15) (exact: a bf16 value has 8
+    // significant bits); qinv[h] undoes the scaling on the scores.
+    f16x8_t qa16[4];
+    float qinv[4] = {1.f, 1.f, 1.f, 1.f};
+    if constexpr (KV_INT8 != 0) {
+        float amax = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)qa[c][e]));
+        amax = fmaxf(amax, __shfl_xor(amax, 16));
+        amax = fmaxf(amax, __shfl_xor(amax, 32));   // lane n: head n & 3, all 128 dims
+        const int sh = amax > 0.f ? 15 - __builtin_amdgcn_frexp_expf(amax) : 0;
+        const float up = __builtin_ldexpf(1.f, sh);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qa16[c][e] = (_Float16)((float)qa[c][e] * up);
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+            qinv[h] = __builtin_ldexpf(1.f, -__builtin_amdgcn_readlane(sh, h));
+    }
 
     float m[4], lpart[4], acc[4][8], psum[4];
 #pragma unroll
@@ -453,45 +490,36 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
         const int valid_next = has_next ? min(P, L - nxt * P) : 0;
         const int valid = min(P, L - pg * P);       // tokens of this page that count
 
-        bf16x8_t kb[4][4];
-        if constexpr (KV_INT8 == 0) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) kb[t][c] = __builtin_bit_cast(bf16x8_t, kr[t][c]);
-        } else {
-            // int8 -> bf16 (exact)
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    uint32_t wds[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const uint32_t src = e < 2 ? kr8[t][c].x : kr8[t][c].y;
-                        const int k0 = (e & 1) * 2;
-                        wds[e] = pack_hi16(i8_bf16_hi(src, k0), i8_bf16_hi(src, k0 + 1));
-                    }
-                    kb[t][c] = __builtin_bit_cast(bf16x8_t, make_uint4(wds[0], wds[1], wds[2], wds[3]));
-                }
-        }
-
         // ---- S = Q K^T: lane (n, g) gets s[head h][token 16t + n] in sacc[t][h]
         f32x4_t sacc[4];
+        if constexpr (KV_INT8 == 0) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            sacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int t = 0; t < 4; ++t) {
+                sacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-                sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[c], kb[t][c], sacc[t], 0, 0, 0);
+                for (int c = 0; c < 4; ++c)
+                    sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        qa[c], __builtin_bit_cast(bf16x8_t, kr[t][c]), sacc[t], 0, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                sacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa16[c], i8x8_to_f16(kr8[t][c]),
+                                                                     sacc[t], 0, 0, 0);
+            }
         }
         float s[4][4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const float f = KV_INT8 ? p.qk_scale_log2 * ksc[t] : p.qk_scale_log2;
             const bool ok = (16 * t + n) < valid;
 #pragma unroll
-            for (int h = 0; h < 4; ++h) s[t][h] = ok ? sacc[t][h] * f : kNegInf;
+            for (int h = 0; h < 4; ++h) {
+                const float f = KV_INT8 ? p.qk_scale_log2 * ksc[t] * qinv[h] : p.qk_scale_log2;
+                s[t][h] = ok ? sacc[t][h] * f : kNegInf;
+            }
         }
         // keep the prefetch after the last read of the K registers it reuses
         __builtin_amdgcn_sched_barrier(0);
