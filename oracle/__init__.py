@@ -4,9 +4,12 @@ TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
 CPU-baseline leg may import this package; the product path (the HIP library
 and its Python binding) never does, and shares no code with it.
 
-Every function follows a definition stated in oracle.c's header:
+Every function follows a definition stated in oracle.c:
   build_page_table  -- sglang fused metadata kernel docstring (page_table,
                        cache_seqlens, cu_seqlens_k by definition);
+  build_metadata    -- the same update with its optional outputs
+                       (cu_seqlens_q modes, sliding-window page table and
+                       swa_out_cache_loc);
   paged_attention   -- plain softmax attention of one query token over the
                        paged KV cache (lmdeploy's split-K decode computes this
                        exactly, split-K being a reformulation);
@@ -47,6 +50,10 @@ def _load():
     lib.oracle_build_page_table.argtypes = [_P, _I64, _P, _P, _I32, _I32, _I32, _I32, _P, _I64,
                                             _P, _P]
     lib.oracle_build_page_table.restype = _INT
+    lib.oracle_build_metadata.argtypes = [_P, _I64, _P, _P, _I32, _I32, _I32, _I32, _P, _I64, _P,
+                                          _P, _INT, _P, _I32, _P, _P, _P, _I64, _P, _I64, _P,
+                                          _I64]
+    lib.oracle_build_metadata.restype = _INT
     att = [_P, _P, _P, _P, _P, _INT, _P, _I64, _P, _INT, _INT, _INT, _INT, _INT, _F32]
     lib.oracle_paged_attention.argtypes = att + [_P, _P]
     lib.oracle_paged_attention.restype = _INT
@@ -89,6 +96,48 @@ def build_page_table(req_to_token, req_pool_indices, seq_lens, page_size, max_se
     if rc != 0:
         raise ValueError("oracle_build_page_table: invalid arguments")
     return page_table, cache, cu
+
+
+def build_metadata(req_to_token, req_pool_indices, seq_lens, page_size, max_seq_pages, *,
+                   seqlen_offset=0, page_table=None, q_mode=0, qlens=None, q_stride=0,
+                   cu_seqlens_q=None, swa_mapping=None, swa_page_table=None,
+                   out_cache_loc=None, swa_out_cache_loc=None):
+    """The full metadata update.  Outputs given as arrays are updated in place
+    (their unwritten entries keep their values); returns a dict of outputs.
+    page_table defaults to a poisoned [bs, max_seq_pages]; swa_page_table=True
+    asks for one too (None = no sliding-window table, as in the source)."""
+    lib = _load()
+    r2t = _c(req_to_token, np.int32)
+    rpi = _c(req_pool_indices, np.int32)
+    sl = _c(seq_lens, np.int32)
+    bs = int(rpi.shape[0])
+    poison = -0x5A5A5A5A
+    if page_table is None:
+        page_table = np.full((bs, max(1, max_seq_pages)), poison, dtype=np.int32)
+    cache = np.full(bs, poison, dtype=np.int32)
+    cu = np.full(bs + 1, poison, dtype=np.int32)
+    if cu_seqlens_q is None:
+        cu_seqlens_q = np.full(bs + 1, poison, dtype=np.int32)
+    ql = _c(qlens, np.int32) if qlens is not None else None
+    swa = _c(swa_mapping, np.int64) if swa_mapping is not None else None
+    if isinstance(swa_page_table, bool):
+        swa_page_table = (np.full((bs, max(1, max_seq_pages)), poison, dtype=np.int32)
+                          if swa_page_table else None)
+    ocl = _c(out_cache_loc, np.int64) if out_cache_loc is not None else None
+    for a in (page_table, cu_seqlens_q, swa_page_table, swa_out_cache_loc):
+        assert a is None or a.flags.c_contiguous
+    rc = lib.oracle_build_metadata(
+        _ptr(r2t), r2t.shape[1], _ptr(rpi), _ptr(sl), bs, int(seqlen_offset), int(page_size),
+        int(max_seq_pages), _ptr(page_table), page_table.shape[1], _ptr(cache), _ptr(cu),
+        int(q_mode), _ptr(ql), int(q_stride), _ptr(cu_seqlens_q), _ptr(swa),
+        _ptr(swa_page_table), 0 if swa_page_table is None else swa_page_table.shape[1],
+        _ptr(ocl), 0 if ocl is None else ocl.shape[0], _ptr(swa_out_cache_loc),
+        0 if swa_out_cache_loc is None else swa_out_cache_loc.shape[0])
+    if rc != 0:
+        raise ValueError("oracle_build_metadata: invalid arguments")
+    return dict(page_table=page_table, cache_seqlens=cache, cu_seqlens_k=cu,
+                cu_seqlens_q=cu_seqlens_q, swa_page_table=swa_page_table,
+                swa_out_cache_loc=swa_out_cache_loc)
 
 
 def _att_args(q, k_pages, v_pages, k_scales, v_scales, kv_dtype, page_table, seq_lens,

@@ -12,7 +12,12 @@
  *    row and cumsum branches: cache_seqlens = seq_lens + seqlen_offset (int32),
  *    cu_seqlens_k[1:] = cumsum(cache_seqlens) (int32), page_table[i, p] =
  *    req_to_token[req_pool_indices[i], p * page_size] // page_size for every
- *    p < max_seq_pages.
+ *    p < max_seq_pages; and its optional outputs (the docstring, the row
+ *    branch's sliding-window part, the cumsum branch's q modes, the
+ *    swa-out branch and the launcher's num_out_tokens): cu_seqlens_q by
+ *    cumsum of qlens or by (i + 1) * q_stride, the sliding-window page table
+ *    through full_to_swa with -1 for unmapped slots, and swa_out_cache_loc
+ *    translated through full_to_swa and zero padded.
  *  - lmdeploy PR "use PDL for paged attention", Summary/Changes: split-K
  *    paged attention for decode, a producer writing per-split scratch and a
  *    reducer that merges it.  The attention itself is the plain definition
@@ -80,6 +85,76 @@ int oracle_build_page_table(const int32_t *req_to_token, int64_t req_to_token_st
     for (int32_t i = 0; i < bs; ++i) {
         run += (uint32_t)cache_seqlens[i];
         cu_seqlens_k[i + 1] = (int32_t)run;
+    }
+    return 0;
+}
+
+/* The full metadata update, by definition (sglang docstring, kernel row,
+ * cumsum and swa-out branches, launcher):
+ *   everything oracle_build_page_table computes, plus
+ *   cu_seqlens_q[1 + i] = sum_{i' <= i} qlens[i']        (q_mode 1, int32)
+ *   cu_seqlens_q[1 + i] = (i + 1) * q_stride             (q_mode 2, int32)
+ *   cu_seqlens_q untouched                               (q_mode 0)
+ *   swa_page_table[i, p] = -1 if token < 0 or swa[token] < 0,
+ *                          else floor(swa[token] / page_size),
+ *     token = req_to_token[req_pool_indices[i], p * page_size]  (when swa given)
+ *   swa_out_cache_loc[k] = -1 if loc < 0, else swa[loc], loc = out_cache_loc[k],
+ *     for k < num_out = min(swa_out_len, n_out_cache_loc); 0 for
+ *     num_out <= k < swa_out_len                         (when swa_out given)
+ * Like cu_seqlens_k[0], cu_seqlens_q[0] is written as 0 in modes 1 and 2
+ * (the source writes [1:] and relies on a preset 0).  bs == 0 writes nothing
+ * at all, the zero padding included (the launcher returns first). */
+int oracle_build_metadata(const int32_t *req_to_token, int64_t req_to_token_stride,
+                          const int32_t *req_pool_indices, const int32_t *seq_lens, int32_t bs,
+                          int32_t seqlen_offset, int32_t page_size, int32_t max_seq_pages,
+                          int32_t *page_table, int64_t page_table_stride,
+                          int32_t *cache_seqlens, int32_t *cu_seqlens_k, int q_mode,
+                          const int32_t *qlens, int32_t q_stride, int32_t *cu_seqlens_q,
+                          const int64_t *swa, int32_t *swa_page_table,
+                          int64_t swa_page_table_stride, const int64_t *out_cache_loc,
+                          int64_t n_out_cache_loc, int64_t *swa_out_cache_loc,
+                          int64_t swa_out_len) {
+    if (bs == 0) return 0;
+    int rc = oracle_build_page_table(req_to_token, req_to_token_stride, req_pool_indices,
+                                     seq_lens, bs, seqlen_offset, page_size, max_seq_pages,
+                                     page_table, page_table_stride, cache_seqlens,
+                                     cu_seqlens_k);
+    if (rc) return rc;
+    if (q_mode == 1 || q_mode == 2) cu_seqlens_q[0] = 0;
+    if (q_mode == 1) {
+        uint32_t run = 0;
+        for (int32_t i = 0; i < bs; ++i) {
+            run += (uint32_t)qlens[i];
+            cu_seqlens_q[i + 1] = (int32_t)run;
+        }
+    } else if (q_mode == 2) {
+        for (int32_t i = 0; i < bs; ++i)
+            cu_seqlens_q[i + 1] = (int32_t)(uint32_t)((uint64_t)(i + 1) * (uint64_t)(uint32_t)q_stride);
+    } else if (q_mode != 0) {
+        return 1;
+    }
+    if (swa_page_table) {
+        for (int32_t i = 0; i < bs; ++i) {
+            int64_t row = (int64_t)req_pool_indices[i];
+            for (int32_t p = 0; p < max_seq_pages; ++p) {
+                int64_t token = req_to_token[row * req_to_token_stride + (int64_t)p * page_size];
+                int64_t v = token < 0 ? -1 : swa[token];
+                swa_page_table[(int64_t)i * swa_page_table_stride + p] =
+                    (int32_t)(v < 0 ? -1 : floor_div(v, page_size));
+            }
+        }
+    }
+    if (swa_out_cache_loc) {
+        int64_t num_out = n_out_cache_loc < swa_out_len ? n_out_cache_loc : swa_out_len;
+        if (!out_cache_loc) num_out = 0;
+        for (int64_t k = 0; k < swa_out_len; ++k) {
+            if (k < num_out) {
+                int64_t loc = out_cache_loc[k];
+                swa_out_cache_loc[k] = loc < 0 ? -1 : swa[loc];
+            } else {
+                swa_out_cache_loc[k] = 0;
+            }
+        }
     }
     return 0;
 }

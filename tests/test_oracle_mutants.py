@@ -31,6 +31,17 @@ MUTANTS = {
     "int8_value_scale": ("const float *sc = which ? a->v_scales : a->k_scales;",
                          "const float *sc = a->k_scales;"),
     "dropped_offset": ("(uint32_t)seq_lens[i] + (uint32_t)seqlen_offset", "(uint32_t)seq_lens[i]"),
+    "strided_q_from_zero": ("(uint64_t)(i + 1) * (uint64_t)(uint32_t)q_stride",
+                            "(uint64_t)i * (uint64_t)(uint32_t)q_stride"),
+    "cumsum_q_exclusive": ("run += (uint32_t)qlens[i];\n            cu_seqlens_q[i + 1] = (int32_t)run;",
+                           "cu_seqlens_q[i + 1] = (int32_t)run;\n            run += (uint32_t)qlens[i];"),
+    "swa_no_sentinel": ("(int32_t)(v < 0 ? -1 : floor_div(v, page_size));",
+                        "(int32_t)floor_div(v, page_size);"),
+    "swa_padding_minus_one": ("swa_out_cache_loc[k] = 0;", "swa_out_cache_loc[k] = -1;"),
+    "swa_out_untranslated": ("swa_out_cache_loc[k] = loc < 0 ? -1 : swa[loc];",
+                             "swa_out_cache_loc[k] = loc;"),
+    "swa_num_out_max": ("n_out_cache_loc < swa_out_len ? n_out_cache_loc : swa_out_len",
+                        "n_out_cache_loc > swa_out_len ? swa_out_len : swa_out_len"),
 }
 
 pytestmark = pytest.mark.skipif(os.environ.get("SPA_ORACLE_MUTANTS") != "1",

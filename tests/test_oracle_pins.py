@@ -80,6 +80,116 @@ def test_metadata_offset_and_cumsum_wrap_int32():
     assert pt.tolist() == [[2, 3], [0, 1]]
 
 
+def _swa_golden():
+    return json.load(open(os.path.join(GOLDEN, "metadata_swa_tiny.json")))
+
+
+@pytest.mark.parametrize("q_mode", [0, 1, 2])
+def test_metadata_full_golden_hand_example(q_mode):
+    g = _swa_golden()
+    preset_q = np.full(3, 55, np.int32)
+    out = oracle.build_metadata(
+        np.array(g["req_to_token"], np.int32), np.array(g["req_pool_indices"], np.int32),
+        np.array(g["seq_lens"], np.int32), g["page_size"], g["max_seq_pages"],
+        seqlen_offset=g["seqlen_offset"], page_table=np.array(g["table_preset"], np.int32),
+        q_mode=q_mode, qlens=np.array(g["qlens"], np.int32), q_stride=g["q_stride"],
+        cu_seqlens_q=preset_q, swa_mapping=np.array(g["full_to_swa"], np.int64),
+        swa_page_table=np.array(g["table_preset"], np.int32),
+        out_cache_loc=np.array(g["out_cache_loc"], np.int64),
+        swa_out_cache_loc=np.full(g["swa_out_len"], 99, np.int64))
+    assert out["page_table"].tolist() == g["expect_page_table"]
+    assert out["swa_page_table"].tolist() == g["expect_swa_page_table"]
+    assert out["cache_seqlens"].tolist() == g["expect_cache_seqlens"]
+    assert out["cu_seqlens_k"].tolist() == g["expect_cu_seqlens_k"]
+    assert out["swa_out_cache_loc"].tolist() == g["expect_swa_out_cache_loc"]
+    want_q = {0: [55, 55, 55], 1: g["expect_cu_seqlens_q_cumsum"],
+              2: g["expect_cu_seqlens_q_strided"]}[q_mode]
+    assert out["cu_seqlens_q"].tolist() == want_q
+
+
+def test_metadata_swa_out_shorter_than_out_cache_loc():
+    g = _swa_golden()
+    out = oracle.build_metadata(
+        np.array(g["req_to_token"], np.int32), np.array(g["req_pool_indices"], np.int32),
+        np.array(g["seq_lens"], np.int32), g["page_size"], g["max_seq_pages"],
+        swa_mapping=np.array(g["full_to_swa"], np.int64),
+        out_cache_loc=np.array(g["out_cache_loc"], np.int64),
+        swa_out_cache_loc=np.full(g["short_swa_out_len"], 99, np.int64))
+    assert out["swa_out_cache_loc"].tolist() == g["expect_short_swa_out_cache_loc"]
+    assert out["swa_page_table"] is None
+
+
+def test_metadata_swa_out_without_out_cache_loc_is_all_padding():
+    """The launcher sets num_out_tokens = 0 when out_cache_loc is absent: the
+    whole output is the zero padding and the mapping is never read."""
+    r2t = np.arange(16, dtype=np.int32).reshape(2, 8)
+    out = oracle.build_metadata(r2t, np.array([0], np.int32), np.array([3], np.int32), 4, 2,
+                                swa_out_cache_loc=np.full(5, 99, np.int64))
+    assert out["swa_out_cache_loc"].tolist() == [0] * 5
+
+
+def test_metadata_full_bs0_writes_nothing():
+    r2t = np.zeros((1, 8), np.int32)
+    swa_out = np.full(4, 99, np.int64)
+    cuq = np.full(1, 55, np.int32)
+    oracle.build_metadata(r2t, np.zeros(0, np.int32), np.zeros(0, np.int32), 4, 2, q_mode=2,
+                          q_stride=3, cu_seqlens_q=cuq, swa_mapping=np.zeros(8, np.int64),
+                          out_cache_loc=np.zeros(4, np.int64), swa_out_cache_loc=swa_out)
+    assert swa_out.tolist() == [99] * 4 and cuq.tolist() == [55]
+
+
+@pytest.mark.parametrize("cfg", [1, 3, 5])
+def test_metadata_identity_swa_mapping_reproduces_page_table(cfg):
+    """With full_to_swa the identity, every slot the generator placed is >= 0,
+    so the sliding-window table must equal the full page table, and the
+    translated out_cache_loc must equal out_cache_loc with its zero tail."""
+    c = W.make_config(cfg)
+    bs, msp = c.batch, c.page_list.shape[1]
+    n_slots = c.num_pages * c.page_size
+    ident = np.arange(n_slots + c.page_size + 1, dtype=np.int64)
+    rng = np.random.default_rng(cfg)
+    ocl = rng.integers(0, n_slots, size=bs).astype(np.int64)
+    out = oracle.build_metadata(c.req_to_token, c.req_pool_indices, c.seq_lens, c.page_size,
+                                msp, swa_mapping=ident, swa_page_table=True, out_cache_loc=ocl,
+                                swa_out_cache_loc=np.full(bs + 9, 99, np.int64))
+    assert np.array_equal(out["swa_page_table"], out["page_table"])
+    assert out["swa_out_cache_loc"].tolist() == ocl.tolist() + [0] * 9
+
+
+def test_metadata_swa_unmapped_and_negative_slots_give_minus_one():
+    """A mapping that evicts every slot gives page -1 everywhere; a negative
+    slot gives -1 without reading the mapping."""
+    r2t = np.array([[-3, -3, -3, -3, 7, 7, 7, 7]], np.int32)
+    out = oracle.build_metadata(r2t, np.array([0, 0], np.int32), np.array([1, 1], np.int32), 4,
+                                2, swa_mapping=np.full(8, -9, np.int64), swa_page_table=True,
+                                out_cache_loc=np.array([-1, 3], np.int64),
+                                swa_out_cache_loc=np.zeros(2, np.int64))
+    assert out["swa_page_table"].tolist() == [[-1, -1], [-1, -1]]
+    assert out["page_table"].tolist() == [[-1, 1], [-1, 1]]
+    # any negative mapped slot is the sentinel -1, not floor(-9 / 4) = -3 ...
+    # ... but swa_out_cache_loc passes the mapped value through unchanged
+    assert out["swa_out_cache_loc"].tolist() == [-1, -9]
+
+
+def test_metadata_q_modes_agree_and_wrap_int32():
+    """Equal qlens make the cumsum mode the strided mode; the cumsum's steps
+    give back qlens; both wrap modulo 2^32 like the int32 arithmetic."""
+    bs = 37
+    r2t = np.zeros((1, 64), np.int32)
+    rpi = np.zeros(bs, np.int32)
+    sl = np.ones(bs, np.int32)
+    for stride in (1, 5, 2**30 + 3):
+        a = oracle.build_metadata(r2t, rpi, sl, 64, 1, q_mode=1,
+                                  qlens=np.full(bs, stride, np.int32))["cu_seqlens_q"]
+        b = oracle.build_metadata(r2t, rpi, sl, 64, 1, q_mode=2, q_stride=stride)["cu_seqlens_q"]
+        assert np.array_equal(a, b)
+        want = ((np.arange(bs + 1, dtype=np.int64) * stride + 2**31) % 2**32 - 2**31)
+        assert a.tolist() == want.tolist()
+    ql = np.random.default_rng(5).integers(0, 9, size=bs).astype(np.int32)
+    cu = oracle.build_metadata(r2t, rpi, sl, 64, 1, q_mode=1, qlens=ql)["cu_seqlens_q"]
+    assert cu[0] == 0 and np.array_equal(np.diff(cu), ql)
+
+
 # ---------------------------------------------------------------- attention: golden
 
 def _golden_case(c, int8=False):
