@@ -82,7 +82,9 @@ int spa_abi_version(void);
  *
  * bs == 0 returns SPA_OK without launching (the source launcher's early
  * return).  Requires page_size >= 1, 0 <= max_seq_pages <= page_table_stride
- * and (max_seq_pages - 1) * page_size < req_to_token_stride.
+ * and (max_seq_pages - 1) * page_size < req_to_token_stride.  Same launch
+ * as spa_build_metadata with q_mode SPA_Q_MODE_NONE and no sliding-window
+ * outputs.
  */
 spa_status spa_build_page_table(const int32_t *req_to_token, int64_t req_to_token_stride,
                                 int32_t pool_size, const int32_t *req_pool_indices,
@@ -90,6 +92,54 @@ spa_status spa_build_page_table(const int32_t *req_to_token, int64_t req_to_toke
                                 int32_t page_size, int32_t max_seq_pages, int32_t *page_table,
                                 int64_t page_table_stride, int32_t *cache_seqlens,
                                 int32_t *cu_seqlens_k, hipStream_t stream);
+
+/* cu_seqlens_q modes of spa_build_metadata (the source's Q_MODE values). */
+#define SPA_Q_MODE_NONE 0      /* cu_seqlens_q is preset by the caller and not touched */
+#define SPA_Q_MODE_CUMSUM 1    /* cu_seqlens_q[0] = 0, cu_seqlens_q[1+i] = qlens[0] + ... + qlens[i] */
+#define SPA_Q_MODE_STRIDED 2   /* cu_seqlens_q[0] = 0, cu_seqlens_q[1+i] = (i + 1) * q_stride */
+
+/*
+ * The whole decode metadata update in ONE launch: everything
+ * spa_build_page_table writes, plus three optional outputs (same sglang
+ * source: docstring, the row branch's sliding-window part, the cumsum
+ * branch's Q modes, the swa-out branch, the launcher's num_out_tokens).
+ *
+ *   cu_seqlens_q        [bs + 1] int32, per q_mode above (int32 arithmetic,
+ *                       wraps); qlens [bs] int32 is read in CUMSUM mode only.
+ *   swa_page_table      [bs, swa_page_table_stride] int32 or NULL.  For
+ *                       p < max_seq_pages, with slot = the same req_to_token
+ *                       entry page_table reads:
+ *                         -1                               if slot < 0
+ *                         -1                               if full_to_swa[slot] < 0
+ *                         full_to_swa[slot] / page_size    otherwise
+ *   swa_out_cache_loc   [swa_out_len] int64 or NULL.  With
+ *                       num_out = min(swa_out_len, num_out_cache_loc), or 0
+ *                       if out_cache_loc is NULL:
+ *                         k < num_out:  -1 if out_cache_loc[k] < 0,
+ *                                       else full_to_swa[out_cache_loc[k]]
+ *                         otherwise:    0
+ *   full_to_swa         int64 map from full-pool slots to sliding-window
+ *                       slots (-1 = not resident), indexed by every
+ *                       non-negative slot read above; may be NULL when
+ *                       neither output reads it.
+ *
+ * cu_seqlens_q[0] is written as 0 in the two computed modes, like
+ * cu_seqlens_k[0].  bs == 0 returns SPA_OK and writes nothing, the zero
+ * padding of swa_out_cache_loc included (the source launcher returns
+ * first).  Alignment: int32 arrays 4 bytes, int64 arrays 8 bytes.
+ * SPA_ERR_INVALID_ARGUMENT for an unknown q_mode, a missing array the
+ * chosen outputs need, swa_page_table_stride < max_seq_pages, or negative
+ * lengths; the checks of spa_build_page_table apply too.
+ */
+spa_status spa_build_metadata(
+    const int32_t *req_to_token, int64_t req_to_token_stride, int32_t pool_size,
+    const int32_t *req_pool_indices, const int32_t *seq_lens, int32_t bs, int32_t seqlen_offset,
+    int32_t page_size, int32_t max_seq_pages, int32_t *page_table, int64_t page_table_stride,
+    int32_t *cache_seqlens, int32_t *cu_seqlens_k, int32_t q_mode, const int32_t *qlens,
+    int32_t q_stride, int32_t *cu_seqlens_q, const int64_t *full_to_swa,
+    int32_t *swa_page_table, int64_t swa_page_table_stride, const int64_t *out_cache_loc,
+    int64_t num_out_cache_loc, int64_t *swa_out_cache_loc, int64_t swa_out_len,
+    hipStream_t stream);
 
 /*
  * Bytes of workspace spa_paged_decode_attention needs: the per-split partial

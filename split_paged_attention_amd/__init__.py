@@ -77,6 +77,10 @@ def lib():
     L.spa_build_page_table.argtypes = [_P, _I64, _I32, _P, _P, _I32, _I32, _I32, _I32, _P, _I64,
                                        _P, _P, _P]
     L.spa_build_page_table.restype = _ST
+    L.spa_build_metadata.argtypes = [_P, _I64, _I32, _P, _P, _I32, _I32, _I32, _I32, _P, _I64,
+                                     _P, _P, _I32, _P, _I32, _P, _P, _P, _I64, _P, _I64, _P,
+                                     _I64, _P]
+    L.spa_build_metadata.restype = _ST
     L.spa_decode_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32, _I32]
     L.spa_decode_workspace_bytes.restype = _SZ
     L.spa_workspace_reset.argtypes = [_P, _SZ, _P]
@@ -157,6 +161,72 @@ def build_page_table(req_to_token: torch.Tensor, req_pool_indices: torch.Tensor,
         _ptr(cu_seqlens_k), _stream(stream))
     _check(st, "spa_build_page_table")
     return page_table, cache_seqlens, cu_seqlens_k
+
+
+Q_MODE_NONE, Q_MODE_CUMSUM, Q_MODE_STRIDED = 0, 1, 2
+
+
+def build_metadata(req_to_token: torch.Tensor, req_pool_indices: torch.Tensor,
+                   seq_lens: torch.Tensor, page_size: int, max_seq_pages: int, *,
+                   seqlen_offset: int = 0, page_table: Optional[torch.Tensor] = None,
+                   cache_seqlens: Optional[torch.Tensor] = None,
+                   cu_seqlens_k: Optional[torch.Tensor] = None, q_mode: int = Q_MODE_NONE,
+                   qlens: Optional[torch.Tensor] = None, q_stride: int = 0,
+                   cu_seqlens_q: Optional[torch.Tensor] = None,
+                   full_to_swa: Optional[torch.Tensor] = None,
+                   swa_page_table: Optional[torch.Tensor] = None,
+                   out_cache_loc: Optional[torch.Tensor] = None,
+                   swa_out_cache_loc: Optional[torch.Tensor] = None,
+                   stream=None) -> dict:
+    """spa_build_metadata.  Outputs not given are allocated (page_table,
+    cache_seqlens, cu_seqlens_k always; cu_seqlens_q when q_mode is not NONE);
+    swa_page_table and swa_out_cache_loc are produced only when passed in, as
+    in the source.  Returns a dict of the output tensors."""
+    _need(req_to_token, "req_to_token", torch.int32, contiguous=False)
+    if req_to_token.dim() != 2 or req_to_token.stride(1) != 1:
+        raise ValueError("req_to_token must be 2-D with unit column stride")
+    _need(req_pool_indices, "req_pool_indices", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32)
+    bs = int(req_pool_indices.shape[0])
+    dev = req_to_token.device
+
+    def table(t, name):
+        _need(t, name, torch.int32, contiguous=False)
+        if t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError(f"{name} must be 2-D with unit column stride")
+
+    if page_table is None:
+        page_table = torch.empty((bs, max(1, max_seq_pages)), dtype=torch.int32, device=dev)
+    table(page_table, "page_table")
+    if cache_seqlens is None:
+        cache_seqlens = torch.empty((bs,), dtype=torch.int32, device=dev)
+    if cu_seqlens_k is None:
+        cu_seqlens_k = torch.empty((bs + 1,), dtype=torch.int32, device=dev)
+    _need(cache_seqlens, "cache_seqlens", torch.int32)
+    _need(cu_seqlens_k, "cu_seqlens_k", torch.int32)
+    if q_mode != Q_MODE_NONE and cu_seqlens_q is None:
+        cu_seqlens_q = torch.empty((bs + 1,), dtype=torch.int32, device=dev)
+    for t, name, dt in ((qlens, "qlens", torch.int32), (cu_seqlens_q, "cu_seqlens_q", torch.int32),
+                        (full_to_swa, "full_to_swa", torch.int64),
+                        (out_cache_loc, "out_cache_loc", torch.int64),
+                        (swa_out_cache_loc, "swa_out_cache_loc", torch.int64)):
+        if t is not None:
+            _need(t, name, dt)
+    if swa_page_table is not None:
+        table(swa_page_table, "swa_page_table")
+    st = lib().spa_build_metadata(
+        _ptr(req_to_token), req_to_token.stride(0), req_to_token.shape[0],
+        _ptr(req_pool_indices), _ptr(seq_lens), bs, int(seqlen_offset), int(page_size),
+        int(max_seq_pages), _ptr(page_table), page_table.stride(0), _ptr(cache_seqlens),
+        _ptr(cu_seqlens_k), int(q_mode), _ptr(qlens), int(q_stride), _ptr(cu_seqlens_q),
+        _ptr(full_to_swa), _ptr(swa_page_table),
+        0 if swa_page_table is None else swa_page_table.stride(0), _ptr(out_cache_loc),
+        0 if out_cache_loc is None else out_cache_loc.numel(), _ptr(swa_out_cache_loc),
+        0 if swa_out_cache_loc is None else swa_out_cache_loc.numel(), _stream(stream))
+    _check(st, "spa_build_metadata")
+    return dict(page_table=page_table, cache_seqlens=cache_seqlens, cu_seqlens_k=cu_seqlens_k,
+                cu_seqlens_q=cu_seqlens_q, swa_page_table=swa_page_table,
+                swa_out_cache_loc=swa_out_cache_loc)
 
 
 # ---------------------------------------------------------------- workspace

@@ -56,26 +56,85 @@ int spa_last_hip_error(void) { return g_last_hip_error; }
 
 int spa_abi_version(void) { return 1; }
 
+spa_status spa_build_metadata(
+    const int32_t *req_to_token, int64_t req_to_token_stride, int32_t pool_size,
+    const int32_t *req_pool_indices, const int32_t *seq_lens, int32_t bs, int32_t seqlen_offset,
+    int32_t page_size, int32_t max_seq_pages, int32_t *page_table, int64_t page_table_stride,
+    int32_t *cache_seqlens, int32_t *cu_seqlens_k, int32_t q_mode, const int32_t *qlens,
+    int32_t q_stride, int32_t *cu_seqlens_q, const int64_t *full_to_swa,
+    int32_t *swa_page_table, int64_t swa_page_table_stride, const int64_t *out_cache_loc,
+    int64_t num_out_cache_loc, int64_t *swa_out_cache_loc, int64_t swa_out_len,
+    hipStream_t stream) {
+    const int64_t min_stride = max_seq_pages > 1 ? max_seq_pages : 1;
+    if (bs < 0 || page_size < 1 || max_seq_pages < 0 || pool_size < 1 ||
+        page_table_stride < min_stride || req_to_token_stride < 1)
+        return SPA_ERR_INVALID_ARGUMENT;
+    if (max_seq_pages > 0 && (int64_t)(max_seq_pages - 1) * page_size >= req_to_token_stride)
+        return SPA_ERR_INVALID_ARGUMENT;
+    if (q_mode != spa::kQModeNone && q_mode != spa::kQModeCumsum &&
+        q_mode != spa::kQModeStrided)
+        return SPA_ERR_INVALID_ARGUMENT;
+    if (swa_page_table && swa_page_table_stride < min_stride) return SPA_ERR_INVALID_ARGUMENT;
+    if (swa_out_cache_loc && (swa_out_len < 0 || num_out_cache_loc < 0))
+        return SPA_ERR_INVALID_ARGUMENT;
+    int64_t num_out = 0;
+    if (swa_out_cache_loc && out_cache_loc)
+        num_out = num_out_cache_loc < swa_out_len ? num_out_cache_loc : swa_out_len;
+    const int64_t out_len = swa_out_cache_loc ? swa_out_len : 0;
+    const int64_t max_groups = (int64_t)(UINT32_MAX / 256);   // work-items fit in 32 bits
+    if (out_len > max_groups * 1024 || spa::metadata_grid(bs, out_len) > max_groups)
+        return SPA_ERR_INVALID_ARGUMENT;
+    if (bs == 0) return SPA_OK;
+    if (!req_to_token || !req_pool_indices || !seq_lens || !page_table || !cache_seqlens ||
+        !cu_seqlens_k)
+        return SPA_ERR_INVALID_ARGUMENT;
+    if (q_mode != spa::kQModeNone && !cu_seqlens_q) return SPA_ERR_INVALID_ARGUMENT;
+    if (q_mode == spa::kQModeCumsum && !qlens) return SPA_ERR_INVALID_ARGUMENT;
+    if ((swa_page_table || num_out > 0) && !full_to_swa) return SPA_ERR_INVALID_ARGUMENT;
+    if (!aligned(req_to_token, 4) || !aligned(req_pool_indices, 4) || !aligned(seq_lens, 4) ||
+        !aligned(page_table, 4) || !aligned(cache_seqlens, 4) || !aligned(cu_seqlens_k, 4) ||
+        !aligned(qlens, 4) || !aligned(cu_seqlens_q, 4) || !aligned(full_to_swa, 8) ||
+        !aligned(swa_page_table, 4) || !aligned(out_cache_loc, 8) ||
+        !aligned(swa_out_cache_loc, 8))
+        return SPA_ERR_INVALID_ARGUMENT;
+    spa::MetadataParams p{};
+    p.req_to_token = req_to_token;
+    p.req_to_token_stride = req_to_token_stride;
+    p.req_pool_indices = req_pool_indices;
+    p.seq_lens = seq_lens;
+    p.bs = bs;
+    p.seqlen_offset = seqlen_offset;
+    p.page_size = page_size;
+    p.max_seq_pages = max_seq_pages;
+    p.page_table = page_table;
+    p.page_table_stride = page_table_stride;
+    p.cache_seqlens = cache_seqlens;
+    p.cu_seqlens_k = cu_seqlens_k;
+    p.q_mode = q_mode;
+    p.q_stride = q_stride;
+    p.qlens = qlens;
+    p.cu_seqlens_q = cu_seqlens_q;
+    p.full_to_swa = full_to_swa;
+    p.swa_page_table = swa_page_table;
+    p.swa_page_table_stride = swa_page_table_stride;
+    p.out_cache_loc = num_out > 0 ? out_cache_loc : nullptr;
+    p.num_out = num_out;
+    p.swa_out_cache_loc = swa_out_cache_loc;
+    p.swa_out_len = out_len;
+    return hip_status(spa::launch_build_metadata(p, stream));
+}
+
 spa_status spa_build_page_table(const int32_t *req_to_token, int64_t req_to_token_stride,
                                 int32_t pool_size, const int32_t *req_pool_indices,
                                 const int32_t *seq_lens, int32_t bs, int32_t seqlen_offset,
                                 int32_t page_size, int32_t max_seq_pages, int32_t *page_table,
                                 int64_t page_table_stride, int32_t *cache_seqlens,
                                 int32_t *cu_seqlens_k, hipStream_t stream) {
-    if (bs < 0 || page_size < 1 || max_seq_pages < 0 || pool_size < 1 ||
-        page_table_stride < max_seq_pages || page_table_stride < 1 || req_to_token_stride < 1)
-        return SPA_ERR_INVALID_ARGUMENT;
-    if (max_seq_pages > 0 && (int64_t)(max_seq_pages - 1) * page_size >= req_to_token_stride)
-        return SPA_ERR_INVALID_ARGUMENT;
-    if (bs == 0) return SPA_OK;
-    if (!req_to_token || !req_pool_indices || !seq_lens || !page_table || !cache_seqlens ||
-        !cu_seqlens_k)
-        return SPA_ERR_INVALID_ARGUMENT;
-    if (bs == INT32_MAX) return SPA_ERR_INVALID_ARGUMENT;   // grid is bs + 1
-    return hip_status(spa::launch_build_page_table(
-        req_to_token, req_to_token_stride, req_pool_indices, seq_lens, bs, seqlen_offset,
-        page_size, max_seq_pages, page_table, page_table_stride, cache_seqlens, cu_seqlens_k,
-        stream));
+    return spa_build_metadata(req_to_token, req_to_token_stride, pool_size, req_pool_indices,
+                              seq_lens, bs, seqlen_offset, page_size, max_seq_pages, page_table,
+                              page_table_stride, cache_seqlens, cu_seqlens_k, spa::kQModeNone,
+                              nullptr, 0, nullptr, nullptr, nullptr, 0, nullptr, 0, nullptr, 0,
+                              stream);
 }
 
 size_t spa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

@@ -39,13 +39,38 @@ struct DecodeParams {
     float *lse;                // [B, Hq] or nullptr
 };
 
+// cu_seqlens_q handling of the metadata build.
+constexpr int32_t kQModeNone = 0;      // preset by the caller, untouched
+constexpr int32_t kQModeCumsum = 1;    // cu_seqlens_q[1 + i] = qlens[0] + ... + qlens[i]
+constexpr int32_t kQModeStrided = 2;   // cu_seqlens_q[1 + i] = (i + 1) * q_stride
+
+struct MetadataParams {
+    const int32_t *req_to_token;     // [pool, req_to_token_stride]
+    int64_t req_to_token_stride;
+    const int32_t *req_pool_indices; // [bs]
+    const int32_t *seq_lens;         // [bs]
+    int32_t bs, seqlen_offset, page_size, max_seq_pages;
+    int32_t *page_table;             // [bs, page_table_stride]
+    int64_t page_table_stride;
+    int32_t *cache_seqlens;          // [bs]
+    int32_t *cu_seqlens_k;           // [bs + 1]
+    int32_t q_mode, q_stride;
+    const int32_t *qlens;            // [bs] (cumsum mode)
+    int32_t *cu_seqlens_q;           // [bs + 1] (cumsum / strided mode)
+    const int64_t *full_to_swa;      // slot -> sliding-window slot, or nullptr
+    int32_t *swa_page_table;         // [bs, swa_page_table_stride] or nullptr
+    int64_t swa_page_table_stride;
+    const int64_t *out_cache_loc;    // [>= num_out]
+    int64_t num_out;                 // translated prefix of swa_out_cache_loc
+    int64_t *swa_out_cache_loc;      // [swa_out_len] or nullptr
+    int64_t swa_out_len;
+};
+
+// Workgroups the metadata launch needs (bs rows, one scan, the swa-out tiles).
+int64_t metadata_grid(int32_t bs, int64_t swa_out_len);
+
 // Launchers: return hipSuccess or the launch error.
-hipError_t launch_build_page_table(const int32_t *req_to_token, int64_t req_to_token_stride,
-                                   const int32_t *req_pool_indices, const int32_t *seq_lens,
-                                   int32_t bs, int32_t seqlen_offset, int32_t page_size,
-                                   int32_t max_seq_pages, int32_t *page_table,
-                                   int64_t page_table_stride, int32_t *cache_seqlens,
-                                   int32_t *cu_seqlens_k, hipStream_t stream);
+hipError_t launch_build_metadata(const MetadataParams &p, hipStream_t stream);
 
 // Producer workgroup shape (same arithmetic per split, different rounding of
 // the in-workgroup combination, so one shape always uses one mode).

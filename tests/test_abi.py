@@ -26,7 +26,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ["spa_build_page_table", "spa_paged_decode_attention", "spa_split_merge",
+    for n in ["spa_build_page_table", "spa_build_metadata", "spa_paged_decode_attention",
+              "spa_split_merge",
               "spa_decode_workspace_bytes", "spa_workspace_reset", "spa_status_string"]:
         assert n in names
 
@@ -133,6 +134,39 @@ def _meta(**kw):
 ])
 def test_page_table_argument_checks(kw, code):
     assert _meta(**kw) == code
+
+
+def _full(**kw):
+    a = dict(r2t=FAKE, r2ts=8192, pool=64, rpi=FAKE, sl=FAKE, bs=4, off=0, P=64, msp=128,
+             pt=FAKE, pts=128, cache=FAKE, cu=FAKE, qm=0, ql=None, qs=0, cuq=None, swa=None,
+             spt=None, spts=0, ocl=None, nocl=0, sout=None, soutl=0)
+    a.update(kw)
+    return spa.lib().spa_build_metadata(
+        a["r2t"], a["r2ts"], a["pool"], a["rpi"], a["sl"], a["bs"], a["off"], a["P"], a["msp"],
+        a["pt"], a["pts"], a["cache"], a["cu"], a["qm"], a["ql"], a["qs"], a["cuq"], a["swa"],
+        a["spt"], a["spts"], a["ocl"], a["nocl"], a["sout"], a["soutl"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(qm=3), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(qm=-1), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(qm=1, cuq=FAKE), spa.SPA_ERR_INVALID_ARGUMENT),         # cumsum needs qlens
+    (dict(qm=1, ql=FAKE), spa.SPA_ERR_INVALID_ARGUMENT),          # ... and cu_seqlens_q
+    (dict(qm=2), spa.SPA_ERR_INVALID_ARGUMENT),                   # strided needs cu_seqlens_q
+    (dict(spt=FAKE, spts=128), spa.SPA_ERR_INVALID_ARGUMENT),     # swa table needs the map
+    (dict(spt=FAKE, spts=100, swa=FAKE), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(sout=FAKE, soutl=8, ocl=FAKE, nocl=4), spa.SPA_ERR_INVALID_ARGUMENT),  # needs the map
+    (dict(sout=FAKE, soutl=-1), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(sout=FAKE, soutl=8, ocl=FAKE, nocl=-1, swa=FAKE), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(sout=FAKE, soutl=2**62, swa=FAKE), spa.SPA_ERR_INVALID_ARGUMENT),   # grid too large
+    (dict(sout=FAKE_ODD, soutl=8, swa=FAKE), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(swa=FAKE_ODD, spt=FAKE, spts=128), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(pts=100), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(bs=2**31 - 1), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(bs=0, qm=1, sout=FAKE, soutl=8, ocl=FAKE, nocl=8), spa.SPA_OK),   # no launch
+])
+def test_full_metadata_argument_checks(kw, code):
+    assert _full(**kw) == code
 
 
 @pytest.mark.parametrize("args,code", [
