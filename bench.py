@@ -119,6 +119,144 @@ def summarize_pmc(fetch_dir: str, write_dir: str, out_path: str, copy_mib: int, 
     return rec
 
 
+class Rig:
+    """Device copies of one workload and the calls of one step on them."""
+
+    def __init__(self, case):
+        import numpy as np
+        import torch
+
+        import split_paged_attention_amd as spa
+        self.case = case
+        dev = "cuda:0"
+
+        def bf16(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(
+                torch.bfloat16)
+
+        self.q = bf16(case.q)
+        if case.kv_dtype == "bf16":
+            k0, v0 = bf16(case.k_pages), bf16(case.v_pages)
+            ks0 = vs0 = None
+        else:
+            k0 = torch.from_numpy(case.k_pages).to(dev)
+            v0 = torch.from_numpy(case.v_pages).to(dev)
+            ks0 = torch.from_numpy(case.k_scales).to(dev)
+            vs0 = torch.from_numpy(case.v_scales).to(dev)
+        # two copies of the pool alternate so consecutive calls read new addresses
+        self.copies = [(k0, v0, ks0, vs0),
+                       (k0.clone(), v0.clone(), None if ks0 is None else ks0.clone(),
+                        None if vs0 is None else vs0.clone())]
+        self.r2t = torch.from_numpy(case.req_to_token).to(dev)
+        self.rpi = torch.from_numpy(case.req_pool_indices).to(dev)
+        self.sl = torch.from_numpy(case.seq_lens).to(dev)
+        B, Hq, D, S = case.batch, case.num_q_heads, case.head_dim, case.num_splits
+        self.pt = torch.empty((B, case.max_seq_pages), dtype=torch.int32, device=dev)
+        self.cache = torch.empty((B,), dtype=torch.int32, device=dev)
+        self.cu = torch.empty((B + 1,), dtype=torch.int32, device=dev)
+        self.out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+        self.ws = spa.new_workspace(B, Hq, case.num_kv_heads, D, S, device=dev)
+        self.spa = spa
+        self.merge = None
+        self.producer = None
+        self.k1()                     # attention reads the page table this builds
+        torch.cuda.synchronize()
+
+    def k1(self):
+        c = self.case
+        self.spa.build_page_table(self.r2t, self.rpi, self.sl, c.page_size, c.max_seq_pages,
+                                  page_table=self.pt, cache_seqlens=self.cache,
+                                  cu_seqlens_k=self.cu)
+
+    def attn(self, i):
+        c = self.case
+        k, v, ks, vs = self.copies[i % 2]
+        self.spa.paged_decode_attention(self.q, k, v, self.pt, self.sl, c.num_splits,
+                                        float(c.scale), kv_dtype=c.kv_dtype, k_scales=ks,
+                                        v_scales=vs, workspace=self.ws, out=self.out,
+                                        lse=self.lse, merge=self.merge,
+                                        producer=self.producer)
+
+
+def capture(fn):
+    """Two HIP graphs of fn(0) and fn(1), after a warm-up on a side stream."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(2):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    gl = []
+    for i in range(2):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn(i)
+        gl.append(g)
+    return gl
+
+
+def time_graphs(gl, R):
+    """Microseconds per replay over R back-to-back replays between two events."""
+    import torch
+    for i in range(20):
+        gl[i % 2].replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(R):
+        gl[i % 2].replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / R
+
+
+def time_eager(fn, K, warmup=10):
+    """Per-call microseconds (mean, median) from events around each of K calls."""
+    import numpy as np
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    for i in range(K):
+        ev[i][0].record()
+        fn(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    us = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    return float(np.mean(us)), float(np.median(us))
+
+
+def ablation(args) -> int:
+    """Launch-gap ablation: every workload, eager (events around each call)
+    and HIP-graph replay, merge fused into the producer launch vs a second
+    launch, for each producer shape the workload supports.  One JSON line."""
+    import workloads as W
+    cfgs = [int(x) for x in args.ablation_configs.split(",")]
+    rows = []
+    for cfg in cfgs:
+        case = W.make_config(cfg)
+        rig = Rig(case)
+        for producer in ("head_grouped", "page_split"):
+            for merge in ("fused", "separate"):
+                rig.producer, rig.merge = producer, merge
+                e_mean, e_med = time_eager(rig.attn, args.steps)
+                g_us = time_graphs(capture(rig.attn), max(1, args.graph_replays))
+                rows.append({"workload": case.name, "producer": producer, "merge": merge,
+                             "eager_us_mean": round(e_mean, 3), "eager_us_median": round(e_med, 3),
+                             "graph_us": round(g_us, 3),
+                             "h200_graph_us_pre_pdl": H200_GRAPH_US.get(case.name)})
+                print(f"[ablation] {rows[-1]}", file=sys.stderr, flush=True)
+        del rig
+    print(json.dumps({"ablation": "launch gap: eager vs graph x fused vs two-launch merge",
+                      "rows": rows}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -134,6 +272,9 @@ def main() -> int:
                     help="turn two rocprofv3 --pmc runs into a traffic record and exit")
     ap.add_argument("--pmc-out", default=None)
     ap.add_argument("--pmc-commands", nargs="*", default=[])
+    ap.add_argument("--ablation", action="store_true",
+                    help="launch-gap ablation over workloads instead of the bench line")
+    ap.add_argument("--ablation-configs", default="1,2,3,4,5")
     args = ap.parse_args()
 
     if args.summarize_pmc:
@@ -160,48 +301,16 @@ def main() -> int:
 
     torch.cuda.set_device(0)
     spa.lib()  # fail loudly if the HIP library is missing
+    if args.ablation:
+        return ablation(args)
     t_gen = time.time()
     case = W.make_config(args.config)
     gen_s = time.time() - t_gen
+    rig = Rig(case)
     dev = "cuda:0"
-
-    def bf16(bits):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(
-            torch.bfloat16)
-
-    q = bf16(case.q)
-    if case.kv_dtype == "bf16":
-        k0, v0 = bf16(case.k_pages), bf16(case.v_pages)
-        ks0 = vs0 = None
-    else:
-        k0 = torch.from_numpy(case.k_pages).to(dev)
-        v0 = torch.from_numpy(case.v_pages).to(dev)
-        ks0 = torch.from_numpy(case.k_scales).to(dev)
-        vs0 = torch.from_numpy(case.v_scales).to(dev)
-    copies = [(k0, v0, ks0, vs0),
-              (k0.clone(), v0.clone(), None if ks0 is None else ks0.clone(),
-               None if vs0 is None else vs0.clone())]
-    r2t = torch.from_numpy(case.req_to_token).to(dev)
-    rpi = torch.from_numpy(case.req_pool_indices).to(dev)
-    sl = torch.from_numpy(case.seq_lens).to(dev)
     B, Hq, D, S = case.batch, case.num_q_heads, case.head_dim, case.num_splits
-    Hkv, P, msp = case.num_kv_heads, case.page_size, case.max_seq_pages
-    pt = torch.empty((B, msp), dtype=torch.int32, device=dev)
-    cache = torch.empty((B,), dtype=torch.int32, device=dev)
-    cu = torch.empty((B + 1,), dtype=torch.int32, device=dev)
-    out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
-    ws = spa.new_workspace(B, Hq, Hkv, D, S, device=dev)
-    scale = float(case.scale)
-
-    def k1():
-        spa.build_page_table(r2t, rpi, sl, P, msp, page_table=pt, cache_seqlens=cache,
-                             cu_seqlens_k=cu)
-
-    def attn(i):
-        k, v, ks, vs = copies[i % 2]
-        spa.paged_decode_attention(q, k, v, pt, sl, S, scale, kv_dtype=case.kv_dtype,
-                                   k_scales=ks, v_scales=vs, workspace=ws, out=out, lse=lse)
+    Hkv, P = case.num_kv_heads, case.page_size
+    k1, attn = rig.k1, rig.attn
 
     for i in range(args.warmup):
         k1()
@@ -240,34 +349,6 @@ def main() -> int:
     # HIP-graph replays: the whole step, and the attention call alone (the
     # pages quote CUDA-graph latency of the attention), two graphs each over
     # the two KV copies.  Timed back to back: R replays between two events.
-    def capture(fn):
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            for i in range(2):
-                fn(i)
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        gl = []
-        for i in range(2):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                fn(i)
-            gl.append(g)
-        return gl
-
-    def time_graphs(gl, R):
-        for i in range(20):
-            gl[i % 2].replay()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for i in range(R):
-            gl[i % 2].replay()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) * 1e3 / R
-
     def step_fn(i):
         k1()
         attn(i)

@@ -15,8 +15,10 @@
  * failure returns SPA_ERR_HIP (spa_last_hip_error() gives the hipError_t).
  * Contract violations that only the device data could reveal -- a page id
  * outside [0, num_pages), a req_pool_indices entry outside the pool, a
- * seq_len larger than the page-table row covers -- are NOT checked and give
- * undefined results (possibly a memory fault), as in the source kernels.
+ * seq_len outside [0, page_table_stride * page_size] -- give unspecified
+ * results but no out-of-bounds access: the kernels guard these reads (see
+ * each call).  Slot values inside req_to_token are not checked against
+ * anything (they are only divided, or looked up in a map of known length).
  */
 #ifndef SPA_H_
 #define SPA_H_
@@ -118,10 +120,18 @@ spa_status spa_build_page_table(const int32_t *req_to_token, int64_t req_to_toke
  *                         k < num_out:  -1 if out_cache_loc[k] < 0,
  *                                       else full_to_swa[out_cache_loc[k]]
  *                         otherwise:    0
- *   full_to_swa         int64 map from full-pool slots to sliding-window
- *                       slots (-1 = not resident), indexed by every
- *                       non-negative slot read above; may be NULL when
- *                       neither output reads it.
+ *   full_to_swa         [full_to_swa_len] int64 map from full-pool slots to
+ *                       sliding-window slots (-1 = not resident), indexed by
+ *                       every non-negative slot read above (the source sizes
+ *                       it full_size + page_size + 1); may be NULL when
+ *                       neither output reads it.  A slot at or past
+ *                       full_to_swa_len is treated as unmapped (-1) instead
+ *                       of being read.
+ *
+ * Device-side guards (not in the source, which reads whatever it is given):
+ * a req_pool_indices entry outside [0, pool_size) leaves that row of
+ * page_table and swa_page_table unwritten instead of reading outside
+ * req_to_token.  Valid inputs never reach either guard.
  *
  * cu_seqlens_q[0] is written as 0 in the two computed modes, like
  * cu_seqlens_k[0].  bs == 0 returns SPA_OK and writes nothing, the zero
@@ -137,9 +147,9 @@ spa_status spa_build_metadata(
     int32_t page_size, int32_t max_seq_pages, int32_t *page_table, int64_t page_table_stride,
     int32_t *cache_seqlens, int32_t *cu_seqlens_k, int32_t q_mode, const int32_t *qlens,
     int32_t q_stride, int32_t *cu_seqlens_q, const int64_t *full_to_swa,
-    int32_t *swa_page_table, int64_t swa_page_table_stride, const int64_t *out_cache_loc,
-    int64_t num_out_cache_loc, int64_t *swa_out_cache_loc, int64_t swa_out_len,
-    hipStream_t stream);
+    int64_t full_to_swa_len, int32_t *swa_page_table, int64_t swa_page_table_stride,
+    const int64_t *out_cache_loc, int64_t num_out_cache_loc, int64_t *swa_out_cache_loc,
+    int64_t swa_out_len, hipStream_t stream);
 
 /*
  * Bytes of workspace spa_paged_decode_attention needs: the per-split partial
@@ -171,8 +181,10 @@ spa_status spa_workspace_reset(void *workspace, size_t bytes, hipStream_t stream
  *   k_scales,
  *   v_scales    [num_pages, page_size, num_kv_heads] fp32 (SPA_KV_INT8 only,
  *               else ignored; may be NULL for bf16)
- *   page_table  [batch, page_table_stride] int32 physical page ids
+ *   page_table  [batch, page_table_stride] int32 physical page ids; an id
+ *               outside [0, num_pages) is read as a page of zeros
  *   seq_lens    [batch] int32, each in [0, page_table_stride * page_size]
+ *               (a length outside is clamped into that range)
  *   out         [batch, num_q_heads, head_dim] bf16 (output)
  *   lse         [batch, num_q_heads] fp32 (output, may be NULL):
  *               ln(sum_t exp(s_t)) with s_t = scale * q . k_t

@@ -78,8 +78,8 @@ def lib():
                                        _P, _P, _P]
     L.spa_build_page_table.restype = _ST
     L.spa_build_metadata.argtypes = [_P, _I64, _I32, _P, _P, _I32, _I32, _I32, _I32, _P, _I64,
-                                     _P, _P, _I32, _P, _I32, _P, _P, _P, _I64, _P, _I64, _P,
-                                     _I64, _P]
+                                     _P, _P, _I32, _P, _I32, _P, _P, _I64, _P, _I64, _P, _I64,
+                                     _P, _I64, _P]
     L.spa_build_metadata.restype = _ST
     L.spa_decode_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32, _I32]
     L.spa_decode_workspace_bytes.restype = _SZ
@@ -219,7 +219,8 @@ def build_metadata(req_to_token: torch.Tensor, req_pool_indices: torch.Tensor,
         _ptr(req_pool_indices), _ptr(seq_lens), bs, int(seqlen_offset), int(page_size),
         int(max_seq_pages), _ptr(page_table), page_table.stride(0), _ptr(cache_seqlens),
         _ptr(cu_seqlens_k), int(q_mode), _ptr(qlens), int(q_stride), _ptr(cu_seqlens_q),
-        _ptr(full_to_swa), _ptr(swa_page_table),
+        _ptr(full_to_swa), 0 if full_to_swa is None else full_to_swa.numel(),
+        _ptr(swa_page_table),
         0 if swa_page_table is None else swa_page_table.stride(0), _ptr(out_cache_loc),
         0 if out_cache_loc is None else out_cache_loc.numel(), _ptr(swa_out_cache_loc),
         0 if swa_out_cache_loc is None else swa_out_cache_loc.numel(), _stream(stream))

@@ -62,9 +62,9 @@ spa_status spa_build_metadata(
     int32_t page_size, int32_t max_seq_pages, int32_t *page_table, int64_t page_table_stride,
     int32_t *cache_seqlens, int32_t *cu_seqlens_k, int32_t q_mode, const int32_t *qlens,
     int32_t q_stride, int32_t *cu_seqlens_q, const int64_t *full_to_swa,
-    int32_t *swa_page_table, int64_t swa_page_table_stride, const int64_t *out_cache_loc,
-    int64_t num_out_cache_loc, int64_t *swa_out_cache_loc, int64_t swa_out_len,
-    hipStream_t stream) {
+    int64_t full_to_swa_len, int32_t *swa_page_table, int64_t swa_page_table_stride,
+    const int64_t *out_cache_loc, int64_t num_out_cache_loc, int64_t *swa_out_cache_loc,
+    int64_t swa_out_len, hipStream_t stream) {
     const int64_t min_stride = max_seq_pages > 1 ? max_seq_pages : 1;
     if (bs < 0 || page_size < 1 || max_seq_pages < 0 || pool_size < 1 ||
         page_table_stride < min_stride || req_to_token_stride < 1)
@@ -75,6 +75,7 @@ spa_status spa_build_metadata(
         q_mode != spa::kQModeStrided)
         return SPA_ERR_INVALID_ARGUMENT;
     if (swa_page_table && swa_page_table_stride < min_stride) return SPA_ERR_INVALID_ARGUMENT;
+    if (full_to_swa && full_to_swa_len < 0) return SPA_ERR_INVALID_ARGUMENT;
     if (swa_out_cache_loc && (swa_out_len < 0 || num_out_cache_loc < 0))
         return SPA_ERR_INVALID_ARGUMENT;
     int64_t num_out = 0;
@@ -100,6 +101,7 @@ spa_status spa_build_metadata(
     spa::MetadataParams p{};
     p.req_to_token = req_to_token;
     p.req_to_token_stride = req_to_token_stride;
+    p.pool_size = pool_size;
     p.req_pool_indices = req_pool_indices;
     p.seq_lens = seq_lens;
     p.bs = bs;
@@ -115,6 +117,7 @@ spa_status spa_build_metadata(
     p.qlens = qlens;
     p.cu_seqlens_q = cu_seqlens_q;
     p.full_to_swa = full_to_swa;
+    p.full_to_swa_len = full_to_swa ? full_to_swa_len : 0;
     p.swa_page_table = swa_page_table;
     p.swa_page_table_stride = swa_page_table_stride;
     p.out_cache_loc = num_out > 0 ? out_cache_loc : nullptr;
@@ -133,7 +136,7 @@ spa_status spa_build_page_table(const int32_t *req_to_token, int64_t req_to_toke
     return spa_build_metadata(req_to_token, req_to_token_stride, pool_size, req_pool_indices,
                               seq_lens, bs, seqlen_offset, page_size, max_seq_pages, page_table,
                               page_table_stride, cache_seqlens, cu_seqlens_k, spa::kQModeNone,
-                              nullptr, 0, nullptr, nullptr, nullptr, 0, nullptr, 0, nullptr, 0,
+                              nullptr, 0, nullptr, nullptr, 0, nullptr, 0, nullptr, 0, nullptr, 0,
                               stream);
 }
 
@@ -205,6 +208,7 @@ spa_status spa_paged_decode_attention(const void *q, const void *k_pages, const 
     p.hq = num_q_heads;
     p.hkv = num_kv_heads;
     p.splits = num_splits;
+    p.num_pages = num_pages;
     p.qk_scale_log2 = scale * 1.4426950408889634f;
     p.part_acc = reinterpret_cast<float *>(ws + w.acc_off);
     p.part_max = reinterpret_cast<float *>(ws + w.max_off);

@@ -200,12 +200,17 @@ __device__ __forceinline__ void merge_element(const float *__restrict__ acc,
     const float *arow = acc + row * splits * (int64_t)head_dim + d;
     constexpr int CH = kMergeChunk;
     float M = kNegInf;
-    for (int j0 = 0; j0 < splits; j0 += CH) {
-        float mv[CH];
+    // With at most CH splits one batch of loads holds all of them, and M
+    // comes from it (one memory round trip instead of two).
+    const bool one_pass = splits <= CH;
+    if (!one_pass) {
+        for (int j0 = 0; j0 < splits; j0 += CH) {
+            float mv[CH];
 #pragma unroll
-        for (int u = 0; u < CH; ++u) mv[u] = mrow[min(j0 + u, splits - 1)];
+            for (int u = 0; u < CH; ++u) mv[u] = mrow[min(j0 + u, splits - 1)];
 #pragma unroll
-        for (int u = 0; u < CH; ++u) M = fmaxf(M, mv[u]);
+            for (int u = 0; u < CH; ++u) M = fmaxf(M, mv[u]);
+        }
     }
     float l = 0.f, o[1] = {0.f};
     for (int j0 = 0; j0 < splits; j0 += CH) {
@@ -216,6 +221,10 @@ __device__ __forceinline__ void merge_element(const float *__restrict__ acc,
             mv[u] = mrow[j];
             lv[u] = lrow[j];
             av[u][0] = arow[(int64_t)j * head_dim];
+        }
+        if (one_pass) {
+#pragma unroll
+            for (int u = 0; u < CH; ++u) M = fmaxf(M, mv[u]);
         }
 #pragma unroll
         for (int u = 0; u < CH; ++u)
@@ -241,12 +250,15 @@ __device__ __forceinline__ void merge_vec_sys(__amdgpu_buffer_rsrc_t racc,
     const int arow = (hl * splits * head_dim + d0) * 4;
     auto ldf = [&](__amdgpu_buffer_rsrc_t r, int off) { return buf_ldf<kSysCoherent>(r, off, 0); };
     float M = kNegInf;
-    for (int j0 = 0; j0 < splits; j0 += CH) {
-        float mv[CH];
+    const bool one_pass = splits <= CH;   // as in merge_element
+    if (!one_pass) {
+        for (int j0 = 0; j0 < splits; j0 += CH) {
+            float mv[CH];
 #pragma unroll
-        for (int u = 0; u < CH; ++u) mv[u] = ldf(rmax, mrow + 4 * min(j0 + u, splits - 1));
+            for (int u = 0; u < CH; ++u) mv[u] = ldf(rmax, mrow + 4 * min(j0 + u, splits - 1));
 #pragma unroll
-        for (int u = 0; u < CH; ++u) M = fmaxf(M, mv[u]);
+            for (int u = 0; u < CH; ++u) M = fmaxf(M, mv[u]);
+        }
     }
     float l = 0.f, o[VEC];
 #pragma unroll
@@ -273,6 +285,10 @@ __device__ __forceinline__ void merge_vec_sys(__amdgpu_buffer_rsrc_t racc,
                     av[u][4 * q4 + 3] = __uint_as_float(w.w);
                 }
             }
+        }
+        if (one_pass) {
+#pragma unroll
+            for (int u = 0; u < CH; ++u) M = fmaxf(M, mv[u]);
         }
 #pragma unroll
         for (int u = 0; u < CH; ++u)
@@ -332,7 +348,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
     const int r = grp / grp_per_b;
     const int kvblock = grp - r * grp_per_b;
     int b, L;
-    if (p.batch <= 64) {
+    if (p.batch == 1) {   // nothing to rank: the query load need not wait for seq_lens
+        b = 0;
+        L = seq_lens[0];
+    } else if (p.batch <= 64) {
         const int Li = lane < p.batch ? seq_lens[lane] : INT32_MIN;
         int rank = 0;
         for (int k = 0; k < p.batch; ++k) {
@@ -346,6 +365,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
         b = r;
         L = seq_lens[b];
     }
+    // A length the page-table row cannot cover is cut to the row, so the
+    // page-id loads stay inside it.
+    L = (int)min((int64_t)max(L, 0), p.pt_stride * P);
     const int kvh = kvblock * kv_per_grp + (HG ? wave : 0);
     const int pages = (L + P - 1) / P;
     const int pps = (pages + S - 1) / S;
@@ -476,18 +498,27 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
     // stay in flight while the current page is computed.
     constexpr int PSTEP = HG ? 1 : NW;              // page stride of one wave
     int pg = HG ? pg0 : pg0 + wave;
+    // Rows of logical page i that are loaded: a page id outside the pool is
+    // loaded with a zero range (reads 0, touches no memory) instead of
+    // faulting, so a bad page table gives wrong numbers, never a fault.
+    auto page_rows = [&](int i, int64_t &page) {
+        const int32_t id = pt_row[i];
+        const bool ok = (uint32_t)id < (uint32_t)p.num_pages;
+        page = ok ? id : 0;
+        return ok ? min(P, L - i * P) : 0;
+    };
     if (pg < pg1) {
-        const int64_t page = pt_row[pg];
-        const int valid = min(P, L - pg * P);
-        load_k(page, valid);
-        load_v_half(page, valid, 0);
-        load_v_half(page, valid, 1);
+        int64_t page;
+        const int rows = page_rows(pg, page);
+        load_k(page, rows);
+        load_v_half(page, rows, 0);
+        load_v_half(page, rows, 1);
     }
     for (; pg < pg1; pg += PSTEP) {
         const int nxt = pg + PSTEP;
         const bool has_next = nxt < pg1;
-        const int64_t page_next = has_next ? (int64_t)pt_row[nxt] : 0;
-        const int valid_next = has_next ? min(P, L - nxt * P) : 0;
+        int64_t page_next = 0;
+        const int valid_next = has_next ? page_rows(nxt, page_next) : 0;
         const int valid = min(P, L - pg * P);       // tokens of this page that count
 
         // ---- S = Q K^T: lane (n, g) gets s[head h][token 16t + n] in sacc[t][h]

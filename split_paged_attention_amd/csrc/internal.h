@@ -30,6 +30,7 @@ struct DecodeParams {
     int64_t pt_stride;
     const int32_t *seq_lens;   // [B]
     int32_t batch, hq, hkv, splits;
+    int32_t num_pages;         // pool size: page ids outside [0, num_pages) load nothing
     float qk_scale_log2;       // scale * log2(e)
     float *part_acc;           // [B, Hq, S, D]
     float *part_max;           // [B, Hq, S], natural-log units
@@ -47,6 +48,7 @@ constexpr int32_t kQModeStrided = 2;   // cu_seqlens_q[1 + i] = (i + 1) * q_stri
 struct MetadataParams {
     const int32_t *req_to_token;     // [pool, req_to_token_stride]
     int64_t req_to_token_stride;
+    int32_t pool_size;               // rows of req_to_token
     const int32_t *req_pool_indices; // [bs]
     const int32_t *seq_lens;         // [bs]
     int32_t bs, seqlen_offset, page_size, max_seq_pages;
@@ -58,6 +60,7 @@ struct MetadataParams {
     const int32_t *qlens;            // [bs] (cumsum mode)
     int32_t *cu_seqlens_q;           // [bs + 1] (cumsum / strided mode)
     const int64_t *full_to_swa;      // slot -> sliding-window slot, or nullptr
+    int64_t full_to_swa_len;         // slots at or past it count as unmapped
     int32_t *swa_page_table;         // [bs, swa_page_table_stride] or nullptr
     int64_t swa_page_table_stride;
     const int64_t *out_cache_loc;    // [>= num_out]

@@ -70,9 +70,13 @@ __global__ __launch_bounds__(kThreads) void build_metadata_kernel(MetadataParams
     const int64_t wg = blockIdx.x;
     if (wg < p.bs) {
         const int32_t i = (int32_t)wg;
-        const int64_t row = (int64_t)p.req_pool_indices[i];
+        const int32_t row_id = p.req_pool_indices[i];
         if (tid == 0)
             p.cache_seqlens[i] = (int32_t)((uint32_t)p.seq_lens[i] + (uint32_t)p.seqlen_offset);
+        // A pool index outside the pool leaves the row's tables untouched
+        // rather than reading outside req_to_token.
+        if ((uint32_t)row_id >= (uint32_t)p.pool_size) return;
+        const int64_t row = row_id;
         const int32_t *src = p.req_to_token + row * p.req_to_token_stride;
         int32_t *dst = p.page_table + (int64_t)i * p.page_table_stride;
         int32_t *swa_dst = p.swa_page_table
@@ -82,9 +86,10 @@ __global__ __launch_bounds__(kThreads) void build_metadata_kernel(MetadataParams
             const int32_t token = src[(int64_t)c * p.page_size];
             dst[c] = floor_div_pos(token, p.page_size);
             if (swa_dst) {
-                // Slots are read only where >= 0; any negative mapped slot
-                // becomes the -1 sentinel.
-                const int64_t s = token >= 0 ? p.full_to_swa[token] : -1;
+                // The map is read only at slots inside it; any negative
+                // mapped slot becomes the -1 sentinel.
+                const int64_t s = token >= 0 && token < p.full_to_swa_len ? p.full_to_swa[token]
+                                                                           : -1;
                 swa_dst[c] = s < 0 ? -1 : (int32_t)(s / p.page_size);
             }
         }
@@ -116,7 +121,7 @@ __global__ __launch_bounds__(kThreads) void build_metadata_kernel(MetadataParams
         int64_t v = 0;
         if (k < p.num_out) {
             const int64_t loc = p.out_cache_loc[k];
-            v = loc < 0 ? -1 : p.full_to_swa[loc];
+            v = loc < 0 || loc >= p.full_to_swa_len ? -1 : p.full_to_swa[loc];
         }
         p.swa_out_cache_loc[k] = v;
     }

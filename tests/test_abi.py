@@ -139,12 +139,12 @@ def test_page_table_argument_checks(kw, code):
 def _full(**kw):
     a = dict(r2t=FAKE, r2ts=8192, pool=64, rpi=FAKE, sl=FAKE, bs=4, off=0, P=64, msp=128,
              pt=FAKE, pts=128, cache=FAKE, cu=FAKE, qm=0, ql=None, qs=0, cuq=None, swa=None,
-             spt=None, spts=0, ocl=None, nocl=0, sout=None, soutl=0)
+             swal=1 << 20, spt=None, spts=0, ocl=None, nocl=0, sout=None, soutl=0)
     a.update(kw)
     return spa.lib().spa_build_metadata(
         a["r2t"], a["r2ts"], a["pool"], a["rpi"], a["sl"], a["bs"], a["off"], a["P"], a["msp"],
         a["pt"], a["pts"], a["cache"], a["cu"], a["qm"], a["ql"], a["qs"], a["cuq"], a["swa"],
-        a["spt"], a["spts"], a["ocl"], a["nocl"], a["sout"], a["soutl"], None)
+        a["swal"], a["spt"], a["spts"], a["ocl"], a["nocl"], a["sout"], a["soutl"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -161,6 +161,7 @@ def _full(**kw):
     (dict(sout=FAKE, soutl=2**62, swa=FAKE), spa.SPA_ERR_INVALID_ARGUMENT),   # grid too large
     (dict(sout=FAKE_ODD, soutl=8, swa=FAKE), spa.SPA_ERR_INVALID_ARGUMENT),
     (dict(swa=FAKE_ODD, spt=FAKE, spts=128), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(swa=FAKE, swal=-1, spt=FAKE, spts=128), spa.SPA_ERR_INVALID_ARGUMENT),
     (dict(pts=100), spa.SPA_ERR_INVALID_ARGUMENT),
     (dict(bs=2**31 - 1), spa.SPA_ERR_INVALID_ARGUMENT),
     (dict(bs=0, qm=1, sout=FAKE, soutl=8, ocl=FAKE, nocl=8), spa.SPA_OK),   # no launch
