@@ -31,6 +31,7 @@ _lib = None
 
 KV_BF16 = 0
 KV_INT8 = 1
+KV_FP8 = 2
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
@@ -149,12 +150,20 @@ def _att_args(q, k_pages, v_pages, k_scales, v_scales, kv_dtype, page_table, seq
         k = _c(k_pages, np.uint16)
         v = _c(v_pages, np.uint16)
         ks = vs = None
-    else:
+    elif kv_dtype in ("int8", KV_INT8):
         kd = KV_INT8
         k = _c(k_pages, np.int8)
         v = _c(v_pages, np.int8)
         ks = _c(k_scales, np.float32)
         vs = _c(v_scales, np.float32)
+    elif kv_dtype in ("fp8", KV_FP8):
+        kd = KV_FP8
+        k = _c(k_pages, np.uint8)
+        v = _c(v_pages, np.uint8)
+        ks = _c(k_scales, np.float32)
+        vs = _c(v_scales, np.float32)
+    else:
+        raise ValueError(f"unknown kv_dtype {kv_dtype!r}")
     pt = _c(page_table, np.int32)
     sl = _c(seq_lens, np.int32)
     keep = (q, k, v, ks, vs, pt, sl)

@@ -32,6 +32,8 @@
  *  - query head h reads KV head h / (Hq / Hkv).
  *  - s_t = scale * q . k_t with scale the float32 value given, widened.
  *  - int8 KV: k = (double)q8 * (double)sigma per (token, kv head).
+ *  - fp8 KV (OCP e4m3, bias 7, no infinities; codes 0x7F / 0xFF are NaN):
+ *    k = e4m3(code) * (double)sigma per (token, kv head).
  *  - lse = m + ln(sum_t exp(s_t - m)), natural log, scale applied.
  *  - split j of a request covers logical pages [j*pps, min((j+1)*pps, pages))
  *    with pages = ceil(L/P), pps = ceil(pages/S); an empty split's state is
@@ -46,6 +48,7 @@
 
 #define ORACLE_KV_BF16 0
 #define ORACLE_KV_INT8 1
+#define ORACLE_KV_FP8 2
 
 /* bf16 bit pattern -> double: the bits are the top half of a float32. */
 static double bf16_to_double(uint16_t bits) {
@@ -53,6 +56,16 @@ static double bf16_to_double(uint16_t bits) {
     float f;
     memcpy(&f, &u, sizeof f);
     return (double)f;
+}
+
+/* Value of an OCP e4m3 code: sign bit 7, exponent bits 6..3 with bias 7,
+ * mantissa bits 2..0; exponent field 0 is subnormal (2^-6 * m/8); exponent
+ * 15 with mantissa 7 is NaN; there are no infinities. */
+static double e4m3_to_double(uint8_t code) {
+    int sign = code >> 7, e = (code >> 3) & 15, m = code & 7;
+    if (e == 15 && m == 7) return NAN;
+    double v = e == 0 ? ldexp(m / 8.0, -6) : ldexp(1.0 + m / 8.0, e - 7);
+    return sign ? -v : v;
 }
 
 /* Python-style floor division of a (possibly negative) int by a positive int. */
@@ -180,8 +193,12 @@ static double kv_elem(const oracle_args *a, int which, int b, int t, int kvh, in
         const uint16_t *base = (const uint16_t *)(which ? a->v_pages : a->k_pages);
         return bf16_to_double(base[idx]);
     }
-    const int8_t *base = (const int8_t *)(which ? a->v_pages : a->k_pages);
     const float *sc = which ? a->v_scales : a->k_scales;
+    if (a->kv_dtype == ORACLE_KV_FP8) {
+        const uint8_t *base = (const uint8_t *)(which ? a->v_pages : a->k_pages);
+        return e4m3_to_double(base[idx]) * (double)sc[row * a->Hkv + kvh];
+    }
+    const int8_t *base = (const int8_t *)(which ? a->v_pages : a->k_pages);
     return (double)base[idx] * (double)sc[row * a->Hkv + kvh];
 }
 

@@ -10,9 +10,19 @@ from scipy.special import logsumexp, softmax
 from workloads import bf16_bits_to_f32
 
 
+def e4m3_codes_to_f64(codes):
+    """OCP e4m3 codes -> values through PyTorch's float8_e4m3fn dtype (a
+    library conversion, independent of the oracle's own decoding)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float32).numpy().astype(np.float64)
+
+
 def dequant_rows(k, ks):
     if ks is None:
         return bf16_bits_to_f32(k).astype(np.float64)
+    if k.dtype == np.uint8:   # e4m3 codes
+        return e4m3_codes_to_f64(k) * ks.astype(np.float64)[..., None]
     return k.astype(np.float64) * ks.astype(np.float64)[..., None]
 
 

@@ -40,6 +40,11 @@ MUTANTS = {
     "swa_padding_minus_one": ("swa_out_cache_loc[k] = 0;", "swa_out_cache_loc[k] = -1;"),
     "swa_out_untranslated": ("swa_out_cache_loc[k] = loc < 0 ? -1 : swa[loc];",
                              "swa_out_cache_loc[k] = loc;"),
+    "fp8_exponent_bias": ("ldexp(1.0 + m / 8.0, e - 7)", "ldexp(1.0 + m / 8.0, e - 8)"),
+    "fp8_subnormal_as_normal": ("e == 0 ? ldexp(m / 8.0, -6)", "e == 0 ? ldexp(1.0 + m / 8.0, -7)"),
+    "fp8_sign_dropped": ("return sign ? -v : v;", "return v;"),
+    "fp8_scale_dropped": ("return e4m3_to_double(base[idx]) * (double)sc[row * a->Hkv + kvh];",
+                          "return e4m3_to_double(base[idx]);"),
     "swa_num_out_max": ("n_out_cache_loc < swa_out_len ? n_out_cache_loc : swa_out_len",
                         "n_out_cache_loc > swa_out_len ? swa_out_len : swa_out_len"),
 }

@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import workloads as W
-from tests.brute import dense_attention
+from tests.brute import dense_attention, e4m3_codes_to_f64
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -374,7 +374,7 @@ def _repermute(c, seed):
     return k, v, pl, kw
 
 
-@pytest.mark.parametrize("kv", ["bf16", "int8"])
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8"])
 def test_physical_page_permutation_is_bit_identical(kv):
     c = _small([50, 3, 17], num_pages=30, kv_dtype=kv)
     out, lse = oracle.case_attention(c)
@@ -412,6 +412,67 @@ def test_gqa_identical_queries_in_group_give_identical_outputs():
     for h in range(1, 4):
         assert np.array_equal(o[:, h], o[:, 0]) and np.array_equal(l[:, h], l[:, 0])
     assert not np.array_equal(o[:, 4], o[:, 0])
+
+
+def _fp8_every_code_case():
+    """Two one-token requests whose K and V rows (8 kv heads x 128 dims each)
+    hold every finite e4m3 code; NaN codes are replaced by 0."""
+    c = _small([1, 1], kv_dtype="fp8", num_q_heads=32, num_kv_heads=8, head_dim=128)
+    codes = (np.arange(2 * 8 * 128) % 256).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0
+    codes = codes.reshape(2, 8, 128)
+    for b in range(2):
+        page = c.page_list[b, 0]
+        c.k_pages[page, 0] = codes[b]
+        c.v_pages[page, 0] = np.roll(codes[b], 3, axis=1)
+    return c
+
+
+def test_fp8_value_decoding_of_every_code_matches_torch():
+    """One-token context: the output is the dequantised V row itself, so each
+    element must equal PyTorch's e4m3 value of the code times sigma_v."""
+    c = _fp8_every_code_case()
+    out, _ = oracle.case_attention(c)
+    for b in range(2):
+        _, v, _, vs = c.dense_kv(b)
+        want = e4m3_codes_to_f64(v[0]) * vs[0].astype(np.float64)[:, None]   # [Hkv, D]
+        for h in range(c.num_q_heads):
+            assert np.array_equal(out[b, h], want[h // c.group]), (b, h)
+
+
+def test_fp8_key_decoding_of_every_code_matches_torch():
+    """One-token context with a one-hot query: lse = s = scale * sigma_k *
+    e4m3(code) of the selected dimension, for every dimension and head."""
+    base = _fp8_every_code_case()
+    for d0 in range(0, 128, 4):
+        q = np.zeros((2, 32, 128), np.float32)
+        for h in range(32):
+            q[:, h, (d0 + h % 4) % 128] = 1.0
+        qb = W.f32_to_bf16_bits(q)
+        _, lse = oracle.paged_attention(qb, base.k_pages, base.v_pages, base.page_list,
+                                        base.seq_lens, num_kv_heads=8, page_size=base.page_size,
+                                        scale=base.scale, kv_dtype="fp8",
+                                        k_scales=base.k_scales, v_scales=base.v_scales)
+        for b in range(2):
+            k, _, ks, _ = base.dense_kv(b)
+            kv = e4m3_codes_to_f64(k[0]) * ks[0].astype(np.float64)[:, None]
+            for h in range(32):
+                want = float(base.scale) * kv[h // 4, (d0 + h % 4) % 128]
+                assert lse[b, h] == pytest.approx(want, rel=1e-15, abs=1e-300), (d0, b, h)
+
+
+def test_fp8_known_code_values():
+    """Values fixed by the e4m3 format: 448 is the largest finite value,
+    2^-6 the smallest normal, 2^-9 the smallest subnormal, 1.0 is 0x38, and
+    the sign bit negates."""
+    c = _small([1], kv_dtype="fp8", num_q_heads=32, num_kv_heads=8, head_dim=128)
+    page = c.page_list[0, 0]
+    row = np.zeros((8, 128), np.uint8)
+    row[0, :6] = [0x7E, 0x08, 0x01, 0x38, 0xB8, 0xFE]
+    c.v_pages[page, 0] = row
+    c.v_scales[page, 0] = 1.0
+    out, _ = oracle.case_attention(c)
+    assert out[0, 0, :6].tolist() == [448.0, 2.0**-6, 2.0**-9, 1.0, -1.0, -448.0]
 
 
 def test_int8_dequantisation_is_exact_product():

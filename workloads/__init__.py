@@ -25,6 +25,10 @@ seq_lens [bs]):
 * int8 values: per (page, row, kv_head) a float32 N(0,1) vector over D is
   quantised symmetrically, sigma = amax/127 (float32),
   q8 = clamp(rint(x/sigma), -127, 127) with rint rounding half to even.
+* fp8 values (OCP e4m3, "e4m3fn": bias 7, no infinities, 448 the largest
+  finite value): per (page, row, kv_head) sigma = amax/448 (float32) and
+  each x/sigma (float32) is rounded to the nearest e4m3 value, ties to the
+  even code, stored as uint8 codes (never a NaN code).
 
 Determinism: large arrays are split into fixed chunks along their first axis
 and chunk i draws from PCG64(SeedSequence(seed, spawn_key=(tag, i))); the
@@ -120,6 +124,44 @@ def normal_int8(shape, seed: int, tag: int):
     return q8, sig
 
 
+def _e4m3_magnitudes() -> np.ndarray:
+    """Values of the non-negative finite e4m3 codes 0..126, increasing."""
+    c = np.arange(127)
+    e, m = c >> 3, (c & 7).astype(np.float64)
+    return np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 7))
+
+
+def encode_e4m3(y: np.ndarray) -> np.ndarray:
+    """Round float values to e4m3 codes: nearest, ties to the even code,
+    magnitudes above 448 saturated to 448."""
+    tab = _e4m3_magnitudes()
+    a = np.minimum(np.abs(y.astype(np.float64)), tab[-1])
+    hi = np.clip(np.searchsorted(tab, a, side="left"), 0, 126)
+    lo = np.maximum(hi - 1, 0)
+    dlo, dhi = a - tab[lo], tab[hi] - a
+    code = np.where((dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0)), hi, lo)
+    return (code | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
+
+
+def normal_fp8(shape, seed: int, tag: int):
+    """e4m3 quantisation of N(0,1) vectors over the last axis, scaled so the
+    largest magnitude becomes 448.  Returns (codes uint8 [..., D], sigma
+    float32 [...])."""
+    codes = np.empty(shape, dtype=np.uint8)
+    sig = np.empty(shape[:-1], dtype=np.float32)
+
+    def fill(i, lo, hi, rng):
+        x = rng.standard_normal((hi - lo,) + tuple(shape[1:]), dtype=np.float32)
+        amax = np.max(np.abs(x), axis=-1)
+        s = (amax / np.float32(448.0)).astype(np.float32)
+        s = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+        codes[lo:hi] = encode_e4m3((x / s[..., None]).astype(np.float32))
+        sig[lo:hi] = s
+
+    _chunked(shape, seed, tag, fill)
+    return codes, sig
+
+
 @dataclass
 class DecodeCase:
     """One seeded decode batch: query, paged KV pool and the req_to_token map."""
@@ -132,12 +174,12 @@ class DecodeCase:
     page_size: int
     num_pages: int
     num_splits: int
-    kv_dtype: str                       # "bf16" or "int8"
+    kv_dtype: str                       # "bf16", "int8" or "fp8"
     scale: np.float32
     q: np.ndarray                       # uint16 bf16 bits [B, Hq, D]
-    k_pages: np.ndarray                 # uint16 or int8 [num_pages, P, Hkv, D]
+    k_pages: np.ndarray                 # uint16, int8 or uint8 (e4m3) [num_pages, P, Hkv, D]
     v_pages: np.ndarray
-    k_scales: Optional[np.ndarray]      # float32 [num_pages, P, Hkv] (int8 only)
+    k_scales: Optional[np.ndarray]      # float32 [num_pages, P, Hkv] (int8 / fp8 only)
     v_scales: Optional[np.ndarray]
     seq_lens: np.ndarray                # int32 [B]
     req_to_token: np.ndarray            # int32 [rows, stride]
@@ -171,7 +213,7 @@ class DecodeCase:
 
     def kv_bytes_per_token(self) -> int:
         per = self.num_kv_heads * self.head_dim * (2 if self.kv_dtype == "bf16" else 1)
-        if self.kv_dtype == "int8":
+        if self.kv_dtype != "bf16":
             per += self.num_kv_heads * 4
         return 2 * per
 
@@ -187,7 +229,7 @@ def make_case(*, seed: int, seq_lens, num_pages: int, num_splits: int,
     seq_lens = np.asarray(seq_lens, dtype=np.int32).reshape(-1)
     B = int(seq_lens.shape[0])
     P = page_size
-    if kv_dtype not in ("bf16", "int8"):
+    if kv_dtype not in ("bf16", "int8", "fp8"):
         raise ValueError(kv_dtype)
     if B > req_pool_rows:
         raise ValueError("batch larger than the req_to_token pool")
@@ -209,9 +251,12 @@ def make_case(*, seed: int, seq_lens, num_pages: int, num_splits: int,
         k_pages = normal_bf16(shape, seed, _TAG_K)
         v_pages = normal_bf16(shape, seed, _TAG_V)
         k_scales = v_scales = None
-    else:
+    elif kv_dtype == "int8":
         k_pages, k_scales = normal_int8(shape, seed, _TAG_K)
         v_pages, v_scales = normal_int8(shape, seed, _TAG_V)
+    else:
+        k_pages, k_scales = normal_fp8(shape, seed, _TAG_K)
+        v_pages, v_scales = normal_fp8(shape, seed, _TAG_V)
 
     rpi = _gen(seed, _TAG_RPI).choice(req_pool_rows, size=B, replace=False).astype(np.int32)
     fill_rng = _gen(seed, _TAG_FILL)
@@ -238,7 +283,8 @@ def make_case(*, seed: int, seq_lens, num_pages: int, num_splits: int,
 
 
 # The five measured workloads: lmdeploy's H200 table (batch 1/ctx 1K,
-# batch 1/ctx 8K, batch 8/ctx 1K, batch 32/ctx 8K) plus a ragged int8 batch.
+# batch 1/ctx 8K, batch 8/ctx 1K, batch 32/ctx 8K) plus a ragged int8 batch;
+# then the headline shape with e4m3 KV.
 CONFIGS = {
     1: dict(name="b1_ctx1k_s4_bf16", lens=("const", 1, 1024), num_pages=256,
             num_splits=4, kv_dtype="bf16"),
@@ -250,6 +296,8 @@ CONFIGS = {
             num_splits=16, kv_dtype="bf16"),
     5: dict(name="b32_ragged8k_s16_int8", lens=("uniform", 32, 1, 8192), num_pages=4096,
             num_splits=16, kv_dtype="int8"),
+    6: dict(name="b32_ctx8k_s16_fp8", lens=("const", 32, 8192), num_pages=4096,
+            num_splits=16, kv_dtype="fp8"),
 }
 
 
