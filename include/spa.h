@@ -42,7 +42,9 @@ typedef enum spa_status {
 
 typedef enum spa_kv_dtype {
     SPA_KV_BF16 = 0,   /* K/V pages hold bf16 values */
-    SPA_KV_INT8 = 1    /* K/V pages hold int8 codes; value = code * fp32 scale per (token, kv head) */
+    SPA_KV_INT8 = 1,   /* K/V pages hold int8 codes; value = code * fp32 scale per (token, kv head) */
+    SPA_KV_FP8 = 2     /* K/V pages hold OCP e4m3 codes (bias 7, largest finite 448, 0x7F/0xFF NaN);
+                          value = e4m3(code) * fp32 scale per (token, kv head) */
 } spa_kv_dtype;
 
 /* flags for spa_paged_decode_attention (0 = the library chooses).  None of
@@ -175,12 +177,12 @@ spa_status spa_workspace_reset(void *workspace, size_t bytes, hipStream_t stream
  *
  *   q           [batch, num_q_heads, head_dim] bf16, contiguous, 16-byte aligned
  *   k_pages,
- *   v_pages     [num_pages, page_size, num_kv_heads, head_dim], bf16 or int8
- *               codes, contiguous, 16-byte aligned; token t of request b is
+ *   v_pages     [num_pages, page_size, num_kv_heads, head_dim], bf16, int8
+ *               codes or e4m3 codes, contiguous, 16-byte aligned; token t of request b is
  *               row (page_table[b*page_table_stride + t/page_size], t % page_size)
  *   k_scales,
- *   v_scales    [num_pages, page_size, num_kv_heads] fp32 (SPA_KV_INT8 only,
- *               else ignored; may be NULL for bf16)
+ *   v_scales    [num_pages, page_size, num_kv_heads] fp32 (SPA_KV_INT8 and
+ *               SPA_KV_FP8; ignored and may be NULL for bf16)
  *   page_table  [batch, page_table_stride] int32 physical page ids; an id
  *               outside [0, num_pages) is read as a page of zeros
  *   seq_lens    [batch] int32, each in [0, page_table_stride * page_size]
@@ -202,7 +204,7 @@ spa_status spa_workspace_reset(void *workspace, size_t bytes, hipStream_t stream
  * flags (both merges, both producers) are SPA_ERR_INVALID_ARGUMENT.
  *
  * Supported: head_dim 128, page_size 64, num_q_heads == 4 * num_kv_heads,
- * kv_dtype bf16 or int8, 1 <= num_splits <= 1024 (SPA_DECODE_HEAD_GROUPED
+ * kv_dtype bf16, int8 or fp8, 1 <= num_splits <= 1024 (SPA_DECODE_HEAD_GROUPED
  * also needs an even num_kv_heads); otherwise SPA_ERR_UNSUPPORTED.  workspace: spa_decode_workspace_bytes(...) bytes,
  * 16-byte aligned, zeroed before first use (see spa_workspace_reset);
  * concurrent calls must not share a workspace.  batch == 0 returns SPA_OK

@@ -19,7 +19,7 @@ __all__ = [
     "SpaError", "lib", "status_string", "build_page_table", "decode_workspace_bytes",
     "workspace_reset", "new_workspace", "paged_decode_attention", "split_merge",
     "SPA_OK", "SPA_ERR_INVALID_ARGUMENT", "SPA_ERR_UNSUPPORTED",
-    "SPA_ERR_WORKSPACE_TOO_SMALL", "SPA_ERR_HIP", "SPA_KV_BF16", "SPA_KV_INT8",
+    "SPA_ERR_WORKSPACE_TOO_SMALL", "SPA_ERR_HIP", "SPA_KV_BF16", "SPA_KV_INT8", "SPA_KV_FP8",
     "SPA_DECODE_SEPARATE_MERGE", "SPA_DECODE_FUSED_MERGE", "SPA_DECODE_HEAD_GROUPED",
     "SPA_DECODE_PAGE_SPLIT",
 ]
@@ -33,6 +33,7 @@ SPA_ERR_WORKSPACE_TOO_SMALL = 3
 SPA_ERR_HIP = 4
 SPA_KV_BF16 = 0
 SPA_KV_INT8 = 1
+SPA_KV_FP8 = 2
 SPA_DECODE_SEPARATE_MERGE = 0x1
 SPA_DECODE_FUSED_MERGE = 0x2
 SPA_DECODE_HEAD_GROUPED = 0x4
@@ -270,8 +271,9 @@ def paged_decode_attention(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torc
                            producer: Optional[str] = None,
                            stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """spa_paged_decode_attention.  q [B, Hq, D] bf16; k/v_pages
-    [num_pages, P, Hkv, D] bf16 or int8; k/v_scales [num_pages, P, Hkv] fp32
-    for int8; page_table [B, stride] int32; seq_lens [B] int32.
+    [num_pages, P, Hkv, D] bf16, int8, or e4m3 codes (uint8 or
+    float8_e4m3fn) for kv_dtype "fp8"; k/v_scales [num_pages, P, Hkv] fp32
+    for int8 and fp8; page_table [B, stride] int32; seq_lens [B] int32.
     Returns (out [B, Hq, D] bf16, lse [B, Hq] fp32).
 
     merge: None (library default), "fused" or "separate" (``separate_merge=True``
@@ -280,8 +282,10 @@ def paged_decode_attention(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torc
     if q.dim() != 3:
         raise ValueError("q must be [batch, num_q_heads, head_dim]")
     B, Hq, D = q.shape
-    kvd = {"bf16": SPA_KV_BF16, "int8": SPA_KV_INT8}[kv_dtype]
-    kv_t = torch.bfloat16 if kvd == SPA_KV_BF16 else torch.int8
+    kvd = {"bf16": SPA_KV_BF16, "int8": SPA_KV_INT8, "fp8": SPA_KV_FP8}[kv_dtype]
+    kv_t = {SPA_KV_BF16: torch.bfloat16, SPA_KV_INT8: torch.int8, SPA_KV_FP8: torch.uint8}[kvd]
+    if kvd == SPA_KV_FP8 and k_pages.dtype == torch.float8_e4m3fn:
+        kv_t = torch.float8_e4m3fn
     _need(k_pages, "k_pages", kv_t)
     _need(v_pages, "v_pages", kv_t)
     if k_pages.dim() != 4 or k_pages.shape != v_pages.shape:
@@ -289,10 +293,10 @@ def paged_decode_attention(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torc
     num_pages, P, Hkv, Dk = k_pages.shape
     if Dk != D:
         raise ValueError("head_dim of q and the KV pages differ")
-    if kvd == SPA_KV_INT8:
+    if kvd != SPA_KV_BF16:
         for nm, t in (("k_scales", k_scales), ("v_scales", v_scales)):
             if t is None:
-                raise ValueError(f"{nm} is required for int8 KV")
+                raise ValueError(f"{nm} is required for {kv_dtype} KV")
             _need(t, nm, torch.float32)
             if tuple(t.shape) != (num_pages, P, Hkv):
                 raise ValueError(f"{nm} must be [num_pages, page_size, num_kv_heads]")

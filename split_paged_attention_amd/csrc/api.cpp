@@ -166,7 +166,9 @@ spa_status spa_paged_decode_attention(const void *q, const void *k_pages, const 
         num_pages < 1 || num_splits < 1 || page_table_stride < 1)
         return SPA_ERR_INVALID_ARGUMENT;
     if (num_q_heads % num_kv_heads != 0) return SPA_ERR_INVALID_ARGUMENT;
-    if (kv_dtype != SPA_KV_BF16 && kv_dtype != SPA_KV_INT8) return SPA_ERR_INVALID_ARGUMENT;
+    if (kv_dtype != SPA_KV_BF16 && kv_dtype != SPA_KV_INT8 && kv_dtype != SPA_KV_FP8)
+        return SPA_ERR_INVALID_ARGUMENT;
+    const bool quant = kv_dtype != SPA_KV_BF16;
     const uint32_t known = SPA_DECODE_SEPARATE_MERGE | SPA_DECODE_FUSED_MERGE |
                            SPA_DECODE_HEAD_GROUPED | SPA_DECODE_PAGE_SPLIT;
     if ((flags & ~known) != 0) return SPA_ERR_INVALID_ARGUMENT;
@@ -184,11 +186,11 @@ spa_status spa_paged_decode_attention(const void *q, const void *k_pages, const 
     if (batch == 0) return SPA_OK;
     if (!q || !k_pages || !v_pages || !page_table || !seq_lens || !out || !workspace)
         return SPA_ERR_INVALID_ARGUMENT;
-    if (kv_dtype == SPA_KV_INT8 && (!k_scales || !v_scales)) return SPA_ERR_INVALID_ARGUMENT;
+    if (quant && (!k_scales || !v_scales)) return SPA_ERR_INVALID_ARGUMENT;
     if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) ||
         !aligned(workspace, 16) || !aligned(out, 2) || !aligned(page_table, 4) ||
         !aligned(seq_lens, 4) || (lse && !aligned(lse, 4)) ||
-        (kv_dtype == SPA_KV_INT8 && (!aligned(k_scales, 4) || !aligned(v_scales, 4))))
+        (quant && (!aligned(k_scales, 4) || !aligned(v_scales, 4))))
         return SPA_ERR_INVALID_ARGUMENT;
     const spa::WorkspaceLayout w =
         spa::workspace_layout(batch, num_q_heads, num_kv_heads, head_dim, num_splits);
@@ -227,7 +229,11 @@ spa_status spa_paged_decode_attention(const void *q, const void *k_pages, const 
     if (flags & SPA_DECODE_SEPARATE_MERGE) fused = false;
     if (flags & SPA_DECODE_FUSED_MERGE) fused = true;
     return hip_status(
-        spa::launch_decode(p, kv_dtype == SPA_KV_INT8 ? 1 : 0, mode, fused, stream));
+        spa::launch_decode(p,
+                           kv_dtype == SPA_KV_INT8 ? spa::kKvInt8
+                           : kv_dtype == SPA_KV_FP8 ? spa::kKvFp8
+                                                    : spa::kKvBf16,
+                           mode, fused, stream));
 }
 
 spa_status spa_split_merge(const float *partial_acc, const float *partial_max,

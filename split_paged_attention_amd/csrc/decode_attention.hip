@@ -30,6 +30,9 @@
 //   * int8 KV: key codes become exact f16 values for the f16 matrix cores
 //     (query scaled by a per-head power of two), value codes exact f16
 //     1152 + code for v_dot2_f32_f16, the bias removed once per split;
+//   * fp8 (e4m3) KV: the same f16 matrix cores and f16 dot products; the
+//     hardware converter turns codes into exact f16 values (keys at scale 1,
+//     values at scale 1/256, the 256 going into the value scale);
 //   * P.V on the vector ALUs with v_dot2_f32_bf16: lane (r, c) owns dims
 //     8c..8c+7 of tokens 4i + r (so one V load instruction reads 4 whole
 //     256-byte rows), pairs tokens t and t + 16 in one dot2, and gets the
@@ -149,6 +152,33 @@ __device__ __forceinline__ f16x8_t i8x8_to_f16(uint2 w) {
     return f16x8_t{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
 }
 
+// Eight e4m3 key codes (dims in byte order) -> their exact f16 values; the
+// converter takes bytes 0-1 (word_sel false) or 2-3 of a word, low byte to
+// the low half.
+__device__ __forceinline__ f16x8_t e4m3x8_to_f16(uint2 w) {
+    const f16x2_t h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.x, 1.f, false);
+    const f16x2_t h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.x, 1.f, true);
+    const f16x2_t h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.f, false);
+    const f16x2_t h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.f, true);
+    return f16x8_t{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+}
+
+// e4m3 value codes -> f16 pairs for the token pair (a, b): bytes k and k+1
+// of wa and wb (k = 0 or 2) give the pairs (a_k, b_k) and (a_k+1, b_k+1),
+// each value / 256 (exact: the converter keeps f16 subnormals).
+constexpr float kF8ValueScale = 256.f;
+template <int K>
+__device__ __forceinline__ void e4m3_pairs_f16(uint32_t wb, uint32_t wa, uint32_t &p0,
+                                               uint32_t &p1) {
+    constexpr uint32_t sel = (uint32_t)K | ((uint32_t)(4 + K) << 8) | ((uint32_t)(K + 1) << 16) |
+                             ((uint32_t)(5 + K) << 24);
+    const uint32_t w = __builtin_amdgcn_perm(wb, wa, sel);   // a_k, b_k, a_k+1, b_k+1
+    p0 = __builtin_bit_cast(uint32_t,
+                            __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.f / kF8ValueScale, false));
+    p1 = __builtin_bit_cast(uint32_t,
+                            __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.f / kF8ValueScale, true));
+}
+
 // int8 value codes -> exact f16, biased: byte k of wa (token a) and of wb
 // (token b) become the f16 pair (1152 + a_k, 1152 + b_k).  With its sign bit
 // flipped a code is x + 128 in [1, 255]; placed as the low mantissa byte under
@@ -168,7 +198,8 @@ __device__ __forceinline__ uint32_t i8_pair_f16(uint32_t wb, uint32_t wa) {
 //   M = max_j m_j;  for each non-empty j: w = 2^((m_j - M) log2 e),
 //   l = fma(w, l_j, l),  o = fma(w, acc_j, o);  out = bf16(o / l), lse = M + ln l.
 // Loads are issued CH splits at a time so that their latencies overlap.
-constexpr int kMergeChunk = 8;
+constexpr int kMergeChunk = 8;            // fused tail (VEC outputs per thread)
+constexpr int kMergeChunkSeparate = 16;   // merge kernel (one output per thread)
 
 template <int VEC>
 __device__ __forceinline__ void merge_step(float mj, float lj, const float (&aj)[VEC], float M,
@@ -188,7 +219,9 @@ __device__ __forceinline__ void merge_finish(float M, float l, const float (&o)[
     if (write_lse) *lse = l > 0.f ? M + __builtin_amdgcn_logf(l) * kLn2 : kNegInf;
 }
 
-// One output element of row (b, h), plain loads (separate merge kernel).
+// One output element of row (b, h), plain loads (separate merge kernel),
+// CH splits per batch of loads.
+template <int CH>
 __device__ __forceinline__ void merge_element(const float *__restrict__ acc,
                                               const float *__restrict__ mx,
                                               const float *__restrict__ sum, int splits,
@@ -198,7 +231,6 @@ __device__ __forceinline__ void merge_element(const float *__restrict__ acc,
     const float *mrow = mx + row * splits;
     const float *lrow = sum + row * splits;
     const float *arow = acc + row * splits * (int64_t)head_dim + d;
-    constexpr int CH = kMergeChunk;
     float M = kNegInf;
     // With at most CH splits one batch of loads holds all of them, and M
     // comes from it (one memory round trip instead of two).
@@ -310,11 +342,15 @@ __device__ __forceinline__ void st_sys(float *p, float v) {
 // HG = true:  a workgroup is one (request, block of NW kv heads, split); wave w
 //             is kv head block*NW + w and walks all the split's pages, so the
 //             NW waves read the same token rows of the same pages together.
-template <int KV_INT8, int NW, bool FUSED, bool HG>
+// KV: 0 = bf16 pages, 1 = int8 codes, 2 = e4m3 codes (1 and 2 with fp32
+// scales per token and kv head).
+template <int KV, int NW, bool FUSED, bool HG>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
                                                         const int32_t *__restrict__ page_table,
                                                         const int32_t *__restrict__ seq_lens) {
     constexpr int D = kHeadDim, P = kPageSize;
+    constexpr bool QUANT = KV != 0;        // 1-byte codes + scales, f16 arithmetic
+    constexpr bool I8 = KV == 1;
     const int lane = threadIdx.x & 63;
     // wave index is uniform per wave; say so, so that page ids, buffer
     // descriptors and loop bounds live in scalar registers
@@ -390,7 +426,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
     // significant bits); qinv[h] undoes the scaling on the scores.
     f16x8_t qa16[4];
     float qinv[4] = {1.f, 1.f, 1.f, 1.f};
-    if constexpr (KV_INT8 != 0) {
+    if constexpr (QUANT) {
         float amax = 0.f;
 #pragma unroll
         for (int c = 0; c < 4; ++c)
@@ -434,16 +470,16 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
     // after the page's last valid token row: rows past the context read as 0
     // without touching memory (so V needs no masking), and a zero range turns
     // the prefetch past the split's last page into a no-op.
-    constexpr int ES = KV_INT8 ? 1 : 2;                   // bytes per element
+    constexpr int ES = QUANT ? 1 : 2;                     // bytes per element
     const int row_bytes = row_stride * ES;
     const int k_lane = (n * row_stride + 8 * g) * ES;     // byte offsets inside a page
     const int v_lane = (vr * row_stride + 8 * vc) * ES;
     const int s_lane = n * p.hkv * 4;
     uint4 kr[4][4];          // bf16 K
     uint4 vr16[16];          // bf16 V
-    uint2 kr8[4][4];         // int8 K codes
-    uint2 vr8[16];           // int8 V codes
-    float ksc[4], vsc[4];    // int8 scales of token 16t + n
+    uint2 kr8[4][4];         // int8 / e4m3 K codes
+    uint2 vr8[16];           // int8 / e4m3 V codes
+    float ksc[4], vsc[4];    // scales of token 16t + n (e4m3 V: times 256)
     auto rsrc = [&](const void *base, int64_t page, int64_t elem_per_page, int64_t elem_off,
                     int esize, int nbytes) {
         const char *ptr = static_cast<const char *>(base) + (page * elem_per_page + elem_off) * esize;
@@ -458,12 +494,12 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const int off = k_lane + 32 * c * ES;
-                if constexpr (KV_INT8 == 0)
+                if constexpr (!QUANT)
                     kr[t][c] = buf_ld16(r, off, 16 * t * row_bytes);
                 else
                     kr8[t][c] = buf_ld8(r, off, 16 * t * row_bytes);
             }
-        if constexpr (KV_INT8 != 0) {
+        if constexpr (QUANT) {
             const auto rs = rsrc(p.k_scales, page, (int64_t)P * p.hkv, kvh, 4,
                                  valid_rows * p.hkv * 4);
 #pragma unroll
@@ -478,17 +514,17 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
                             valid_rows * row_bytes);
 #pragma unroll
         for (int i = 8 * half; i < 8 * half + 8; ++i) {
-            if constexpr (KV_INT8 == 0)
+            if constexpr (!QUANT)
                 vr16[i] = buf_ld16(r, v_lane, 4 * i * row_bytes);
             else
                 vr8[i] = buf_ld8(r, v_lane, 4 * i * row_bytes);
         }
-        if (KV_INT8 != 0 && half == 1) {
+        if (QUANT && half == 1) {
             const auto rs = rsrc(p.v_scales, page, (int64_t)P * p.hkv, kvh, 4,
                                  valid_rows * p.hkv * 4);
 #pragma unroll
             for (int t = 0; t < 4; ++t)
-                vsc[t] = buf_ldf(rs, s_lane, 16 * t * p.hkv * 4);
+                vsc[t] = buf_ldf(rs, s_lane, 16 * t * p.hkv * 4) * (I8 ? 1.f : kF8ValueScale);
         }
     };
 
@@ -523,7 +559,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
 
         // ---- S = Q K^T: lane (n, g) gets s[head h][token 16t + n] in sacc[t][h]
         f32x4_t sacc[4];
-        if constexpr (KV_INT8 == 0) {
+        if constexpr (!QUANT) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 sacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -538,8 +574,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
                 sacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
-                    sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa16[c], i8x8_to_f16(kr8[t][c]),
-                                                                     sacc[t], 0, 0, 0);
+                    sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        qa16[c], I8 ? i8x8_to_f16(kr8[t][c]) : e4m3x8_to_f16(kr8[t][c]),
+                        sacc[t], 0, 0, 0);
             }
         }
         float s[4][4];
@@ -548,7 +585,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
             const bool ok = (16 * t + n) < valid;
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
-                const float f = KV_INT8 ? p.qk_scale_log2 * ksc[t] * qinv[h] : p.qk_scale_log2;
+                const float f = QUANT ? p.qk_scale_log2 * ksc[t] * qinv[h] : p.qk_scale_log2;
                 s[t][h] = ok ? sacc[t][h] * f : kNegInf;
             }
         }
@@ -585,12 +622,12 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
                 float a0 = pv[2 * qq][0], a1 = pv[2 * qq][1], a2 = pv[2 * qq][2], a3 = pv[2 * qq][3];
                 float b0 = pv[2 * qq + 1][0], b1 = pv[2 * qq + 1][1], b2 = pv[2 * qq + 1][2],
                       b3 = pv[2 * qq + 1][3];
-                if constexpr (KV_INT8 != 0) {
+                if constexpr (QUANT) {
                     a0 *= vsc[2 * qq]; a1 *= vsc[2 * qq]; a2 *= vsc[2 * qq]; a3 *= vsc[2 * qq];
                     b0 *= vsc[2 * qq + 1]; b1 *= vsc[2 * qq + 1]; b2 *= vsc[2 * qq + 1];
                     b3 *= vsc[2 * qq + 1];
                 }
-                if constexpr (KV_INT8 != 0) {
+                if constexpr (QUANT) {
                     // value scale folded in; f16 keeps 11 significant bits
                     w.x = pack_f16x2(a0, b0);
                     w.y = pack_f16x2(a1, b1);
@@ -614,9 +651,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
         for (int h = 0; h < 4; ++h) {
 #pragma unroll
             for (int d = 0; d < 8; ++d) acc[h][d] *= alpha[h];
-            if constexpr (KV_INT8 != 0) psum[h] *= alpha[h];
+            if constexpr (I8) psum[h] *= alpha[h];
         }
-        if constexpr (KV_INT8 == 0) {
+        if constexpr (!QUANT) {
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 if (u == 4) {   // tokens 0..31 done: request the next page's first half
@@ -642,8 +679,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
                 }
             }
         } else {
-            // int8 codes are finite and masked tokens have probability 0, so
-            // no masking is needed; psum tracks sum(p') for the 1152 bias.
+            // codes are finite (rows past the context read as 0) and masked
+            // tokens have probability 0, so no masking is needed; for int8,
+            // psum tracks sum(p') for the 1152 bias.
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 if (u == 4) {
@@ -655,17 +693,24 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
                 const int ia = u < 4 ? u : u + 4;
                 const int ib = ia + 4;
                 const uint32_t ph[4] = {pk.x, pk.y, pk.z, pk.w};
-#pragma unroll
-                for (int h = 0; h < 4; ++h) psum[h] = dot2_f16(ph[h], kF16One2, psum[h]);
                 uint32_t vp[8];
-                vp[0] = i8_pair_f16<0>(vr8[ib].x, vr8[ia].x);
-                vp[1] = i8_pair_f16<1>(vr8[ib].x, vr8[ia].x);
-                vp[2] = i8_pair_f16<2>(vr8[ib].x, vr8[ia].x);
-                vp[3] = i8_pair_f16<3>(vr8[ib].x, vr8[ia].x);
-                vp[4] = i8_pair_f16<0>(vr8[ib].y, vr8[ia].y);
-                vp[5] = i8_pair_f16<1>(vr8[ib].y, vr8[ia].y);
-                vp[6] = i8_pair_f16<2>(vr8[ib].y, vr8[ia].y);
-                vp[7] = i8_pair_f16<3>(vr8[ib].y, vr8[ia].y);
+                if constexpr (I8) {
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) psum[h] = dot2_f16(ph[h], kF16One2, psum[h]);
+                    vp[0] = i8_pair_f16<0>(vr8[ib].x, vr8[ia].x);
+                    vp[1] = i8_pair_f16<1>(vr8[ib].x, vr8[ia].x);
+                    vp[2] = i8_pair_f16<2>(vr8[ib].x, vr8[ia].x);
+                    vp[3] = i8_pair_f16<3>(vr8[ib].x, vr8[ia].x);
+                    vp[4] = i8_pair_f16<0>(vr8[ib].y, vr8[ia].y);
+                    vp[5] = i8_pair_f16<1>(vr8[ib].y, vr8[ia].y);
+                    vp[6] = i8_pair_f16<2>(vr8[ib].y, vr8[ia].y);
+                    vp[7] = i8_pair_f16<3>(vr8[ib].y, vr8[ia].y);
+                } else {
+                    e4m3_pairs_f16<0>(vr8[ib].x, vr8[ia].x, vp[0], vp[1]);
+                    e4m3_pairs_f16<2>(vr8[ib].x, vr8[ia].x, vp[2], vp[3]);
+                    e4m3_pairs_f16<0>(vr8[ib].y, vr8[ia].y, vp[4], vp[5]);
+                    e4m3_pairs_f16<2>(vr8[ib].y, vr8[ia].y, vp[6], vp[7]);
+                }
 #pragma unroll
                 for (int d = 0; d < 8; ++d)
 #pragma unroll
@@ -677,7 +722,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
         load_v_half(page_next, valid_next, 1);
         __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (KV_INT8 != 0) {
+    if constexpr (I8) {
         // remove the 1152 bias carried by every f16 value code
 #pragma unroll
         for (int h = 0; h < 4; ++h)
@@ -824,7 +869,7 @@ __global__ __launch_bounds__(128) void split_merge_kernel(const float *__restric
                                                           float *__restrict__ lse) {
     const int64_t row = blockIdx.x;
     for (int d = threadIdx.x; d < head_dim; d += blockDim.x)
-        merge_element(acc, mx, sum, splits, head_dim, row, d, out, lse);
+        merge_element<kMergeChunkSeparate>(acc, mx, sum, splits, head_dim, row, d, out, lse);
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t *__restrict__ ptr, size_t words) {
@@ -857,16 +902,22 @@ constexpr int kNwPageSplit = 4;
 // One wave per (request, kv head, split) fills 2 waves per SIMD from here on.
 constexpr int64_t kHeadGroupedMinWaves = 2048;
 
-hipError_t launch_decode(const DecodeParams &p, int kv_int8, DecodeMode mode, bool fused,
+template <int KV>
+hipError_t launch_kv(const DecodeParams &p, DecodeMode mode, bool fused, hipStream_t stream) {
+    if (mode == DecodeMode::kHeadGrouped)
+        return launch_nw<KV, kNwHeadGrouped, true>(p, fused, stream);
+    return launch_nw<KV, kNwPageSplit, false>(p, fused, stream);
+}
+
+hipError_t launch_decode(const DecodeParams &p, int kv_type, DecodeMode mode, bool fused,
                          hipStream_t stream) {
-    const bool hg = mode == DecodeMode::kHeadGrouped;
     hipError_t err;
-    if (hg)
-        err = kv_int8 ? launch_nw<1, kNwHeadGrouped, true>(p, fused, stream)
-                      : launch_nw<0, kNwHeadGrouped, true>(p, fused, stream);
+    if (kv_type == kKvInt8)
+        err = launch_kv<1>(p, mode, fused, stream);
+    else if (kv_type == kKvFp8)
+        err = launch_kv<2>(p, mode, fused, stream);
     else
-        err = kv_int8 ? launch_nw<1, kNwPageSplit, false>(p, fused, stream)
-                      : launch_nw<0, kNwPageSplit, false>(p, fused, stream);
+        err = launch_kv<0>(p, mode, fused, stream);
     if (err != hipSuccess || fused) return err;
     return launch_split_merge(p.part_acc, p.part_max, p.part_sum, p.batch * p.hq, kHeadDim,
                               p.splits, p.out, p.lse, stream);

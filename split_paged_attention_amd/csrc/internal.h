@@ -81,9 +81,10 @@ enum class DecodeMode { kPageSplit, kHeadGrouped };
 DecodeMode default_mode(int batch, int hkv, int splits);
 bool mode_supported(DecodeMode mode, int hkv);
 
-// kv_int8: 0 = bf16 pages, 1 = int8 pages.  fused: merge in the last split
-// workgroup; otherwise a separate merge launch follows the producer.
-hipError_t launch_decode(const DecodeParams &p, int kv_int8, DecodeMode mode, bool fused,
+// kv_type: kKvBf16, kKvInt8 or kKvFp8 pages.  fused: merge in the last
+// split workgroup; otherwise a separate merge launch follows the producer.
+constexpr int kKvBf16 = 0, kKvInt8 = 1, kKvFp8 = 2;
+hipError_t launch_decode(const DecodeParams &p, int kv_type, DecodeMode mode, bool fused,
                          hipStream_t stream);
 
 hipError_t launch_split_merge(const float *acc, const float *mx, const float *sum,

@@ -77,6 +77,9 @@ def _attn(**kw):
     (dict(out=None), spa.SPA_ERR_INVALID_ARGUMENT),
     (dict(ws=None), spa.SPA_ERR_INVALID_ARGUMENT),
     (dict(kvd=1), spa.SPA_ERR_INVALID_ARGUMENT),            # int8 without scales
+    (dict(kvd=2), spa.SPA_ERR_INVALID_ARGUMENT),            # fp8 without scales
+    (dict(kvd=2, ks=FAKE, vs=FAKE, B=0), spa.SPA_OK),
+    (dict(kvd=3), spa.SPA_ERR_INVALID_ARGUMENT),
     (dict(q=FAKE_ODD), spa.SPA_ERR_INVALID_ARGUMENT),
     (dict(k=FAKE_ODD), spa.SPA_ERR_INVALID_ARGUMENT),
     (dict(D=64), spa.SPA_ERR_UNSUPPORTED),

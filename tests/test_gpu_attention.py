@@ -61,10 +61,47 @@ def test_config4_headline_parity():
         assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
 
 
+def test_config6_fp8_headline_parity():
+    """Batch 32 / context 8K with e4m3 KV: library defaults, then both
+    producers with both merges (bit-identical per producer), every output."""
+    c = config_case(6)
+    print(f"[case] attention config 6 ({c.name}) full parity", flush=True)
+    d = DevCase(c)
+    pt, _, _ = d.page_table()
+    out, lse = d.attention(page_table=pt)
+    o_ref, l_ref = oracle.case_attention(c)
+    compare_attention(out, lse, o_ref, l_ref, label=c.name)
+    for producer in PRODUCERS:
+        o1, l1 = d.attention(page_table=pt, producer=producer, merge="fused")
+        compare_attention(o1, l1, o_ref, l_ref, label=f"{c.name} {producer} fused")
+        o2, l2 = d.attention(page_table=pt, producer=producer, merge="separate")
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("producer", PRODUCERS)
+def test_fp8_every_code_in_keys_and_values(producer):
+    """One-token contexts whose K and V rows hold every finite e4m3 code (the
+    hardware conversion of each code meets the oracle's decoding), plus a
+    longer context over the same codes."""
+    c = small_case([1, 1, 300], kv="fp8", S=4)
+    codes = (np.arange(3 * 8 * 128) % 256).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0
+    codes = codes.reshape(3, 8, 128)
+    for b in range(2):
+        page = c.page_list[b, 0]
+        c.k_pages[page, 0] = codes[b]
+        c.v_pages[page, 0] = np.roll(codes[b], 5, axis=1)
+    print(f"[case] fp8 every code {producer}", flush=True)
+    out, lse = DevCase(c).attention(producer=producer)
+    o_ref, l_ref = oracle.case_attention(c)
+    compare_attention(out, lse, o_ref, l_ref, label=f"fp8 codes {producer}")
+
+
 # ---------------------------------------------------------------- ragged / edges
 
 @pytest.mark.parametrize("producer", PRODUCERS)
-@pytest.mark.parametrize("kv", ["bf16", "int8"])
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8"])
 @pytest.mark.parametrize("lens,S", [
     ([1, 63, 64, 65], 1),
     ([127, 128, 129, 1000], 3),
@@ -91,7 +128,7 @@ def test_zero_length_request():
     assert torch.all(torch.isneginf(lse[0])) and torch.all(torch.isneginf(lse[2]))
 
 
-@pytest.mark.parametrize("kv", ["bf16", "int8"])
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8"])
 def test_single_token_returns_value_row_bit_exact(kv):
     c = small_case([1, 1, 1], kv=kv, S=4)
     print(f"[case] one-token context {kv}", flush=True)
@@ -120,7 +157,7 @@ def test_large_logits():
 # ---------------------------------------------------------------- structure
 
 @pytest.mark.parametrize("producer", PRODUCERS)
-@pytest.mark.parametrize("kv", ["bf16", "int8"])
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8"])
 def test_fused_equals_two_launch_bit_exact(kv, producer):
     c = small_case([3000, 64, 1, 777], kv=kv, S=16)
     print(f"[case] fused vs separate merge {kv} {producer}", flush=True)
