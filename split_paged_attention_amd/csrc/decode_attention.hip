@@ -329,6 +329,11 @@ __device__ __forceinline__ void merge_vec_sys(__amdgpu_buffer_rsrc_t racc,
     merge_finish<VEC>(M, l, o, out, lse, write_lse);
 }
 
+// Value of v in lane src (a cross-lane permute, no memory access).
+__device__ __forceinline__ float lane_value(float v, int src) {
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v)));
+}
+
 // Store that is written through to memory (system scope): visible to every
 // XCD once the issuing wave's store counter drains, with no L2 writeback.
 __device__ __forceinline__ void st_sys(float *p, float v) {
@@ -345,7 +350,8 @@ __device__ __forceinline__ void st_sys(float *p, float v) {
 // KV: 0 = bf16 pages, 1 = int8 codes, 2 = e4m3 codes (1 and 2 with fp32
 // scales per token and kv head).
 template <int KV, int NW, bool FUSED, bool HG>
-__global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_kernel(DecodeParams p,
                                                         const int32_t *__restrict__ page_table,
                                                         const int32_t *__restrict__ seq_lens) {
     constexpr int D = kHeadDim, P = kPageSize;
@@ -358,9 +364,16 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
     const int n = lane & 15, g = lane >> 4;     // QK layout: token n of a 16-block, k-chunk g
     const int vr = lane >> 4, vc = lane & 15;   // PV layout: token phase r, dims 8c..8c+7
 
-    // blockIdx -> (group = b * Hkv + kvh, split j).  The S split workgroups of a
-    // group get ids congruent mod 8 so they land on one XCD (dispatch is round
-    // robin over the 8 XCDs) and share its L2 for the merge.
+    // blockIdx -> (group = request rank * groups per request + kv block,
+    // split j).  Dispatch is round robin over the 8 XCDs, so ids congruent
+    // mod 8 share an XCD and its L2.  For 1-byte codes with a batch that is
+    // a multiple of 8, XCD x takes every kv block and split of request ranks
+    // x, x + 8, ...: the XCD then reads whole token rows of its requests'
+    // pages (and their interleaved per-head scales, fetched once instead of
+    // once per kv block) through one L2, and the longest-first ranks are
+    // dealt evenly over the XCDs (measured: 7% faster for int8 and fp8 at
+    // batch 32 / 8K, 2% slower for bf16).  Otherwise the S splits of a group
+    // share an XCD.
     const int S = p.splits;
     const int kv_per_grp = HG ? NW : 1;             // kv heads per workgroup
     const int grp_per_b = p.hkv / kv_per_grp;
@@ -368,8 +381,12 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
     int grp, j;
     {
         const int bid = blockIdx.x;
-        if ((ngroups & 7) == 0) {
-            const int xcd = bid & 7, slot = bid >> 3;
+        const int xcd = bid & 7, slot = bid >> 3;
+        if (QUANT && (p.batch & 7) == 0) {
+            j = slot % S;
+            const int rest = slot / S;
+            grp = ((rest / grp_per_b) * 8 + xcd) * grp_per_b + rest % grp_per_b;
+        } else if ((ngroups & 7) == 0) {
             grp = (slot / S) * 8 + xcd;
             j = slot % S;
         } else {
@@ -411,14 +428,20 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
     const int pg1 = min(pg0 + pps, pages);
     const int row_stride = p.hkv * D;           // elements between consecutive token rows
 
-    // A operand: row i of the MFMA is query head (kvh*4 + (i & 3)); k-chunk g of
-    // MFMA c covers dims 32c + 8g .. +8.
+    // A operand: row i of the MFMA is query head (kvh*4 + (i & 3)).  The
+    // contraction may visit the 128 dims in any order as long as A and B
+    // agree: bf16 k-chunk g of MFMA c covers dims 32c + 8g .. +8 (a 16-byte
+    // key load per chunk); 1-byte codes use dims 64(c/2) + 16g + 8(c%2) .. +8,
+    // so that one 16-byte key load per lane feeds two MFMAs.
     bf16x8_t qa[4];
     {
         const uint16_t *qp = reinterpret_cast<const uint16_t *>(p.q) +
-                             ((int64_t)b * p.hq + kvh * kGroup + (n & 3)) * D + 8 * g;
+                             ((int64_t)b * p.hq + kvh * kGroup + (n & 3)) * D;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) qa[c] = *reinterpret_cast<const bf16x8_t *>(qp + 32 * c);
+        for (int c = 0; c < 4; ++c) {
+            const int d0 = QUANT ? 64 * (c >> 1) + 16 * g + 8 * (c & 1) : 32 * c + 8 * g;
+            qa[c] = *reinterpret_cast<const bf16x8_t *>(qp + d0);
+        }
     }
     // int8 KV: the scores use the f16 matrix cores with exact f16 key codes,
     // so the query goes to f16 too, each head scaled by a power of two that
@@ -444,6 +467,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
         for (int h = 0; h < 4; ++h)
             qinv[h] = __builtin_ldexpf(1.f, -__builtin_amdgcn_readlane(sh, h));
     }
+    float qscale[4];   // score factor per head, times the key scale of a token
+#pragma unroll
+    for (int h = 0; h < 4; ++h) qscale[h] = p.qk_scale_log2 * qinv[h];
 
     float m[4], lpart[4], acc[4][8], psum[4];
 #pragma unroll
@@ -472,14 +498,19 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
     // the prefetch past the split's last page into a no-op.
     constexpr int ES = QUANT ? 1 : 2;                     // bytes per element
     const int row_bytes = row_stride * ES;
-    const int k_lane = (n * row_stride + 8 * g) * ES;     // byte offsets inside a page
+    const int k_lane = (n * row_stride + (QUANT ? 16 : 8) * g) * ES;   // byte offsets in a page
     const int v_lane = (vr * row_stride + 8 * vc) * ES;
-    const int s_lane = n * p.hkv * 4;
+    // A loop iteration handles one page of this wave's page sequence (two
+    // pages per iteration for 1-byte codes measured slower: 256 registers).
     uint4 kr[4][4];          // bf16 K
     uint4 vr16[16];          // bf16 V
-    uint2 kr8[4][4];         // int8 / e4m3 K codes
+    uint4 kr8[4][2];         // int8 / e4m3 K codes: [t][c/2], 16 per lane
     uint2 vr8[16];           // int8 / e4m3 V codes
-    float ksc[4], vsc[4];    // scales of token 16t + n (e4m3 V: times 256)
+    // Scales of a page: lane l holds token l's (one load per page and
+    // tensor); lane (n, g) fetches token 16t + n's with a lane permute when
+    // it needs it.  e4m3 value scales are stored times 256.
+    float ksc_tok, vsc_tok;
+    const int s_lane64 = lane * p.hkv * 4;
     auto rsrc = [&](const void *base, int64_t page, int64_t elem_per_page, int64_t elem_off,
                     int esize, int nbytes) {
         const char *ptr = static_cast<const char *>(base) + (page * elem_per_page + elem_off) * esize;
@@ -490,21 +521,21 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
         const auto r = rsrc(p.k_pages, page, (int64_t)P * row_stride, (int64_t)kvh * D, ES,
                             valid_rows * row_bytes);
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < 4; ++t) {
+            if constexpr (!QUANT) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int off = k_lane + 32 * c * ES;
-                if constexpr (!QUANT)
-                    kr[t][c] = buf_ld16(r, off, 16 * t * row_bytes);
-                else
-                    kr8[t][c] = buf_ld8(r, off, 16 * t * row_bytes);
+                for (int c = 0; c < 4; ++c)
+                    kr[t][c] = buf_ld16(r, k_lane + 64 * c, 16 * t * row_bytes);
+            } else {
+#pragma unroll
+                for (int c2 = 0; c2 < 2; ++c2)
+                    kr8[t][c2] = buf_ld16(r, k_lane + 64 * c2, 16 * t * row_bytes);
             }
+        }
         if constexpr (QUANT) {
             const auto rs = rsrc(p.k_scales, page, (int64_t)P * p.hkv, kvh, 4,
                                  valid_rows * p.hkv * 4);
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-                ksc[t] = buf_ldf(rs, s_lane, 16 * t * p.hkv * 4);
+            ksc_tok = buf_ldf(rs, s_lane64, 0);
         }
     };
     // V in two halves (tokens 0..31, 32..63): P.V consumes the first half's
@@ -522,22 +553,23 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
         if (QUANT && half == 1) {
             const auto rs = rsrc(p.v_scales, page, (int64_t)P * p.hkv, kvh, 4,
                                  valid_rows * p.hkv * 4);
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-                vsc[t] = buf_ldf(rs, s_lane, 16 * t * p.hkv * 4) * (I8 ? 1.f : kF8ValueScale);
+            vsc_tok = buf_ldf(rs, s_lane64, 0) * (I8 ? 1.f : kF8ValueScale);
         }
     };
 
     // Software pipeline over this wave's pages: the next page's K loads are
     // issued as soon as QK^T has consumed the K registers, each half of its V
-    // loads as soon as P.V has consumed that half of the V registers, so loads
-    // stay in flight while the current page is computed.
+    // loads as soon as P.V has consumed that half of the V registers, so
+    // loads stay in flight while the current page is computed.
     constexpr int PSTEP = HG ? 1 : NW;              // page stride of one wave
     int pg = HG ? pg0 : pg0 + wave;
     // Rows of logical page i that are loaded: a page id outside the pool is
     // loaded with a zero range (reads 0, touches no memory) instead of
-    // faulting, so a bad page table gives wrong numbers, never a fault.
+    // faulting, so a bad page table gives wrong numbers, never a fault; a
+    // page at or past the split's end loads nothing.
     auto page_rows = [&](int i, int64_t &page) {
+        page = 0;
+        if (i >= pg1) return 0;
         const int32_t id = pt_row[i];
         const bool ok = (uint32_t)id < (uint32_t)p.num_pages;
         page = ok ? id : 0;
@@ -551,10 +583,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
         load_v_half(page, rows, 1);
     }
     for (; pg < pg1; pg += PSTEP) {
-        const int nxt = pg + PSTEP;
-        const bool has_next = nxt < pg1;
-        int64_t page_next = 0;
-        const int valid_next = has_next ? page_rows(nxt, page_next) : 0;
+        int64_t page_next;
+        const int valid_next = page_rows(pg + PSTEP, page_next);
         const int valid = min(P, L - pg * P);       // tokens of this page that count
 
         // ---- S = Q K^T: lane (n, g) gets s[head h][token 16t + n] in sacc[t][h]
@@ -573,19 +603,22 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
             for (int t = 0; t < 4; ++t) {
                 sacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int c = 0; c < 4; ++c)
+                for (int c = 0; c < 4; ++c) {
+                    const uint4 w = kr8[t][c >> 1];
+                    const uint2 h = (c & 1) ? make_uint2(w.z, w.w) : make_uint2(w.x, w.y);
                     sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                        qa16[c], I8 ? i8x8_to_f16(kr8[t][c]) : e4m3x8_to_f16(kr8[t][c]),
-                        sacc[t], 0, 0, 0);
+                        qa16[c], I8 ? i8x8_to_f16(h) : e4m3x8_to_f16(h), sacc[t], 0, 0, 0);
+                }
             }
         }
         float s[4][4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const bool ok = (16 * t + n) < valid;
+            const float kt = QUANT ? lane_value(ksc_tok, 16 * t + n) : 1.f;
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
-                const float f = QUANT ? p.qk_scale_log2 * ksc[t] * qinv[h] : p.qk_scale_log2;
+                const float f = QUANT ? qscale[h] * kt : p.qk_scale_log2;
                 s[t][h] = ok ? sacc[t][h] * f : kNegInf;
             }
         }
@@ -613,8 +646,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
         }
 
         // ---- probabilities for P.V: pair (token 32q + n, token 32q + 16 + n),
-        // packed bf16; stored by row 0 of the wave as pbuf[pair u][phase r][h]
-        // with u = 4q + n/4, r = n % 4.
+        // stored by row 0 of the wave as pbuf[pair u][phase r][h]
+        // with u = 4q + n/4, r = n % 4 (bf16, or f16 with the value scale
+        // folded in for 1-byte codes).
         {   // every row g holds the same values, so all lanes may store
 #pragma unroll
             for (int qq = 0; qq < 2; ++qq) {
@@ -623,12 +657,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
                 float b0 = pv[2 * qq + 1][0], b1 = pv[2 * qq + 1][1], b2 = pv[2 * qq + 1][2],
                       b3 = pv[2 * qq + 1][3];
                 if constexpr (QUANT) {
-                    a0 *= vsc[2 * qq]; a1 *= vsc[2 * qq]; a2 *= vsc[2 * qq]; a3 *= vsc[2 * qq];
-                    b0 *= vsc[2 * qq + 1]; b1 *= vsc[2 * qq + 1]; b2 *= vsc[2 * qq + 1];
-                    b3 *= vsc[2 * qq + 1];
-                }
-                if constexpr (QUANT) {
-                    // value scale folded in; f16 keeps 11 significant bits
+                    const float va = lane_value(vsc_tok, 32 * qq + n);
+                    const float vb = lane_value(vsc_tok, 32 * qq + 16 + n);
+                    a0 *= va; a1 *= va; a2 *= va; a3 *= va;
+                    b0 *= vb; b1 *= vb; b2 *= vb; b3 *= vb;
+                    // f16 keeps 11 significant bits
                     w.x = pack_f16x2(a0, b0);
                     w.y = pack_f16x2(a1, b1);
                     w.z = pack_f16x2(a2, b2);
@@ -646,25 +679,25 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
         // from moving the reads above the writes.
         __asm__ volatile("" ::: "memory");
 
-        // ---- P.V
+        // ---- P.V.  Pair u: tokens 4*ia + r and 4*ia + r + 16, ia = u < 4 ? u : u + 4.
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
 #pragma unroll
             for (int d = 0; d < 8; ++d) acc[h][d] *= alpha[h];
             if constexpr (I8) psum[h] *= alpha[h];
         }
-        if constexpr (!QUANT) {
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                if (u == 4) {   // tokens 0..31 done: request the next page's first half
-                    __builtin_amdgcn_sched_barrier(0);
-                    load_v_half(page_next, valid_next, 0);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                const uint4 pk = *reinterpret_cast<const uint4 *>(&pbuf[wave][u][vr][0]);
-                const int ia = u < 4 ? u : u + 4;       // token 4*ia + r
-                const int ib = ia + 4;                  // token 4*ia + r + 16
-                const uint32_t ph[4] = {pk.x, pk.y, pk.z, pk.w};
+        for (int u = 0; u < 8; ++u) {
+            if (u == 4) {   // tokens 0..31 done: request the next page's first half
+                __builtin_amdgcn_sched_barrier(0);
+                load_v_half(page_next, valid_next, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            const uint4 pk = *reinterpret_cast<const uint4 *>(&pbuf[wave][u][vr][0]);
+            const int ia = u < 4 ? u : u + 4;       // token 4*ia + r
+            const int ib = ia + 4;                  // token 4*ia + r + 16
+            const uint32_t ph[4] = {pk.x, pk.y, pk.z, pk.w};
+            if constexpr (!QUANT) {
                 const uint32_t wa[4] = {vr16[ia].x, vr16[ia].y, vr16[ia].z, vr16[ia].w};
                 const uint32_t wb[4] = {vr16[ib].x, vr16[ib].y, vr16[ib].z, vr16[ib].w};
 #pragma unroll
@@ -677,22 +710,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p,
                         acc[h][2 * e + 1] = dot2(ph[h], hi, acc[h][2 * e + 1]);
                     }
                 }
-            }
-        } else {
-            // codes are finite (rows past the context read as 0) and masked
-            // tokens have probability 0, so no masking is needed; for int8,
-            // psum tracks sum(p') for the 1152 bias.
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                if (u == 4) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    load_v_half(page_next, valid_next, 0);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                const uint4 pk = *reinterpret_cast<const uint4 *>(&pbuf[wave][u][vr][0]);
-                const int ia = u < 4 ? u : u + 4;
-                const int ib = ia + 4;
-                const uint32_t ph[4] = {pk.x, pk.y, pk.z, pk.w};
+            } else {
+                // codes are finite (rows past the context read as 0) and
+                // masked tokens have probability 0, so no masking is needed;
+                // for int8, psum tracks sum(p') for the 1152 bias.
                 uint32_t vp[8];
                 if constexpr (I8) {
 #pragma unroll
