@@ -51,6 +51,10 @@ def _load():
     lib.oracle_build_page_table.argtypes = [_P, _I64, _P, _P, _I32, _I32, _I32, _I32, _P, _I64,
                                             _P, _P]
     lib.oracle_build_page_table.restype = _INT
+    lib.oracle_paged_verify_attention.argtypes = [_P, _P, _P, _P, _P, _INT, _P, _I64, _P, _P,
+                                                  _INT, _INT, _INT, _INT, _INT, _INT, _F32, _P,
+                                                  _P]
+    lib.oracle_paged_verify_attention.restype = _INT
     lib.oracle_build_metadata.argtypes = [_P, _I64, _P, _P, _I32, _I32, _I32, _I32, _P, _I64, _P,
                                           _P, _INT, _P, _I32, _P, _P, _P, _I64, _P, _I64, _P,
                                           _I64]
@@ -216,6 +220,29 @@ def split_merge(acc, m, l):
     rc = lib.oracle_split_merge(_ptr(acc), _ptr(m), _ptr(l), B, Hq, D, S, _ptr(out), _ptr(lse))
     if rc != 0:
         raise ValueError("oracle_split_merge: invalid arguments")
+    return out, lse
+
+
+def verify_attention(q, k_pages, v_pages, page_table, seq_lens, cu_seqlens_q, *,
+                     num_kv_heads, page_size, scale, kv_dtype="bf16", k_scales=None,
+                     v_scales=None):
+    """Multi-token query decode: q [total_q, Hq, D] bf16 bits, request b's
+    query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1, query token i of b sees
+    tokens 0 .. seq_lens[b] - n_b + i.  Returns (out [total_q, Hq, D] f64,
+    lse [total_q, Hq] f64)."""
+    lib = _load()
+    keep, args, (total_q, Hq, D) = _att_args(q, k_pages, v_pages, k_scales, v_scales, kv_dtype,
+                                             page_table, seq_lens, num_kv_heads, page_size,
+                                             scale)
+    cu = _c(cu_seqlens_q, np.int32)
+    B = int(cu.shape[0]) - 1
+    out = np.full((total_q, Hq, D), np.nan)
+    lse = np.full((total_q, Hq), np.nan)
+    # args: q k v ks vs kd pt pts sl B Hq Hkv D P scale -> insert cu, B, total_q
+    a = args[:9] + [_ptr(cu), B, total_q] + args[10:] + [_ptr(out), _ptr(lse)]
+    if lib.oracle_paged_verify_attention(*a) != 0:
+        raise ValueError("oracle_paged_verify_attention: invalid arguments")
+    del keep
     return out, lse
 
 

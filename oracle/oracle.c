@@ -182,6 +182,7 @@ typedef struct {
     const int32_t *seq_lens;
     int B, Hq, Hkv, D, P;
     double scale;
+    int64_t q_row;   /* query row to use instead of b (multi-token decode), or -1 */
 } oracle_args;
 
 /* Element d of the K (which = 0) or V (which = 1) row of token t, KV head kvh. */
@@ -206,8 +207,9 @@ static double kv_elem(const oracle_args *a, int which, int b, int t, int kvh, in
 static double score(const oracle_args *a, int b, int h, int t) {
     int kvh = h / (a->Hq / a->Hkv);
     double acc = 0.0;
+    int64_t row = a->q_row >= 0 ? a->q_row : b;
     for (int d = 0; d < a->D; ++d)
-        acc += bf16_to_double(a->q[((int64_t)b * a->Hq + h) * a->D + d]) *
+        acc += bf16_to_double(a->q[(row * a->Hq + h) * a->D + d]) *
                kv_elem(a, 0, b, t, kvh, d);
     return a->scale * acc;
 }
@@ -260,6 +262,7 @@ static void set_args(oracle_args *a, const uint16_t *q, const void *k_pages, con
     a->D = D;
     a->P = P;
     a->scale = (double)scale;
+    a->q_row = -1;
 }
 
 static int check_shape(int B, int Hq, int Hkv, int D, int P) {
@@ -291,6 +294,58 @@ int oracle_paged_attention(const uint16_t *q, const void *k_pages, const void *v
         } else {
             for (int d = 0; d < D; ++d) o[d] = 0.0;
             lse[bh] = -INFINITY;
+        }
+    }
+    return 0;
+}
+
+/* Multi-token query decode (target verify / draft extend), by definition.
+ * Request b owns query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 (n_b of
+ * them) and L_b = seq_lens[b] cached tokens, the last n_b of which are the
+ * query tokens' own: query token i (row cu_seqlens_q[b] + i) attends the
+ * tokens 0 .. L_b - n_b + i (causal within the draft).  For each row r and
+ * head h: out[r,h,:] = sum_t softmax(s)_t v_t over those tokens, lse = m +
+ * ln l; out = 0 and lse = -inf where a row sees no token.  q, out: [total_q,
+ * Hq, D]; lse [total_q, Hq]. */
+int oracle_paged_verify_attention(const uint16_t *q, const void *k_pages, const void *v_pages,
+                                  const float *k_scales, const float *v_scales, int kv_dtype,
+                                  const int32_t *page_table, int64_t page_table_stride,
+                                  const int32_t *seq_lens, const int32_t *cu_seqlens_q, int B,
+                                  int total_q, int Hq, int Hkv, int D, int P, float scale,
+                                  double *out, double *lse) {
+    if (check_shape(B, Hq, Hkv, D, P) || total_q < 0) return 1;
+    for (int b = 0; b < B; ++b)
+        if (cu_seqlens_q[b + 1] < cu_seqlens_q[b] || cu_seqlens_q[b] < 0 ||
+            cu_seqlens_q[b + 1] > total_q)
+            return 1;
+    long n = (long)total_q * Hq;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long rh = 0; rh < n; ++rh) {
+        int row = (int)(rh / Hq), h = (int)(rh % Hq);
+        double *o = out + rh * D;
+        int b = -1;
+        for (int bb = 0; bb < B; ++bb)
+            if (row >= cu_seqlens_q[bb] && row < cu_seqlens_q[bb + 1]) b = bb;
+        int visible = 0;
+        if (b >= 0) {
+            int nq = cu_seqlens_q[b + 1] - cu_seqlens_q[b];
+            int i = row - cu_seqlens_q[b];
+            visible = seq_lens[b] - nq + i + 1;
+            if (visible < 0) visible = 0;
+            if (visible > seq_lens[b]) visible = seq_lens[b];
+        }
+        oracle_args a;
+        set_args(&a, q, k_pages, v_pages, k_scales, v_scales, kv_dtype, page_table,
+                 page_table_stride, seq_lens, B, Hq, Hkv, D, P, scale);
+        a.q_row = row;
+        double m = -INFINITY, l = 0.0;
+        if (b >= 0) attend_range(&a, b, h, 0, visible, &m, &l, o);
+        if (l > 0.0) {
+            for (int d = 0; d < D; ++d) o[d] /= l;
+            lse[rh] = m + log(l);
+        } else {
+            for (int d = 0; d < D; ++d) o[d] = 0.0;
+            lse[rh] = -INFINITY;
         }
     }
     return 0;

@@ -46,3 +46,29 @@ def dense_attention(case):
             out[b, h] = w @ V[:, h // G, :]
             lse[b, h] = logsumexp(s)
     return out, lse
+
+
+def dense_verify(case, q_rows, cu_seqlens_q):
+    """Multi-token decode by dense causal attention: query token i of request
+    b (row cu[b] + i) sees the first L_b - n_b + i + 1 logical rows."""
+    T, Hq, D = q_rows.shape
+    G = case.group
+    out = np.zeros((T, Hq, D))
+    lse = np.full((T, Hq), -np.inf)
+    qf = bf16_bits_to_f32(q_rows).astype(np.float64)
+    for b in range(case.batch):
+        k, v, ks, vs = case.dense_kv(b)
+        K = dequant_rows(k, ks)
+        V = dequant_rows(v, vs)
+        L = K.shape[0]
+        r0, r1 = int(cu_seqlens_q[b]), int(cu_seqlens_q[b + 1])
+        n = r1 - r0
+        for i in range(n):
+            vis = min(max(L - n + i + 1, 0), L)
+            if vis == 0:
+                continue
+            for h in range(Hq):
+                s = float(case.scale) * (K[:vis, h // G, :] @ qf[r0 + i, h])
+                out[r0 + i, h] = softmax(s) @ V[:vis, h // G, :]
+                lse[r0 + i, h] = logsumexp(s)
+    return out, lse

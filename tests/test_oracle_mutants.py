@@ -45,6 +45,10 @@ MUTANTS = {
     "fp8_sign_dropped": ("return sign ? -v : v;", "return v;"),
     "fp8_scale_dropped": ("return e4m3_to_double(base[idx]) * (double)sc[row * a->Hkv + kvh];",
                           "return e4m3_to_double(base[idx]);"),
+    "verify_causal_off_by_one": ("visible = seq_lens[b] - nq + i + 1;",
+                                 "visible = seq_lens[b] - nq + i;"),
+    "verify_not_causal": ("visible = seq_lens[b] - nq + i + 1;", "visible = seq_lens[b];"),
+    "verify_query_row": ("a.q_row = row;", "a.q_row = cu_seqlens_q[b < 0 ? 0 : b];"),
     "swa_num_out_max": ("n_out_cache_loc < swa_out_len ? n_out_cache_loc : swa_out_len",
                         "n_out_cache_loc > swa_out_len ? swa_out_len : swa_out_len"),
 }

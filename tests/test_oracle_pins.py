@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import workloads as W
-from tests.brute import dense_attention, e4m3_codes_to_f64
+from tests.brute import dense_attention, dense_verify, e4m3_codes_to_f64
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -484,3 +484,76 @@ def test_int8_dequantisation_is_exact_product():
     np.testing.assert_allclose(out, bo, atol=1e-12)
     np.testing.assert_allclose(lse, bl, atol=1e-12)
     assert np.max(np.abs(k.astype(np.int32))) <= 127
+
+
+# ---------------------------------------------------------------- multi-token decode
+
+def _verify(c, q_rows, cu):
+    return oracle.verify_attention(q_rows, c.k_pages, c.v_pages, c.page_list, c.seq_lens, cu,
+                                   num_kv_heads=c.num_kv_heads, page_size=c.page_size,
+                                   scale=c.scale, kv_dtype=c.kv_dtype, k_scales=c.k_scales,
+                                   v_scales=c.v_scales)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8"])
+@pytest.mark.parametrize("lens,qlens", [([20, 9, 33], [4, 1, 3]), ([5, 64, 2], [2, 4, 2]),
+                                        ([17, 40], [0, 4])])
+def test_verify_matches_dense_causal_brute_force(kv, lens, qlens):
+    c = _small(lens, kv_dtype=kv)
+    q_rows, cu = W.verify_queries(c, qlens)
+    out, lse = _verify(c, q_rows, cu)
+    bo, bl = dense_verify(c, q_rows, cu)
+    np.testing.assert_allclose(out, bo, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, bl, rtol=0, atol=1e-12)
+
+
+def test_verify_query_i_is_decode_over_its_prefix():
+    """Query token i of a request with n queries is exactly the one-token
+    decode of the same query over the first L - n + i + 1 tokens."""
+    c = _small([30, 23, 11], kv_dtype="bf16")
+    qlens = [4, 3, 2]
+    q_rows, cu = W.verify_queries(c, qlens)
+    out, lse = _verify(c, q_rows, cu)
+    for b in range(c.batch):
+        n = qlens[b]
+        for i in range(n):
+            row = cu[b] + i
+            sl = c.seq_lens.copy()
+            sl[b] = c.seq_lens[b] - n + i + 1
+            q1 = np.repeat(q_rows[row][None], c.batch, axis=0)
+            o1, l1 = oracle.paged_attention(q1, c.k_pages, c.v_pages, c.page_list, sl,
+                                            num_kv_heads=c.num_kv_heads, page_size=c.page_size,
+                                            scale=c.scale)
+            assert np.array_equal(out[row], o1[b]) and np.array_equal(lse[row], l1[b])
+
+
+def test_verify_zero_query_closed_form():
+    """With q = 0 every visible score is 0: query token i of a request of
+    length L with n queries averages the first L - n + i + 1 value rows and
+    lse = ln(L - n + i + 1)."""
+    c = _small([7, 3], kv_dtype="bf16")
+    qlens = [3, 3]
+    q_rows, cu = W.verify_queries(c, qlens)
+    q_rows[:] = 0
+    out, lse = _verify(c, q_rows, cu)
+    for b in range(2):
+        _, v, _, _ = c.dense_kv(b)
+        vf = W.bf16_bits_to_f32(v).astype(np.float64)
+        for i in range(3):
+            vis = int(c.seq_lens[b]) - 3 + i + 1
+            row = cu[b] + i
+            for h in range(c.num_q_heads):
+                np.testing.assert_allclose(out[row, h], vf[:vis, h // c.group].mean(axis=0),
+                                           rtol=0, atol=1e-15)
+                assert lse[row, h] == pytest.approx(math.log(vis), abs=1e-15)
+
+
+def test_verify_single_query_equals_decode():
+    c = _small([50, 1, 17], kv_dtype="int8")
+    q_rows, cu = W.verify_queries(c, [1, 1, 1])
+    out, lse = _verify(c, q_rows, cu)
+    o1, l1 = oracle.paged_attention(q_rows, c.k_pages, c.v_pages, c.page_list, c.seq_lens,
+                                    num_kv_heads=c.num_kv_heads, page_size=c.page_size,
+                                    scale=c.scale, kv_dtype="int8", k_scales=c.k_scales,
+                                    v_scales=c.v_scales)
+    assert np.array_equal(out, o1) and np.array_equal(lse, l1)

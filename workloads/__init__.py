@@ -54,7 +54,7 @@ REQ_TO_TOKEN_STRIDE = 8192
 MAX_SEQ_PAGES = 128
 SCALE = np.float32(1.0 / np.sqrt(np.float64(HEAD_DIM)))
 
-_TAG_Q, _TAG_K, _TAG_V, _TAG_PERM, _TAG_LEN, _TAG_RPI, _TAG_FILL = range(1, 8)
+_TAG_Q, _TAG_K, _TAG_V, _TAG_PERM, _TAG_LEN, _TAG_RPI, _TAG_FILL, _TAG_QROWS = range(1, 9)
 _CHUNK_ELEMS = 1 << 22
 
 
@@ -315,6 +315,23 @@ def make_config(config_id: int) -> DecodeCase:
                      num_pages=spec["num_pages"], num_splits=spec["num_splits"],
                      kv_dtype=spec["kv_dtype"], name=spec["name"])
     return case
+
+
+def verify_queries(case: DecodeCase, q_lens, seed: Optional[int] = None):
+    """Query rows for multi-token decode (target verify / draft extend) over
+    a case's KV cache: request b gets q_lens[b] rows, laid out back to back.
+    Returns (q_rows uint16 bf16 bits [total_q, Hq, D], cu_seqlens_q int32
+    [B + 1]).  The last q_lens[b] cached tokens of request b are the draft
+    tokens these rows stand for."""
+    q_lens = np.asarray(q_lens, dtype=np.int32).reshape(-1)
+    if q_lens.shape[0] != case.batch or np.any(q_lens < 0) or np.any(q_lens > case.seq_lens):
+        raise ValueError("need 0 <= q_lens[b] <= seq_lens[b] for every request")
+    cu = np.zeros(case.batch + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(q_lens)
+    total = int(cu[-1])
+    q = normal_bf16((max(total, 1), case.num_q_heads, case.head_dim),
+                    case.seed if seed is None else seed, _TAG_QROWS)[:total]
+    return np.ascontiguousarray(q), cu
 
 
 def algorithmic_bytes(case: DecodeCase) -> int:
