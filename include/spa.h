@@ -221,6 +221,56 @@ spa_status spa_paged_decode_attention(const void *q, const void *k_pages, const 
                                       void *out, float *lse, hipStream_t stream);
 
 /*
+ * Bytes of workspace spa_paged_verify_attention needs: the per-split state
+ * of every (query row, head) (fp32 accumulator [total_q, Hq, S, D], fp32 max
+ * and sum [total_q, Hq, S]), 256-byte aligned regions.  0 for invalid sizes.
+ */
+size_t spa_verify_workspace_bytes(int32_t total_q, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t num_splits);
+
+/*
+ * Multi-token query decode (target verify / draft extend): several query
+ * tokens per request, causal among themselves, over the paged KV cache --
+ * the step whose cu_seqlens_q the sglang fused metadata update builds
+ * (module docstring; cumsum branch, Q modes 1 and 2).
+ *
+ * Request b owns query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 (n_b of
+ * them, 0 <= n_b <= max_q_len) and seq_lens[b] = L_b cached tokens, whose
+ * last n_b are the query tokens' own.  Query token i (row cu_seqlens_q[b] +
+ * i) attends tokens 0 .. L_b - n_b + i:
+ *   out[row, h, :] = softmax_t(s_t) . v_t,  lse[row, h] = ln sum_t exp(s_t),
+ *   s_t = scale * q[row, h, :] . k_t,  query head h reads kv head h / 4;
+ * a row that sees no token gets out = 0 and lse = -inf.  Split-K as in
+ * spa_paged_decode_attention (same page partition, split states merged in
+ * split order by a second launch).
+ *
+ *   q           [total_q, num_q_heads, head_dim] bf16, contiguous, 16-byte aligned
+ *   cu_seqlens_q [batch + 1] int32 (device), non-decreasing, cu[0] >= 0,
+ *               cu[batch] <= total_q (the metadata build writes it)
+ *   out         [total_q, num_q_heads, head_dim] bf16 (output, 16-byte aligned)
+ *   lse         [total_q, num_q_heads] fp32 (output, may be NULL)
+ *   other arguments as in spa_paged_decode_attention.
+ *
+ * Supported: max_q_len 1..4 (n_b above 4 computes only the first 4 rows of
+ * the request), head_dim 128, page_size 64, num_q_heads == 4 *
+ * num_kv_heads with num_kv_heads even, bf16 / int8 / fp8 KV, 1 <= num_splits
+ * <= 1024.  Rows not covered by cu_seqlens_q, and the rows of a request
+ * whose span leaves [0, total_q), are left unspecified (never written
+ * outside the output).  The workspace needs no zeroing.  batch == 0 or
+ * total_q == 0 returns SPA_OK without launching.
+ */
+spa_status spa_paged_verify_attention(const void *q, const void *k_pages, const void *v_pages,
+                                      const float *k_scales, const float *v_scales,
+                                      const int32_t *page_table, int64_t page_table_stride,
+                                      const int32_t *seq_lens, const int32_t *cu_seqlens_q,
+                                      int32_t batch, int32_t total_q, int32_t max_q_len,
+                                      int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t page_size, int32_t num_pages,
+                                      int32_t num_splits, float scale, spa_kv_dtype kv_dtype,
+                                      void *workspace, size_t workspace_bytes, void *out,
+                                      float *lse, hipStream_t stream);
+
+/*
  * Log-sum-exp merge of per-split partial softmax state (the reducer of the
  * lmdeploy split-K decode).  For each (b, h), with j = 0..num_splits-1 in order:
  *   M = max_j m_j;  w_j = exp(m_j - M), or 0 where m_j = -inf (an empty split)

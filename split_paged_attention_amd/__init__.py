@@ -90,6 +90,12 @@ def lib():
                                              _I32, _I32, _I32, _I32, _F32, _ST, _U32, _P, _SZ,
                                              _P, _P, _P]
     L.spa_paged_decode_attention.restype = _ST
+    L.spa_verify_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32, _I32]
+    L.spa_verify_workspace_bytes.restype = _SZ
+    L.spa_paged_verify_attention.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _P, _P, _I32, _I32,
+                                             _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                             ctypes.c_float, _I32, _P, _SZ, _P, _P, _P]
+    L.spa_paged_verify_attention.restype = _ST
     L.spa_split_merge.argtypes = [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P]
     L.spa_split_merge.restype = _ST
     _lib = L
@@ -330,6 +336,80 @@ def paged_decode_attention(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torc
         float(scale), kvd, flags, _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse),
         _stream(stream))
     _check(st, "spa_paged_decode_attention")
+    return out, lse
+
+
+def verify_workspace_bytes(total_q: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                           num_splits: int) -> int:
+    return int(lib().spa_verify_workspace_bytes(total_q, num_q_heads, num_kv_heads, head_dim,
+                                                num_splits))
+
+
+def paged_verify_attention(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
+                           page_table: torch.Tensor, seq_lens: torch.Tensor,
+                           cu_seqlens_q: torch.Tensor, num_splits: int, scale: float, *,
+                           max_q_len: int = 4, kv_dtype: str = "bf16",
+                           k_scales: Optional[torch.Tensor] = None,
+                           v_scales: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None,
+                           out: Optional[torch.Tensor] = None,
+                           lse: Optional[torch.Tensor] = None,
+                           stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """spa_paged_verify_attention (multi-token decode).  q [total_q, Hq, D]
+    bf16; cu_seqlens_q [batch + 1] int32 (request b's query rows
+    cu[b] .. cu[b+1]-1, at most max_q_len of them); the rest as in
+    paged_decode_attention.  Returns (out [total_q, Hq, D] bf16,
+    lse [total_q, Hq] fp32)."""
+    _need(q, "q", torch.bfloat16)
+    if q.dim() != 3:
+        raise ValueError("q must be [total_q, num_q_heads, head_dim]")
+    T, Hq, D = q.shape
+    kvd = {"bf16": SPA_KV_BF16, "int8": SPA_KV_INT8, "fp8": SPA_KV_FP8}[kv_dtype]
+    kv_t = {SPA_KV_BF16: torch.bfloat16, SPA_KV_INT8: torch.int8, SPA_KV_FP8: torch.uint8}[kvd]
+    if kvd == SPA_KV_FP8 and k_pages.dtype == torch.float8_e4m3fn:
+        kv_t = torch.float8_e4m3fn
+    _need(k_pages, "k_pages", kv_t)
+    _need(v_pages, "v_pages", kv_t)
+    if k_pages.dim() != 4 or k_pages.shape != v_pages.shape:
+        raise ValueError("k_pages/v_pages must be [num_pages, page_size, num_kv_heads, head_dim]")
+    num_pages, P, Hkv, Dk = k_pages.shape
+    if Dk != D:
+        raise ValueError("head_dim of q and the KV pages differ")
+    if kvd != SPA_KV_BF16:
+        for nm, t in (("k_scales", k_scales), ("v_scales", v_scales)):
+            if t is None:
+                raise ValueError(f"{nm} is required for {kv_dtype} KV")
+            _need(t, nm, torch.float32)
+            if tuple(t.shape) != (num_pages, P, Hkv):
+                raise ValueError(f"{nm} must be [num_pages, page_size, num_kv_heads]")
+    else:
+        k_scales = v_scales = None
+    _need(seq_lens, "seq_lens", torch.int32)
+    B = int(seq_lens.shape[0])
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32)
+    if cu_seqlens_q.shape != (B + 1,):
+        raise ValueError("cu_seqlens_q must be [batch + 1]")
+    _need(page_table, "page_table", torch.int32, contiguous=False)
+    if page_table.dim() != 2 or page_table.stride(1) != 1 or page_table.shape[0] != B:
+        raise ValueError("page_table must be [batch, stride] with unit column stride")
+    if workspace is None:
+        n = verify_workspace_bytes(T, Hq, Hkv, D, num_splits)
+        if n == 0:
+            raise ValueError("invalid sizes for a multi-token decode workspace")
+        workspace = torch.empty((n,), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", torch.uint8)
+    if out is None:
+        out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.bfloat16)
+    _need(lse, "lse", torch.float32)
+    st = lib().spa_paged_verify_attention(
+        _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(k_scales), _ptr(v_scales), _ptr(page_table),
+        page_table.stride(0), _ptr(seq_lens), _ptr(cu_seqlens_q), B, T, int(max_q_len), Hq, Hkv,
+        D, P, num_pages, int(num_splits), float(scale), kvd, _ptr(workspace), workspace.numel(),
+        _ptr(out), _ptr(lse), _stream(stream))
+    _check(st, "spa_paged_verify_attention")
     return out, lse
 
 

@@ -12,7 +12,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libspa.so")
 OBJDIR = os.path.join(HERE, "_build")
-SOURCES = ["metadata.hip", "decode_attention.hip", "api.cpp"]
+SOURCES = ["metadata.hip", "decode_attention.hip", "verify_attention.hip", "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -236,6 +236,84 @@ spa_status spa_paged_decode_attention(const void *q, const void *k_pages, const 
                            mode, fused, stream));
 }
 
+size_t spa_verify_workspace_bytes(int32_t total_q, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t num_splits) {
+    if (total_q < 0 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 || num_splits < 1)
+        return 0;
+    return spa::workspace_layout(total_q, num_q_heads, num_kv_heads, head_dim, num_splits).total;
+}
+
+spa_status spa_paged_verify_attention(const void *q, const void *k_pages, const void *v_pages,
+                                      const float *k_scales, const float *v_scales,
+                                      const int32_t *page_table, int64_t page_table_stride,
+                                      const int32_t *seq_lens, const int32_t *cu_seqlens_q,
+                                      int32_t batch, int32_t total_q, int32_t max_q_len,
+                                      int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t page_size, int32_t num_pages,
+                                      int32_t num_splits, float scale, spa_kv_dtype kv_dtype,
+                                      void *workspace, size_t workspace_bytes, void *out,
+                                      float *lse, hipStream_t stream) {
+    if (batch < 0 || total_q < 0 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 ||
+        page_size < 1 || num_pages < 1 || num_splits < 1 || page_table_stride < 1 ||
+        max_q_len < 1)
+        return SPA_ERR_INVALID_ARGUMENT;
+    if (num_q_heads % num_kv_heads != 0) return SPA_ERR_INVALID_ARGUMENT;
+    if (kv_dtype != SPA_KV_BF16 && kv_dtype != SPA_KV_INT8 && kv_dtype != SPA_KV_FP8)
+        return SPA_ERR_INVALID_ARGUMENT;
+    const bool quant = kv_dtype != SPA_KV_BF16;
+    if (!isfinite(scale)) return SPA_ERR_INVALID_ARGUMENT;
+    if (head_dim != spa::kHeadDim || page_size != spa::kPageSize ||
+        num_q_heads != spa::kGroup * num_kv_heads || num_splits > 1024 ||
+        max_q_len > spa::kMaxVerifyQueries || !spa::verify_supported(num_kv_heads))
+        return SPA_ERR_UNSUPPORTED;
+    if ((int64_t)batch * num_kv_heads * num_splits > (int64_t)INT32_MAX ||
+        (int64_t)total_q * num_q_heads > (int64_t)INT32_MAX)
+        return SPA_ERR_UNSUPPORTED;
+    if (batch == 0 || total_q == 0) return SPA_OK;
+    if (!q || !k_pages || !v_pages || !page_table || !seq_lens || !cu_seqlens_q || !out ||
+        !workspace)
+        return SPA_ERR_INVALID_ARGUMENT;
+    if (quant && (!k_scales || !v_scales)) return SPA_ERR_INVALID_ARGUMENT;
+    if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) ||
+        !aligned(workspace, 16) || !aligned(out, 16) || !aligned(page_table, 4) ||
+        !aligned(seq_lens, 4) || !aligned(cu_seqlens_q, 4) || (lse && !aligned(lse, 4)) ||
+        (quant && (!aligned(k_scales, 4) || !aligned(v_scales, 4))))
+        return SPA_ERR_INVALID_ARGUMENT;
+    const spa::WorkspaceLayout w =
+        spa::workspace_layout(total_q, num_q_heads, num_kv_heads, head_dim, num_splits);
+    if (workspace_bytes < w.total) return SPA_ERR_WORKSPACE_TOO_SMALL;
+
+    char *ws = static_cast<char *>(workspace);
+    spa::DecodeParams p{};
+    p.q = q;
+    p.k_pages = k_pages;
+    p.v_pages = v_pages;
+    p.k_scales = k_scales;
+    p.v_scales = v_scales;
+    p.page_table = page_table;
+    p.pt_stride = page_table_stride;
+    p.seq_lens = seq_lens;
+    p.batch = batch;
+    p.hq = num_q_heads;
+    p.hkv = num_kv_heads;
+    p.splits = num_splits;
+    p.num_pages = num_pages;
+    p.qk_scale_log2 = scale * 1.4426950408889634f;
+    p.part_acc = reinterpret_cast<float *>(ws + w.acc_off);
+    p.part_max = reinterpret_cast<float *>(ws + w.max_off);
+    p.part_sum = reinterpret_cast<float *>(ws + w.sum_off);
+    p.counters = nullptr;
+    p.out = static_cast<uint16_t *>(out);
+    p.lse = lse;
+    p.cu_seqlens_q = cu_seqlens_q;
+    p.total_q = total_q;
+    return hip_status(spa::launch_verify(p,
+                                         kv_dtype == SPA_KV_INT8 ? spa::kKvInt8
+                                         : kv_dtype == SPA_KV_FP8 ? spa::kKvFp8
+                                                                  : spa::kKvBf16,
+                                         stream));
+}
+
 spa_status spa_split_merge(const float *partial_acc, const float *partial_max,
                            const float *partial_sum, int32_t batch, int32_t num_q_heads,
                            int32_t head_dim, int32_t num_splits, void *out, float *lse,

@@ -42,154 +42,10 @@
 // The path is HBM-bound (about 4 flop per KV byte for bf16), so the design
 // goal is bytes in flight and a single pass over K and V.
 #include "internal.h"
+#include "kernel_common.h"
 
 namespace spa {
 namespace {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));   // store operand type
-
-// Cache-policy immediate of buffer accesses for system-scope coherence
-// (sc0 sc1): stores write through to memory, loads bypass the caches.
-constexpr int kSysCoherent = 17;
-
-// Raw buffer loads, bit-cast to plain structs at once: reading lanes of the
-// builtins' vector results through a local vector variable was seen to
-// compile to a single-dword load whose value fills every lane.
-template <int AUX = 0>
-__device__ __forceinline__ void buf_st16(uint4 v, __amdgpu_buffer_rsrc_t r, int off) {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, off, 0, AUX);
-}
-// AUX is the cache-policy immediate.
-template <int AUX = 0>
-__device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, int off, int soff) {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, AUX));
-}
-template <int AUX = 0>
-__device__ __forceinline__ uint2 buf_ld8(__amdgpu_buffer_rsrc_t r, int off, int soff) {
-    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, AUX));
-}
-template <int AUX = 0>
-__device__ __forceinline__ float buf_ldf(__amdgpu_buffer_rsrc_t r, int off, int soff) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, AUX));
-}
-
-// Word 3 of a gfx9 buffer resource for raw (untyped, unswizzled) access:
-// data format field = 32-bit, so dword loads of any width are range checked
-// against the descriptor's byte size.
-constexpr int kBufferWord3 = 0x00020000;
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kNegInf = -__builtin_inff();
-
-__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// DPP lane permutations inside a 16-lane row.
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
-}
-// Butterfly over the 16 lanes of a row: xor 1, xor 2, half-row mirror, row mirror.
-__device__ __forceinline__ float row_max16(float x) {
-    x = fmaxf(x, dpp<0xB1>(x));
-    x = fmaxf(x, dpp<0x4E>(x));
-    x = fmaxf(x, dpp<0x141>(x));
-    x = fmaxf(x, dpp<0x140>(x));
-    return x;
-}
-__device__ __forceinline__ float row_sum16(float x) {
-    x = x + dpp<0xB1>(x);
-    x = x + dpp<0x4E>(x);
-    x = x + dpp<0x141>(x);
-    x = x + dpp<0x140>(x);
-    return x;
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    bf16x2_t v;
-    v[0] = (__bf16)lo;   // round to nearest even
-    v[1] = (__bf16)hi;
-    return __builtin_bit_cast(uint32_t, v);
-}
-__device__ __forceinline__ uint16_t to_bf16_bits(float x) {
-    return __builtin_bit_cast(uint16_t, (__bf16)x);
-}
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                           __builtin_bit_cast(bf16x2_t, b), c, false);
-}
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
-    f16x2_t v;
-    v[0] = (_Float16)lo;   // round to nearest even
-    v[1] = (_Float16)hi;
-    return __builtin_bit_cast(uint32_t, v);
-}
-__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b),
-                                  c, false);
-}
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-// Eight int8 key codes -> eight exact f16 values.  The sign bits are flipped
-// (code + 128, in 1..255), each code becomes the low mantissa byte under the
-// f16 exponent of 1024 -- one byte permute with a 0x64 constant per pair --
-// reading 1152 + code, and one packed subtract of 1152 leaves the code.
-__device__ __forceinline__ f16x8_t i8x8_to_f16(uint2 w) {
-    const uint32_t x = w.x ^ 0x80808080u, y = w.y ^ 0x80808080u;
-    constexpr uint32_t kExp = 0x64646464u;
-    const uint32_t d0 = __builtin_amdgcn_perm(kExp, x, 0x04010400u);
-    const uint32_t d1 = __builtin_amdgcn_perm(kExp, x, 0x04030402u);
-    const uint32_t d2 = __builtin_amdgcn_perm(kExp, y, 0x04010400u);
-    const uint32_t d3 = __builtin_amdgcn_perm(kExp, y, 0x04030402u);
-    const f16x2_t bias = {(_Float16)1152.f, (_Float16)1152.f};
-    const f16x2_t h0 = __builtin_bit_cast(f16x2_t, d0) - bias;
-    const f16x2_t h1 = __builtin_bit_cast(f16x2_t, d1) - bias;
-    const f16x2_t h2 = __builtin_bit_cast(f16x2_t, d2) - bias;
-    const f16x2_t h3 = __builtin_bit_cast(f16x2_t, d3) - bias;
-    return f16x8_t{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
-}
-
-// Eight e4m3 key codes (dims in byte order) -> their exact f16 values; the
-// converter takes bytes 0-1 (word_sel false) or 2-3 of a word, low byte to
-// the low half.
-__device__ __forceinline__ f16x8_t e4m3x8_to_f16(uint2 w) {
-    const f16x2_t h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.x, 1.f, false);
-    const f16x2_t h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.x, 1.f, true);
-    const f16x2_t h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.f, false);
-    const f16x2_t h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.f, true);
-    return f16x8_t{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
-}
-
-// e4m3 value codes -> f16 pairs for the token pair (a, b): bytes k and k+1
-// of wa and wb (k = 0 or 2) give the pairs (a_k, b_k) and (a_k+1, b_k+1),
-// each value / 256 (exact: the converter keeps f16 subnormals).
-constexpr float kF8ValueScale = 256.f;
-template <int K>
-__device__ __forceinline__ void e4m3_pairs_f16(uint32_t wb, uint32_t wa, uint32_t &p0,
-                                               uint32_t &p1) {
-    constexpr uint32_t sel = (uint32_t)K | ((uint32_t)(4 + K) << 8) | ((uint32_t)(K + 1) << 16) |
-                             ((uint32_t)(5 + K) << 24);
-    const uint32_t w = __builtin_amdgcn_perm(wb, wa, sel);   // a_k, b_k, a_k+1, b_k+1
-    p0 = __builtin_bit_cast(uint32_t,
-                            __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.f / kF8ValueScale, false));
-    p1 = __builtin_bit_cast(uint32_t,
-                            __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.f / kF8ValueScale, true));
-}
-
-// int8 value codes -> exact f16, biased: byte k of wa (token a) and of wb
-// (token b) become the f16 pair (1152 + a_k, 1152 + b_k).  With its sign bit
-// flipped a code is x + 128 in [1, 255]; placed as the low mantissa byte under
-// the f16 exponent of 1024 it reads 1024 + x + 128.
-constexpr float kI8Bias = 1152.f;
-constexpr uint32_t kF16One2 = 0x3C003C00u;   // f16 pair (1, 1)
-template <int K>
-__device__ __forceinline__ uint32_t i8_pair_f16(uint32_t wb, uint32_t wa) {
-    constexpr uint32_t sel = (uint32_t)K | (0x0Cu << 8) | ((uint32_t)(4 + K) << 16) | (0x0Cu << 24);
-    return __builtin_amdgcn_perm(wb, wa, sel) ^ 0x64806480u;
-}
 
 // ---------------------------------------------------------------------------
 // The log-sum-exp merge.  Both merge paths (the fused tail and the separate
@@ -327,11 +183,6 @@ __device__ __forceinline__ void merge_vec_sys(__amdgpu_buffer_rsrc_t racc,
             if (j0 + u < splits) merge_step<VEC>(mv[u], lv[u], av[u], M, l, o);
     }
     merge_finish<VEC>(M, l, o, out, lse, write_lse);
-}
-
-// Value of v in lane src (a cross-lane permute, no memory access).
-__device__ __forceinline__ float lane_value(float v, int src) {
-    return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v)));
 }
 
 // Store that is written through to memory (system scope): visible to every

@@ -12,6 +12,7 @@ namespace spa {
 constexpr int kHeadDim = 128;
 constexpr int kPageSize = 64;
 constexpr int kGroup = 4;       // query heads per kv head
+constexpr int kMaxVerifyQueries = 4;   // query tokens per request, multi-token decode
 
 // Workspace layout for a decode call (byte offsets, each region 256-aligned).
 struct WorkspaceLayout {
@@ -36,8 +37,12 @@ struct DecodeParams {
     float *part_max;           // [B, Hq, S], natural-log units
     float *part_sum;           // [B, Hq, S]
     int32_t *counters;         // [B, Hkv]
-    uint16_t *out;             // [B, Hq, D] bf16
+    uint16_t *out;             // [B, Hq, D] bf16 ([total_q, Hq, D] multi-token)
     float *lse;                // [B, Hq] or nullptr
+    // multi-token decode only: query rows of request b are
+    // cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 of total_q
+    const int32_t *cu_seqlens_q;
+    int32_t total_q;
 };
 
 // cu_seqlens_q handling of the metadata build.
@@ -86,6 +91,11 @@ bool mode_supported(DecodeMode mode, int hkv);
 constexpr int kKvBf16 = 0, kKvInt8 = 1, kKvFp8 = 2;
 hipError_t launch_decode(const DecodeParams &p, int kv_type, DecodeMode mode, bool fused,
                          hipStream_t stream);
+
+// Multi-token decode producer (2 kv heads per workgroup) + split merge over
+// total_q * hq rows; partial state rows are query rows.
+hipError_t launch_verify(const DecodeParams &p, int kv_type, hipStream_t stream);
+bool verify_supported(int hkv);
 
 hipError_t launch_split_merge(const float *acc, const float *mx, const float *sum,
                               int32_t rows, int32_t head_dim, int32_t splits, uint16_t *out,

@@ -1,0 +1,419 @@
+// Multi-token query decode (target verify / draft extend) over the paged KV
+// cache, split-K like the one-token decode.
+//
+// Request b owns query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 (n_b <= 4
+// of them); the last n_b of its L_b cached tokens are those queries' own, so
+// query token i sees tokens 0 .. L_b - n_b + i (sglang's fused metadata
+// update prepares cu_seqlens_q for exactly these steps: module docstring and
+// the cumsum branch's Q modes).
+//
+// A workgroup is one (request, block of 2 kv heads, split); wave w is kv head
+// 2*block + w and walks the split's pages.  Per page:
+//   * QK^T on the matrix cores with the 16 MFMA rows = 4 heads x 4 query
+//     tokens (row 4i + h: token i, head h), so all of a request's query
+//     tokens cost what one does; lane group g then holds query token g's
+//     scores and keeps its own online-softmax state, with the causal limit
+//     of token g applied as a mask;
+//   * the page's V goes from registers (loaded a page ahead) into a
+//     per-wave LDS tile, and P.V runs on the vector ALUs with lane (g, c)
+//     accumulating query token g, dims 8c .. 8c+7, over all 64 tokens,
+//     reading the V rows from LDS (each row read once per lane group) and
+//     the probabilities of its token from a per-wave LDS buffer.
+// The partial states go to the workspace and the ordinary split merge
+// combines them, one (query row, head) at a time.
+#include "internal.h"
+#include "kernel_common.h"
+
+namespace spa {
+namespace {
+
+constexpr int kVerifyWaves = 2;   // kv heads per workgroup, one per wave
+
+// KV: 0 = bf16 pages, 1 = int8 codes, 2 = e4m3 codes (with fp32 scales).
+template <int KV>
+__global__ __launch_bounds__(kVerifyWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
+                   const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ cu_q) {
+    constexpr int D = kHeadDim, P = kPageSize, NW = kVerifyWaves;
+    constexpr bool QUANT = KV != 0;
+    constexpr bool I8 = KV == 1;
+    constexpr int ES = QUANT ? 1 : 2;            // bytes per element
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // QK layout: lane (n, g) = KV token n of a 16-token block, query token g.
+    // PV layout: lane (g, n) = query token g, dims 8n .. 8n+7.  Same lanes.
+    const int n = lane & 15, g = lane >> 4;
+
+    // blockIdx -> (group = b * blocks + kv block, split j); the S splits of a
+    // group share an XCD when the group count allows.
+    const int S = p.splits;
+    const int grp_per_b = p.hkv / NW;
+    const int ngroups = p.batch * grp_per_b;
+    int grp, j;
+    {
+        const int bid = blockIdx.x;
+        if ((ngroups & 7) == 0) {
+            const int xcd = bid & 7, slot = bid >> 3;
+            grp = (slot / S) * 8 + xcd;
+            j = slot % S;
+        } else {
+            grp = bid / S;
+            j = bid % S;
+        }
+    }
+    const int b = grp / grp_per_b;
+    const int kvh = (grp - b * grp_per_b) * NW + wave;
+
+    // This request's query rows; rows outside [0, total_q) are never touched.
+    const int q0 = cu_q[b];
+    int nq = cu_q[b + 1] - q0;
+    if (q0 < 0 || nq < 0 || q0 > p.total_q - nq) nq = 0;
+    nq = min(nq, kMaxVerifyQueries);
+    if (nq == 0) return;   // the whole workgroup
+
+    int L = seq_lens[b];
+    L = (int)min((int64_t)max(L, 0), p.pt_stride * P);
+    const int pages = (L + P - 1) / P;
+    const int pps = (pages + S - 1) / S;
+    const int pg0 = min(j * pps, pages);
+    const int pg1 = min(pg0 + pps, pages);
+    const int row_stride = p.hkv * D;
+    const int vis = L - nq + g + 1;             // query token g sees tokens < vis
+
+    // A operand: row n is head n & 3 of query token n >> 2 (rows of tokens
+    // past n_b repeat the last one and are never stored).  Same contraction
+    // order as the one-token decode.
+    bf16x8_t qa[4];
+    {
+        const int tq = min(n >> 2, nq - 1);
+        const uint16_t *qp = reinterpret_cast<const uint16_t *>(p.q) +
+                             ((int64_t)(q0 + tq) * p.hq + kvh * kGroup + (n & 3)) * D;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int d0 = QUANT ? 64 * (c >> 1) + 16 * g + 8 * (c & 1) : 32 * c + 8 * g;
+            qa[c] = *reinterpret_cast<const bf16x8_t *>(qp + d0);
+        }
+    }
+    // 1-byte codes: the query goes to f16, each row scaled by a power of two
+    // putting its largest |q| in [2^14, 2^15) (exact); score row 4g + h is
+    // unscaled with the factor of lane 4g + h.
+    f16x8_t qa16[4];
+    float qscale[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) qscale[h] = p.qk_scale_log2;
+    if constexpr (QUANT) {
+        float amax = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)qa[c][e]));
+        amax = fmaxf(amax, __shfl_xor(amax, 16));
+        amax = fmaxf(amax, __shfl_xor(amax, 32));   // lane n: row n, all 128 dims
+        const int sh = amax > 0.f ? 15 - __builtin_amdgcn_frexp_expf(amax) : 0;
+        const float up = __builtin_ldexpf(1.f, sh);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qa16[c][e] = (_Float16)((float)qa[c][e] * up);
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+            qscale[h] = p.qk_scale_log2 * __builtin_ldexpf(1.f, -__shfl(sh, 4 * g + h));
+    }
+
+    float m[4], lpart[4], acc[4][8], psum[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        m[h] = kNegInf;
+        lpart[h] = 0.f;
+        psum[h] = 0.f;
+#pragma unroll
+        for (int d = 0; d < 8; ++d) acc[h][d] = 0.f;
+    }
+
+    // pbuf[wave][query token][pair][head]: probabilities of tokens
+    // (32q + t, 32q + 16 + t) packed as one word, pair = 16q + t.
+    __shared__ uint32_t pbuf[NW][kMaxVerifyQueries][32][4];
+    // vbuf[wave]: the page's V rows of this wave's kv head, row-major.
+    constexpr int VROW = D * ES;
+    __shared__ __attribute__((aligned(16))) unsigned char vbuf[NW][P * VROW];
+    unsigned char *vt = vbuf[wave];
+
+    const int32_t *pt_row = page_table + (int64_t)b * p.pt_stride;
+    const int row_bytes = row_stride * ES;
+    const int k_lane = (n * row_stride + (QUANT ? 16 : 8) * g) * ES;
+    const int v_lane = (g * row_stride + 8 * n) * ES;   // token 4i + g, dims 8n ..
+    const int s_lane64 = lane * p.hkv * 4;
+    uint4 kr[4][4];
+    uint4 vr16[16];
+    uint4 kr8[4][2];
+    uint2 vr8[16];
+    float ksc_tok = 0.f, vsc_tok = 0.f;
+    auto rsrc = [&](const void *base, int64_t page, int64_t elem_per_page, int64_t elem_off,
+                    int esize, int nbytes) {
+        const char *ptr = static_cast<const char *>(base) + (page * elem_per_page + elem_off) * esize;
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(ptr), (short)0, nbytes,
+                                                 kBufferWord3);
+    };
+    auto load_k = [&](int64_t page, int valid_rows) {
+        const auto r = rsrc(p.k_pages, page, (int64_t)P * row_stride, (int64_t)kvh * D, ES,
+                            valid_rows * row_bytes);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            if constexpr (!QUANT) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    kr[t][c] = buf_ld16(r, k_lane + 64 * c, 16 * t * row_bytes);
+            } else {
+#pragma unroll
+                for (int c2 = 0; c2 < 2; ++c2)
+                    kr8[t][c2] = buf_ld16(r, k_lane + 64 * c2, 16 * t * row_bytes);
+            }
+        }
+        if constexpr (QUANT) {
+            const auto rs = rsrc(p.k_scales, page, (int64_t)P * p.hkv, kvh, 4,
+                                 valid_rows * p.hkv * 4);
+            ksc_tok = buf_ldf(rs, s_lane64, 0);
+        }
+    };
+    auto load_v = [&](int64_t page, int valid_rows) {
+        const auto r = rsrc(p.v_pages, page, (int64_t)P * row_stride, (int64_t)kvh * D, ES,
+                            valid_rows * row_bytes);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if constexpr (!QUANT)
+                vr16[i] = buf_ld16(r, v_lane, 4 * i * row_bytes);
+            else
+                vr8[i] = buf_ld8(r, v_lane, 4 * i * row_bytes);
+        }
+        if constexpr (QUANT) {
+            const auto rs = rsrc(p.v_scales, page, (int64_t)P * p.hkv, kvh, 4,
+                                 valid_rows * p.hkv * 4);
+            vsc_tok = buf_ldf(rs, s_lane64, 0) * (I8 ? 1.f : kF8ValueScale);
+        }
+    };
+    // Loaded rows of logical page i (zero range past the split or for a page
+    // id outside the pool: reads 0, touches no memory).
+    auto page_rows = [&](int i, int64_t &page) {
+        page = 0;
+        if (i >= pg1) return 0;
+        const int32_t id = pt_row[i];
+        const bool ok = (uint32_t)id < (uint32_t)p.num_pages;
+        page = ok ? id : 0;
+        return ok ? min(P, L - i * P) : 0;
+    };
+
+    int pg = pg0;
+    if (pg < pg1) {
+        int64_t page;
+        const int rows = page_rows(pg, page);
+        load_k(page, rows);
+        load_v(page, rows);
+    }
+    for (; pg < pg1; ++pg) {
+        int64_t page_next;
+        const int valid_next = page_rows(pg + 1, page_next);
+        const int valid = min(P, L - pg * P);
+
+        // ---- this page's V into LDS; its registers then take the next page's V
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            unsigned char *dst = vt + (4 * i + g) * VROW + 8 * n * ES;
+            if constexpr (!QUANT)
+                *reinterpret_cast<uint4 *>(dst) = vr16[i];
+            else
+                *reinterpret_cast<uint2 *>(dst) = vr8[i];
+        }
+        const float vsc_cur = vsc_tok;
+        __builtin_amdgcn_sched_barrier(0);
+        load_v(page_next, valid_next);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- S = Q K^T: lane (n, g) gets s[token g, head h][KV token 16t + n]
+        f32x4_t sacc[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            sacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                if constexpr (!QUANT) {
+                    sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        qa[c], __builtin_bit_cast(bf16x8_t, kr[t][c]), sacc[t], 0, 0, 0);
+                } else {
+                    const uint4 w = kr8[t][c >> 1];
+                    const uint2 h = (c & 1) ? make_uint2(w.z, w.w) : make_uint2(w.x, w.y);
+                    sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        qa16[c], I8 ? i8x8_to_f16(h) : e4m3x8_to_f16(h), sacc[t], 0, 0, 0);
+                }
+            }
+        }
+        float s[4][4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int tok = 16 * t + n;
+            const bool ok = tok < valid && pg * P + tok < vis;
+            const float kt = QUANT ? lane_value(ksc_tok, tok) : 1.f;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) s[t][h] = ok ? sacc[t][h] * (qscale[h] * kt) : kNegInf;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        load_k(page_next, valid_next);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- online softmax (base 2) per (query token g, head h); a row
+        // that has seen no token yet keeps m = -inf and weights 0
+        float alpha[4], pv[4][4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            float mx = fmaxf(fmaxf(s[0][h], s[1][h]), fmaxf(s[2][h], s[3][h]));
+            mx = row_max16(mx);
+            const float mnew = fmaxf(m[h], mx);
+            const float mref = mnew == kNegInf ? 0.f : mnew;
+            alpha[h] = exp2_fast(m[h] - mref);
+            m[h] = mnew;
+            float rs = 0.f;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                pv[t][h] = exp2_fast(s[t][h] - mref);
+                rs += pv[t][h];
+            }
+            lpart[h] = __builtin_fmaf(lpart[h], alpha[h], rs);
+        }
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp) {
+            float a[4], bb[4];
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                a[h] = pv[2 * tp][h];
+                bb[h] = pv[2 * tp + 1][h];
+            }
+            uint4 w;
+            if constexpr (QUANT) {   // value scale folded in, f16
+                const float va = lane_value(vsc_cur, 32 * tp + n);
+                const float vb = lane_value(vsc_cur, 32 * tp + 16 + n);
+                w = make_uint4(pack_f16x2(a[0] * va, bb[0] * vb), pack_f16x2(a[1] * va, bb[1] * vb),
+                               pack_f16x2(a[2] * va, bb[2] * vb), pack_f16x2(a[3] * va, bb[3] * vb));
+            } else {
+                w = make_uint4(pack_bf16x2(a[0], bb[0]), pack_bf16x2(a[1], bb[1]),
+                               pack_bf16x2(a[2], bb[2]), pack_bf16x2(a[3], bb[3]));
+            }
+            *reinterpret_cast<uint4 *>(&pbuf[wave][g][16 * tp + n][0]) = w;
+        }
+        // LDS ops of one wave complete in order; this only keeps the compiler
+        // from moving the reads above the writes.
+        __asm__ volatile("" ::: "memory");
+
+        // ---- P.V: lane (g, n), pair jp = tokens (ta, ta + 16)
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+#pragma unroll
+            for (int d = 0; d < 8; ++d) acc[h][d] *= alpha[h];
+            if constexpr (I8) psum[h] *= alpha[h];
+        }
+#pragma unroll 4
+        for (int jp = 0; jp < 32; ++jp) {
+            const uint4 pk = *reinterpret_cast<const uint4 *>(&pbuf[wave][g][jp][0]);
+            const uint32_t ph[4] = {pk.x, pk.y, pk.z, pk.w};
+            const int ta = 32 * (jp >> 4) + (jp & 15);
+            const unsigned char *ra = vt + ta * VROW + 8 * n * ES;
+            const unsigned char *rb = ra + 16 * VROW;
+            if constexpr (!QUANT) {
+                const uint4 va = *reinterpret_cast<const uint4 *>(ra);
+                const uint4 vb = *reinterpret_cast<const uint4 *>(rb);
+                const uint32_t wa[4] = {va.x, va.y, va.z, va.w};
+                const uint32_t wb[4] = {vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t lo = __builtin_amdgcn_perm(wb[e], wa[e], 0x05040100u);
+                    const uint32_t hi = __builtin_amdgcn_perm(wb[e], wa[e], 0x07060302u);
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) {
+                        acc[h][2 * e] = dot2(ph[h], lo, acc[h][2 * e]);
+                        acc[h][2 * e + 1] = dot2(ph[h], hi, acc[h][2 * e + 1]);
+                    }
+                }
+            } else {
+                const uint2 va = *reinterpret_cast<const uint2 *>(ra);
+                const uint2 vb = *reinterpret_cast<const uint2 *>(rb);
+                uint32_t vp[8];
+                if constexpr (I8) {
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) psum[h] = dot2_f16(ph[h], kF16One2, psum[h]);
+                    vp[0] = i8_pair_f16<0>(vb.x, va.x);
+                    vp[1] = i8_pair_f16<1>(vb.x, va.x);
+                    vp[2] = i8_pair_f16<2>(vb.x, va.x);
+                    vp[3] = i8_pair_f16<3>(vb.x, va.x);
+                    vp[4] = i8_pair_f16<0>(vb.y, va.y);
+                    vp[5] = i8_pair_f16<1>(vb.y, va.y);
+                    vp[6] = i8_pair_f16<2>(vb.y, va.y);
+                    vp[7] = i8_pair_f16<3>(vb.y, va.y);
+                } else {
+                    e4m3_pairs_f16<0>(vb.x, va.x, vp[0], vp[1]);
+                    e4m3_pairs_f16<2>(vb.x, va.x, vp[2], vp[3]);
+                    e4m3_pairs_f16<0>(vb.y, va.y, vp[4], vp[5]);
+                    e4m3_pairs_f16<2>(vb.y, va.y, vp[6], vp[7]);
+                }
+#pragma unroll
+                for (int d = 0; d < 8; ++d)
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) acc[h][d] = dot2_f16(ph[h], vp[d], acc[h][d]);
+            }
+        }
+        // the next page's V overwrites the tile only after these reads
+        __asm__ volatile("" ::: "memory");
+    }
+    if constexpr (I8) {
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+#pragma unroll
+            for (int d = 0; d < 8; ++d) acc[h][d] = __builtin_fmaf(-kI8Bias, psum[h], acc[h][d]);
+    }
+
+    // ---- partial state of query token g: l over the 16 lanes of its group
+#pragma unroll
+    for (int h = 0; h < 4; ++h) lpart[h] = row_sum16(lpart[h]);
+    if (g < nq) {
+        const int64_t row0 = ((int64_t)(q0 + g) * p.hq + kvh * kGroup) * S + j;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            const int64_t idx = row0 + (int64_t)h * S;
+            float *dst = p.part_acc + idx * D + 8 * n;
+            *reinterpret_cast<uint4 *>(dst) =
+                make_uint4(__float_as_uint(acc[h][0]), __float_as_uint(acc[h][1]),
+                           __float_as_uint(acc[h][2]), __float_as_uint(acc[h][3]));
+            *reinterpret_cast<uint4 *>(dst + 4) =
+                make_uint4(__float_as_uint(acc[h][4]), __float_as_uint(acc[h][5]),
+                           __float_as_uint(acc[h][6]), __float_as_uint(acc[h][7]));
+            if (n == 0) {
+                p.part_max[idx] = m[h] == kNegInf ? kNegInf : m[h] * kLn2;
+                p.part_sum[idx] = lpart[h];
+            }
+        }
+    }
+}
+
+template <int KV>
+hipError_t launch_verify_kv(const DecodeParams &p, hipStream_t stream) {
+    const unsigned grid = (unsigned)(p.batch * (p.hkv / kVerifyWaves) * p.splits);
+    hipLaunchKernelGGL((verify_kernel<KV>), dim3(grid), dim3(kVerifyWaves * 64), 0, stream, p,
+                       p.page_table, p.seq_lens, p.cu_seqlens_q);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_verify(const DecodeParams &p, int kv_type, hipStream_t stream) {
+    hipError_t err;
+    if (kv_type == kKvInt8)
+        err = launch_verify_kv<1>(p, stream);
+    else if (kv_type == kKvFp8)
+        err = launch_verify_kv<2>(p, stream);
+    else
+        err = launch_verify_kv<0>(p, stream);
+    if (err != hipSuccess) return err;
+    return launch_split_merge(p.part_acc, p.part_max, p.part_sum, p.total_q * p.hq, kHeadDim,
+                              p.splits, p.out, p.lse, stream);
+}
+
+bool verify_supported(int hkv) { return hkv % kVerifyWaves == 0; }
+
+}  // namespace spa

@@ -27,7 +27,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["spa_build_page_table", "spa_build_metadata", "spa_paged_decode_attention",
-              "spa_split_merge",
+              "spa_paged_verify_attention", "spa_verify_workspace_bytes", "spa_split_merge",
               "spa_decode_workspace_bytes", "spa_workspace_reset", "spa_status_string"]:
         assert n in names
 
@@ -171,6 +171,44 @@ def _full(**kw):
 ])
 def test_full_metadata_argument_checks(kw, code):
     assert _full(**kw) == code
+
+
+def _verify(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ks=None, vs=None, pt=FAKE, pts=128, sl=FAKE, cu=FAKE, B=2,
+             T=8, mq=4, Hq=32, Hkv=8, D=128, P=64, npg=16, S=4, scale=0.088, kvd=0, ws=FAKE,
+             wsb=1 << 30, out=FAKE, lse=FAKE)
+    a.update(kw)
+    return spa.lib().spa_paged_verify_attention(
+        a["q"], a["k"], a["v"], a["ks"], a["vs"], a["pt"], a["pts"], a["sl"], a["cu"], a["B"],
+        a["T"], a["mq"], a["Hq"], a["Hkv"], a["D"], a["P"], a["npg"], a["S"], a["scale"], a["kvd"],
+        a["ws"], a["wsb"], a["out"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(mq=0), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(mq=5), spa.SPA_ERR_UNSUPPORTED),
+    (dict(T=-1), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(cu=None), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(Hq=12, Hkv=3), spa.SPA_ERR_UNSUPPORTED),            # odd kv heads
+    (dict(kvd=1), spa.SPA_ERR_INVALID_ARGUMENT),              # int8 without scales
+    (dict(kvd=2, ks=FAKE, vs=FAKE, T=0), spa.SPA_OK),
+    (dict(out=FAKE_ODD), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(wsb=1024), spa.SPA_ERR_WORKSPACE_TOO_SMALL),
+    (dict(scale=math.nan), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(D=64), spa.SPA_ERR_UNSUPPORTED),
+    (dict(B=0), spa.SPA_OK),
+])
+def test_verify_argument_checks(kw, code):
+    assert _verify(**kw) == code
+
+
+def test_verify_workspace_bytes():
+    f = spa.verify_workspace_bytes
+    n = f(128, 32, 8, 128, 16)
+    rows = 128 * 32 * 16
+    assert n >= rows * 128 * 4 + 2 * rows * 4 and n % 256 == 0
+    assert f(-1, 32, 8, 128, 4) == 0
+    assert _verify(wsb=n - 1, T=128, S=16) == spa.SPA_ERR_WORKSPACE_TOO_SMALL
 
 
 @pytest.mark.parametrize("args,code", [

@@ -1,0 +1,113 @@
+"""GPU parity for multi-token query decode (target verify / draft extend)
+against the fp64 oracle, through the C ABI; same tolerances as the one-token
+decode (tests/gpu_util.py)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import split_paged_attention_amd as spa
+import workloads as W
+from tests.gpu_util import DevCase, bf16_dev, compare_attention, config_case
+
+pytestmark = pytest.mark.gpu
+
+
+def small_case(lens, kv="bf16", S=4, seed=31):
+    P = 64
+    need = sum(-(-L // P) for L in lens)
+    msp = max(1, max(-(-L // P) for L in lens))
+    return W.make_case(seed=seed, seq_lens=lens, num_pages=need + 3, num_splits=S, kv_dtype=kv,
+                       num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=P,
+                       req_pool_rows=max(4, len(lens)), req_to_token_stride=msp * P,
+                       max_seq_pages=msp, name=f"verify{lens}_{kv}_S{S}")
+
+
+def run_verify(c, q_rows, cu, S=None, page_table=None, cu_dev=None, max_q_len=4):
+    d = DevCase(c)
+    pt = d.page_list if page_table is None else page_table
+    cu_d = torch.from_numpy(cu).cuda() if cu_dev is None else cu_dev
+    out, lse = spa.paged_verify_attention(
+        bf16_dev(q_rows), d.k, d.v, pt, d.seq_lens, cu_d, c.num_splits if S is None else S,
+        float(c.scale), max_q_len=max_q_len, kv_dtype=c.kv_dtype, k_scales=d.ks, v_scales=d.vs)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def oracle_verify(c, q_rows, cu):
+    return oracle.verify_attention(q_rows, c.k_pages, c.v_pages, c.page_list, c.seq_lens, cu,
+                                   num_kv_heads=c.num_kv_heads, page_size=c.page_size,
+                                   scale=c.scale, kv_dtype=c.kv_dtype, k_scales=c.k_scales,
+                                   v_scales=c.v_scales)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8"])
+@pytest.mark.parametrize("lens,qlens,S", [
+    ([20, 9, 33, 300, 1000], [4, 1, 3, 2, 4], 4),
+    ([64, 65, 128, 2000], [4, 4, 4, 4], 16),       # draft rows across page / split edges
+    ([1, 4, 700, 5], [1, 4, 2, 0], 3),             # a request with no query rows
+    ([4096, 3, 129], [3, 3, 1], 64),               # many empty splits
+])
+def test_verify_parity(kv, lens, qlens, S):
+    c = small_case(lens, kv=kv, S=S)
+    q_rows, cu = W.verify_queries(c, qlens)
+    print(f"[case] verify {kv} lens={lens} qlens={qlens} S={S}", flush=True)
+    out, lse = run_verify(c, q_rows, cu)
+    o_ref, l_ref = oracle_verify(c, q_rows, cu)
+    compare_attention(out, lse, o_ref, l_ref, label=f"verify {kv} {lens}")
+
+
+def test_verify_headline_shape_four_draft_tokens():
+    """Batch 32, context 8K, 4 query tokens per request (draft rows at the end
+    of each context): every output against the oracle."""
+    c = config_case(4)
+    q_rows, cu = W.verify_queries(c, [4] * c.batch)
+    print("[case] verify batch 32 / 8K / 4 tokens", flush=True)
+    d = DevCase(c)
+    pt, _, _ = d.page_table()
+    out, lse = run_verify(c, q_rows, cu, page_table=pt)
+    o_ref, l_ref = oracle_verify(c, q_rows, cu)
+    compare_attention(out, lse, o_ref, l_ref, label="verify b32 8K q4")
+
+
+def test_verify_consumes_metadata_cu_seqlens_q():
+    """The metadata build's strided and cumsum modes produce the
+    cu_seqlens_q the verify call reads, on the device."""
+    c = small_case([200, 77, 513, 64], kv="bf16", S=4)
+    d = DevCase(c)
+    print("[case] verify with cu_seqlens_q from the metadata kernel", flush=True)
+    for mode, qlens in ((spa.Q_MODE_STRIDED, [3, 3, 3, 3]), (spa.Q_MODE_CUMSUM, [4, 1, 2, 3])):
+        q_rows, cu = W.verify_queries(c, qlens)
+        md = spa.build_metadata(d.r2t, d.rpi, d.seq_lens, c.page_size, c.max_seq_pages,
+                                q_mode=mode, q_stride=3,
+                                qlens=torch.tensor(qlens, dtype=torch.int32, device="cuda"))
+        out, lse = run_verify(c, q_rows, cu, page_table=md["page_table"],
+                              cu_dev=md["cu_seqlens_q"])
+        assert np.array_equal(md["cu_seqlens_q"].cpu().numpy(), cu)
+        o_ref, l_ref = oracle_verify(c, q_rows, cu)
+        compare_attention(out, lse, o_ref, l_ref, label=f"verify q_mode {mode}")
+
+
+def test_verify_queries_with_nothing_visible():
+    """A request shorter than its query count: its first rows see no token
+    (out 0, lse -inf)."""
+    c = small_case([2, 40], kv="bf16", S=2)
+    c.seq_lens[0] = 2
+    q_rows, cu = W.verify_queries(c, [2, 4])
+    cu = np.array([0, 4, 8], np.int32)              # request 0 claims 4 rows, 2 tokens
+    q_rows = np.concatenate([q_rows[:2], q_rows[:2], q_rows[2:]])
+    print("[case] verify rows with no visible token", flush=True)
+    out, lse = run_verify(c, q_rows, cu)
+    o_ref, l_ref = oracle_verify(c, q_rows, cu)
+    assert np.isneginf(l_ref[:2]).all()
+    compare_attention(out, lse, o_ref, l_ref, label="verify empty rows")
+    assert torch.isneginf(lse[:2]).all() and (out[:2].float() == 0).all()
+
+
+def test_verify_single_token_rows_match_decode_within_tolerance():
+    c = small_case([900, 33, 4000], kv="int8", S=8)
+    q_rows, cu = W.verify_queries(c, [1, 1, 1])
+    print("[case] verify q_len 1 vs decode", flush=True)
+    out, lse = run_verify(c, q_rows, cu, max_q_len=1)
+    o_ref, l_ref = oracle_verify(c, q_rows, cu)
+    compare_attention(out, lse, o_ref, l_ref, label="verify q1")
