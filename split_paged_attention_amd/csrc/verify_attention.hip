@@ -14,11 +14,13 @@
 //     tokens cost what one does; lane group g then holds query token g's
 //     scores and keeps its own online-softmax state, with the causal limit
 //     of token g applied as a mask;
-//   * the page's V goes from registers (loaded a page ahead) into a
-//     per-wave LDS tile, and P.V runs on the vector ALUs with lane (g, c)
-//     accumulating query token g, dims 8c .. 8c+7, over all 64 tokens,
-//     reading the V rows from LDS (each row read once per lane group) and
-//     the probabilities of its token from a per-wave LDS buffer.
+//   * P.V on the matrix cores too: the page's V goes from registers
+//     (loaded a page ahead) into a per-wave LDS tile, token-major (1-byte
+//     codes converted to exact f16 on the way), the probabilities into a
+//     token-major per-wave LDS tile, and the transposed LDS read
+//     (ds_read_b64_tr_b16) turns both into MFMA operands: O[16 rows][128
+//     dims] += P[16 rows][32 tokens] x V[32 tokens][128 dims], 16 MFMAs per
+//     page, with the output rows in the same lanes as the softmax state.
 // The partial states go to the workspace and the ordinary split merge
 // combines them, one (query row, head) at a time.
 #include "internal.h"
@@ -28,6 +30,23 @@ namespace spa {
 namespace {
 
 constexpr int kVerifyWaves = 2;   // kv heads per workgroup, one per wave
+
+// Transposed LDS read of 4 16-bit elements (see the addressing in the kernel).
+__device__ __forceinline__ uint64_t tr_read(const uint16_t *p) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16 *)(const_cast<uint16_t *>(p)));
+    return __builtin_bit_cast(uint64_t, v);
+}
+__device__ __forceinline__ bf16x8_t join_bf16x8(uint64_t lo, uint64_t hi) {
+    return __builtin_bit_cast(bf16x8_t, make_uint4((uint32_t)lo, (uint32_t)(lo >> 32),
+                                                   (uint32_t)hi, (uint32_t)(hi >> 32)));
+}
+__device__ __forceinline__ f16x8_t join_f16x8(uint64_t lo, uint64_t hi) {
+    return __builtin_bit_cast(f16x8_t, make_uint4((uint32_t)lo, (uint32_t)(lo >> 32),
+                                                  (uint32_t)hi, (uint32_t)(hi >> 32)));
+}
 
 // KV: 0 = bf16 pages, 1 = int8 codes, 2 = e4m3 codes (with fp32 scales).
 template <int KV>
@@ -40,20 +59,27 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
     constexpr int ES = QUANT ? 1 : 2;            // bytes per element
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // QK layout: lane (n, g) = KV token n of a 16-token block, query token g.
-    // PV layout: lane (g, n) = query token g, dims 8n .. 8n+7.  Same lanes.
+    // QK layout: lane (n, g) = KV token n of a 16-token block, query token g;
+    // the P.V output has the same rows in the same lanes, with dims 16 blk + n.
+    // V registers: lane (g, n) holds token 4i + g, dims 8n .. 8n+7.
     const int n = lane & 15, g = lane >> 4;
 
-    // blockIdx -> (group = b * blocks + kv block, split j); the S splits of a
-    // group share an XCD when the group count allows.
+    // blockIdx -> (group = b * blocks + kv block, split j), placed on the 8
+    // XCDs as in the one-token decode: for 1-byte codes and a batch that is
+    // a multiple of 8, all kv blocks and splits of a request share an XCD;
+    // otherwise the S splits of a group do when the group count allows.
     const int S = p.splits;
     const int grp_per_b = p.hkv / NW;
     const int ngroups = p.batch * grp_per_b;
     int grp, j;
     {
         const int bid = blockIdx.x;
-        if ((ngroups & 7) == 0) {
-            const int xcd = bid & 7, slot = bid >> 3;
+        const int xcd = bid & 7, slot = bid >> 3;
+        if (QUANT && (p.batch & 7) == 0) {
+            j = slot % S;
+            const int rest = slot / S;
+            grp = ((rest / grp_per_b) * 8 + xcd) * grp_per_b + rest % grp_per_b;
+        } else if ((ngroups & 7) == 0) {
             grp = (slot / S) * 8 + xcd;
             j = slot % S;
         } else {
@@ -120,23 +146,29 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
             qscale[h] = p.qk_scale_log2 * __builtin_ldexpf(1.f, -__shfl(sh, 4 * g + h));
     }
 
-    float m[4], lpart[4], acc[4][8], psum[4];
+    // softmax state of row (query token g, head h); acc[blk][h] = output
+    // row (g, h), dim 16 blk + n (the MFMA output layout)
+    float m[4], lpart[4];
+    f32x4_t acc[8];
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
         m[h] = kNegInf;
         lpart[h] = 0.f;
-        psum[h] = 0.f;
-#pragma unroll
-        for (int d = 0; d < 8; ++d) acc[h][d] = 0.f;
     }
+#pragma unroll
+    for (int blk = 0; blk < 8; ++blk) acc[blk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // pbuf[wave][query token][pair][head]: probabilities of tokens
-    // (32q + t, 32q + 16 + t) packed as one word, pair = 16q + t.
-    __shared__ uint32_t pbuf[NW][kMaxVerifyQueries][32][4];
-    // vbuf[wave]: the page's V rows of this wave's kv head, row-major.
-    constexpr int VROW = D * ES;
-    __shared__ __attribute__((aligned(16))) unsigned char vbuf[NW][P * VROW];
-    unsigned char *vt = vbuf[wave];
+    // Per-wave LDS tiles, 16-bit elements, token-major: V[64 tokens][128
+    // dims] (bf16, or f16 values of the codes) and P[64 tokens][16 rows].
+    __shared__ __attribute__((aligned(16))) uint16_t vbuf[NW][P][D];
+    __shared__ __attribute__((aligned(16))) uint16_t pbuf[NW][P][16];
+    uint16_t(*vt)[D] = vbuf[wave];
+    uint16_t(*pt16)[16] = pbuf[wave];
+    // Transposed-read addressing: lane 16G + 4e + qd supplies row 8G + e
+    // (+ 4 for the second read), columns 4qd .. 4qd+3; lane 16G + i then
+    // receives column i of rows 8G .. 8G+3 (8G+4 .. 8G+7): the MFMA operand
+    // lane (i, k-chunk G).
+    const int tr_row = 8 * g + ((lane & 15) >> 2), tr_col = 4 * (lane & 3);
 
     const int32_t *pt_row = page_table + (int64_t)b * p.pt_stride;
     const int row_bytes = row_stride * ES;
@@ -214,14 +246,28 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
         const int valid_next = page_rows(pg + 1, page_next);
         const int valid = min(P, L - pg * P);
 
-        // ---- this page's V into LDS; its registers then take the next page's V
+        // ---- this page's V into LDS (token 4i + g, dims 8n ..); its registers
+        // then take the next page's V
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            unsigned char *dst = vt + (4 * i + g) * VROW + 8 * n * ES;
-            if constexpr (!QUANT)
-                *reinterpret_cast<uint4 *>(dst) = vr16[i];
-            else
-                *reinterpret_cast<uint2 *>(dst) = vr8[i];
+            uint4 w;
+            if constexpr (!QUANT) {
+                w = vr16[i];
+            } else if constexpr (I8) {
+                w = __builtin_bit_cast(uint4, i8x8_to_f16(vr8[i]));
+            } else {
+                const uint2 c = vr8[i];
+                w = make_uint4(
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
+                                                     c.x, 1.f / kF8ValueScale, false)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
+                                                     c.x, 1.f / kF8ValueScale, true)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
+                                                     c.y, 1.f / kF8ValueScale, false)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
+                                                     c.y, 1.f / kF8ValueScale, true)));
+            }
+            *reinterpret_cast<uint4 *>(&vt[4 * i + g][8 * n]) = w;
         }
         const float vsc_cur = vsc_tok;
         __builtin_amdgcn_sched_barrier(0);
@@ -278,96 +324,52 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
             }
             lpart[h] = __builtin_fmaf(lpart[h], alpha[h], rs);
         }
+        // probabilities of row (g, h) for tokens 16t + n into the P tile
+        // (1-byte codes: value scale folded in, f16)
 #pragma unroll
-        for (int tp = 0; tp < 2; ++tp) {
-            float a[4], bb[4];
+        for (int t = 0; t < 4; ++t) {
+            float a[4];
 #pragma unroll
-            for (int h = 0; h < 4; ++h) {
-                a[h] = pv[2 * tp][h];
-                bb[h] = pv[2 * tp + 1][h];
-            }
-            uint4 w;
-            if constexpr (QUANT) {   // value scale folded in, f16
-                const float va = lane_value(vsc_cur, 32 * tp + n);
-                const float vb = lane_value(vsc_cur, 32 * tp + 16 + n);
-                w = make_uint4(pack_f16x2(a[0] * va, bb[0] * vb), pack_f16x2(a[1] * va, bb[1] * vb),
-                               pack_f16x2(a[2] * va, bb[2] * vb), pack_f16x2(a[3] * va, bb[3] * vb));
+            for (int h = 0; h < 4; ++h) a[h] = pv[t][h];
+            uint2 w;
+            if constexpr (QUANT) {
+                const float vs = lane_value(vsc_cur, 16 * t + n);
+                w = make_uint2(pack_f16x2(a[0] * vs, a[1] * vs), pack_f16x2(a[2] * vs, a[3] * vs));
             } else {
-                w = make_uint4(pack_bf16x2(a[0], bb[0]), pack_bf16x2(a[1], bb[1]),
-                               pack_bf16x2(a[2], bb[2]), pack_bf16x2(a[3], bb[3]));
+                w = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
             }
-            *reinterpret_cast<uint4 *>(&pbuf[wave][g][16 * tp + n][0]) = w;
+            *reinterpret_cast<uint2 *>(&pt16[16 * t + n][4 * g]) = w;
         }
         // LDS ops of one wave complete in order; this only keeps the compiler
         // from moving the reads above the writes.
         __asm__ volatile("" ::: "memory");
 
-        // ---- P.V: lane (g, n), pair jp = tokens (ta, ta + 16)
+        // ---- O += P V on the matrix cores, 32 tokens per step
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
 #pragma unroll
-            for (int d = 0; d < 8; ++d) acc[h][d] *= alpha[h];
-            if constexpr (I8) psum[h] *= alpha[h];
+            for (int blk = 0; blk < 8; ++blk) acc[blk][h] *= alpha[h];
         }
-#pragma unroll 4
-        for (int jp = 0; jp < 32; ++jp) {
-            const uint4 pk = *reinterpret_cast<const uint4 *>(&pbuf[wave][g][jp][0]);
-            const uint32_t ph[4] = {pk.x, pk.y, pk.z, pk.w};
-            const int ta = 32 * (jp >> 4) + (jp & 15);
-            const unsigned char *ra = vt + ta * VROW + 8 * n * ES;
-            const unsigned char *rb = ra + 16 * VROW;
-            if constexpr (!QUANT) {
-                const uint4 va = *reinterpret_cast<const uint4 *>(ra);
-                const uint4 vb = *reinterpret_cast<const uint4 *>(rb);
-                const uint32_t wa[4] = {va.x, va.y, va.z, va.w};
-                const uint32_t wb[4] = {vb.x, vb.y, vb.z, vb.w};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t lo = __builtin_amdgcn_perm(wb[e], wa[e], 0x05040100u);
-                    const uint32_t hi = __builtin_amdgcn_perm(wb[e], wa[e], 0x07060302u);
+        for (int kb = 0; kb < 2; ++kb) {
+            const int r0 = 32 * kb + tr_row;
+            const uint64_t a_lo = tr_read(&pt16[r0][tr_col]);
+            const uint64_t a_hi = tr_read(&pt16[r0 + 4][tr_col]);
 #pragma unroll
-                    for (int h = 0; h < 4; ++h) {
-                        acc[h][2 * e] = dot2(ph[h], lo, acc[h][2 * e]);
-                        acc[h][2 * e + 1] = dot2(ph[h], hi, acc[h][2 * e + 1]);
-                    }
-                }
-            } else {
-                const uint2 va = *reinterpret_cast<const uint2 *>(ra);
-                const uint2 vb = *reinterpret_cast<const uint2 *>(rb);
-                uint32_t vp[8];
-                if constexpr (I8) {
-#pragma unroll
-                    for (int h = 0; h < 4; ++h) psum[h] = dot2_f16(ph[h], kF16One2, psum[h]);
-                    vp[0] = i8_pair_f16<0>(vb.x, va.x);
-                    vp[1] = i8_pair_f16<1>(vb.x, va.x);
-                    vp[2] = i8_pair_f16<2>(vb.x, va.x);
-                    vp[3] = i8_pair_f16<3>(vb.x, va.x);
-                    vp[4] = i8_pair_f16<0>(vb.y, va.y);
-                    vp[5] = i8_pair_f16<1>(vb.y, va.y);
-                    vp[6] = i8_pair_f16<2>(vb.y, va.y);
-                    vp[7] = i8_pair_f16<3>(vb.y, va.y);
-                } else {
-                    e4m3_pairs_f16<0>(vb.x, va.x, vp[0], vp[1]);
-                    e4m3_pairs_f16<2>(vb.x, va.x, vp[2], vp[3]);
-                    e4m3_pairs_f16<0>(vb.y, va.y, vp[4], vp[5]);
-                    e4m3_pairs_f16<2>(vb.y, va.y, vp[6], vp[7]);
-                }
-#pragma unroll
-                for (int d = 0; d < 8; ++d)
-#pragma unroll
-                    for (int h = 0; h < 4; ++h) acc[h][d] = dot2_f16(ph[h], vp[d], acc[h][d]);
+            for (int blk = 0; blk < 8; ++blk) {
+                const uint64_t b_lo = tr_read(&vt[r0][16 * blk + tr_col]);
+                const uint64_t b_hi = tr_read(&vt[r0 + 4][16 * blk + tr_col]);
+                if constexpr (!QUANT)
+                    acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        join_bf16x8(a_lo, a_hi), join_bf16x8(b_lo, b_hi), acc[blk], 0, 0, 0);
+                else
+                    acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        join_f16x8(a_lo, a_hi), join_f16x8(b_lo, b_hi), acc[blk], 0, 0, 0);
             }
         }
         // the next page's V overwrites the tile only after these reads
         __asm__ volatile("" ::: "memory");
     }
-    if constexpr (I8) {
-#pragma unroll
-        for (int h = 0; h < 4; ++h)
-#pragma unroll
-            for (int d = 0; d < 8; ++d) acc[h][d] = __builtin_fmaf(-kI8Bias, psum[h], acc[h][d]);
-    }
-
     // ---- partial state of query token g: l over the 16 lanes of its group
 #pragma unroll
     for (int h = 0; h < 4; ++h) lpart[h] = row_sum16(lpart[h]);
@@ -376,13 +378,9 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
             const int64_t idx = row0 + (int64_t)h * S;
-            float *dst = p.part_acc + idx * D + 8 * n;
-            *reinterpret_cast<uint4 *>(dst) =
-                make_uint4(__float_as_uint(acc[h][0]), __float_as_uint(acc[h][1]),
-                           __float_as_uint(acc[h][2]), __float_as_uint(acc[h][3]));
-            *reinterpret_cast<uint4 *>(dst + 4) =
-                make_uint4(__float_as_uint(acc[h][4]), __float_as_uint(acc[h][5]),
-                           __float_as_uint(acc[h][6]), __float_as_uint(acc[h][7]));
+            float *dst = p.part_acc + idx * D + n;
+#pragma unroll
+            for (int blk = 0; blk < 8; ++blk) dst[16 * blk] = acc[blk][h];
             if (n == 0) {
                 p.part_max[idx] = m[h] == kNegInf ? kNegInf : m[h] * kLn2;
                 p.part_sum[idx] = lpart[h];
