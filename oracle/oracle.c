@@ -185,6 +185,21 @@ typedef struct {
     int64_t q_row;   /* query row to use instead of b (multi-token decode), or -1 */
 } oracle_args;
 
+/* Dequantised element idx of the int8 / e4m3 K (which = 0) or V pool: the
+ * code's value times the scale of its (pool row, kv head).  Kept out of line
+ * so that the bf16 element read stays small enough to be inlined. */
+static __attribute__((noinline)) double quantized_elem(const oracle_args *a, int which,
+                                                      int64_t row, int kvh, int64_t idx) {
+    const float *sc = which ? a->v_scales : a->k_scales;
+    double sigma = (double)sc[row * a->Hkv + kvh];
+    if (a->kv_dtype == ORACLE_KV_FP8) {
+        const uint8_t *base = (const uint8_t *)(which ? a->v_pages : a->k_pages);
+        return e4m3_to_double(base[idx]) * sigma;
+    }
+    const int8_t *base = (const int8_t *)(which ? a->v_pages : a->k_pages);
+    return (double)base[idx] * sigma;
+}
+
 /* Element d of the K (which = 0) or V (which = 1) row of token t, KV head kvh. */
 static double kv_elem(const oracle_args *a, int which, int b, int t, int kvh, int d) {
     int64_t page = a->page_table[(int64_t)b * a->page_table_stride + t / a->P];
@@ -194,13 +209,7 @@ static double kv_elem(const oracle_args *a, int which, int b, int t, int kvh, in
         const uint16_t *base = (const uint16_t *)(which ? a->v_pages : a->k_pages);
         return bf16_to_double(base[idx]);
     }
-    const float *sc = which ? a->v_scales : a->k_scales;
-    if (a->kv_dtype == ORACLE_KV_FP8) {
-        const uint8_t *base = (const uint8_t *)(which ? a->v_pages : a->k_pages);
-        return e4m3_to_double(base[idx]) * (double)sc[row * a->Hkv + kvh];
-    }
-    const int8_t *base = (const int8_t *)(which ? a->v_pages : a->k_pages);
-    return (double)base[idx] * (double)sc[row * a->Hkv + kvh];
+    return quantized_elem(a, which, row, kvh, idx);
 }
 
 /* s_t = scale * q[b,h,:] . k_t */

@@ -43,7 +43,7 @@ MUTANTS = {
     "fp8_exponent_bias": ("ldexp(1.0 + m / 8.0, e - 7)", "ldexp(1.0 + m / 8.0, e - 8)"),
     "fp8_subnormal_as_normal": ("e == 0 ? ldexp(m / 8.0, -6)", "e == 0 ? ldexp(1.0 + m / 8.0, -7)"),
     "fp8_sign_dropped": ("return sign ? -v : v;", "return v;"),
-    "fp8_scale_dropped": ("return e4m3_to_double(base[idx]) * (double)sc[row * a->Hkv + kvh];",
+    "fp8_scale_dropped": ("return e4m3_to_double(base[idx]) * sigma;",
                           "return e4m3_to_double(base[idx]);"),
     "verify_causal_off_by_one": ("visible = seq_lens[b] - nq + i + 1;",
                                  "visible = seq_lens[b] - nq + i;"),
