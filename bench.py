@@ -38,17 +38,30 @@ H200_GRAPH_US = {"b1_ctx1k_s4_bf16": 12.096, "b1_ctx8k_s16_bf16": 22.080,
                  "b8_ctx1k_s4_bf16": 21.376, "b32_ctx8k_s16_bf16": 260.384}
 
 
-def _traffic_for(kernel_file: str, workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
+# Sources of the kernels one call runs (the merge kernel lives with the decode).
+KERNEL_SOURCES = {
+    "decode": ["decode_attention.hip", "kernel_common.h"],
+    "verify": ["verify_attention.hip", "decode_attention.hip", "kernel_common.h"],
+}
+
+
+def _source_hash(kind: str) -> str:
     import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        h.update(open(os.path.join(ROOT, "split_paged_attention_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
+def _traffic_for(kind: str, workload: str):
+    """HBM bytes per call from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     try:
         rec = json.load(open(path))
-        src = open(os.path.join(ROOT, "split_paged_attention_amd", "csrc", kernel_file), "rb").read()
-        if rec.get("kernel_source_sha256") != hashlib.sha256(src).hexdigest():
+        if rec.get("kernel_source_sha256") != _source_hash(kind):
             return None
         return int(rec["hbm_bytes_per_launch"])
     except Exception:
@@ -79,12 +92,11 @@ def _per_dispatch(rows, counter: str, match) -> list:
 
 
 def summarize_pmc(fetch_dir: str, write_dir: str, out_path: str, copy_mib: int, workload: str,
-                  commands: list) -> dict:
+                  commands: list, kind: str = "decode") -> dict:
     """HBM bytes per decode call from two rocprofv3 --pmc runs (FETCH_SIZE, then
     WRITE_SIZE, both in KiB per dispatch), each scaled by what the same counter
     reads for a device copy of copy_mib MiB (which moves exactly that many bytes
     each way)."""
-    import hashlib
     import statistics
     fr, wr = _pmc_rows(fetch_dir), _pmc_rows(write_dir)
     is_copy = lambda k: "copyBuffer" in k or "elementwise" in k or "copy" in k.lower()
@@ -98,8 +110,9 @@ def summarize_pmc(fetch_dir: str, write_dir: str, out_path: str, copy_mib: int, 
     rec["fetch_scale"] = fscale
     rec["write_scale"] = wscale
     total = 0.0
-    for short, pat in (("decode", "decode_kernel"), ("split_merge", "split_merge_kernel"),
-                       ("page_table", "build_page_table_kernel")):
+    producer = ("verify", "verify_kernel") if kind == "verify" else ("decode", "decode_kernel")
+    for short, pat in (producer, ("split_merge", "split_merge_kernel"),
+                       ("metadata", "build_metadata_kernel")):
         f = _per_dispatch(fr, "FETCH_SIZE", lambda k, pat=pat: pat in k)
         w = _per_dispatch(wr, "WRITE_SIZE", lambda k, pat=pat: pat in k)
         if not f or not w or fscale is None or wscale is None:
@@ -108,11 +121,9 @@ def summarize_pmc(fetch_dir: str, write_dir: str, out_path: str, copy_mib: int, 
         wb = statistics.median(w) * 1024.0 * wscale
         rec["kernels"][short] = {"fetch_bytes": round(fb), "write_bytes": round(wb),
                                  "dispatches": len(f)}
-        if short in ("decode", "split_merge"):
+        if short in (producer[0], "split_merge"):
             total += fb + wb
-    src = open(os.path.join(ROOT, "split_paged_attention_amd", "csrc", "decode_attention.hip"),
-               "rb").read()
-    rec["kernel_source_sha256"] = hashlib.sha256(src).hexdigest()
+    rec["kernel_source_sha256"] = _source_hash(kind)
     rec["hbm_bytes_per_launch"] = round(total)
     with open(out_path, "w") as fh:
         json.dump(rec, fh, indent=1)
@@ -122,12 +133,14 @@ def summarize_pmc(fetch_dir: str, write_dir: str, out_path: str, copy_mib: int, 
 class Rig:
     """Device copies of one workload and the calls of one step on them."""
 
-    def __init__(self, case):
+    def __init__(self, case, qlen: int = 0):
         import numpy as np
         import torch
 
         import split_paged_attention_amd as spa
+        import workloads as W
         self.case = case
+        self.qlen = qlen
         dev = "cuda:0"
 
         def bf16(bits):
@@ -157,6 +170,17 @@ class Rig:
         self.out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
         self.ws = spa.new_workspace(B, Hq, case.num_kv_heads, D, S, device=dev)
+        if qlen:
+            # multi-token decode: qlen query rows per request; cu_seqlens_q
+            # comes from the metadata build (strided mode)
+            q_rows, _ = W.verify_queries(case, [qlen] * B)
+            self.q_rows = bf16(q_rows)
+            self.cu_q = torch.empty((B + 1,), dtype=torch.int32, device=dev)
+            T = B * qlen
+            self.ws = torch.empty(spa.verify_workspace_bytes(T, Hq, case.num_kv_heads, D, S),
+                                  dtype=torch.uint8, device=dev)
+            self.out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=dev)
+            self.lse = torch.empty((T, Hq), dtype=torch.float32, device=dev)
         self.spa = spa
         self.merge = None
         self.producer = None
@@ -165,6 +189,12 @@ class Rig:
 
     def k1(self):
         c = self.case
+        if self.qlen:
+            self.spa.build_metadata(self.r2t, self.rpi, self.sl, c.page_size, c.max_seq_pages,
+                                    page_table=self.pt, cache_seqlens=self.cache,
+                                    cu_seqlens_k=self.cu, q_mode=self.spa.Q_MODE_STRIDED,
+                                    q_stride=self.qlen, cu_seqlens_q=self.cu_q)
+            return
         self.spa.build_page_table(self.r2t, self.rpi, self.sl, c.page_size, c.max_seq_pages,
                                   page_table=self.pt, cache_seqlens=self.cache,
                                   cu_seqlens_k=self.cu)
@@ -172,6 +202,12 @@ class Rig:
     def attn(self, i):
         c = self.case
         k, v, ks, vs = self.copies[i % 2]
+        if self.qlen:
+            self.spa.paged_verify_attention(self.q_rows, k, v, self.pt, self.sl, self.cu_q,
+                                            c.num_splits, float(c.scale), max_q_len=self.qlen,
+                                            kv_dtype=c.kv_dtype, k_scales=ks, v_scales=vs,
+                                            workspace=self.ws, out=self.out, lse=self.lse)
+            return
         self.spa.paged_decode_attention(self.q, k, v, self.pt, self.sl, c.num_splits,
                                         float(c.scale), kv_dtype=c.kv_dtype, k_scales=ks,
                                         v_scales=vs, workspace=self.ws, out=self.out,
@@ -275,14 +311,17 @@ def main() -> int:
     ap.add_argument("--ablation", action="store_true",
                     help="launch-gap ablation over workloads instead of the bench line")
     ap.add_argument("--ablation-configs", default="1,2,3,4,5")
+    ap.add_argument("--verify-qlen", type=int, default=0,
+                    help="multi-token decode with this many query tokens per request (1..4)")
     args = ap.parse_args()
 
     if args.summarize_pmc:
         import workloads as W
-        name = W.CONFIGS[args.config]["name"]
+        name = W.CONFIGS[args.config]["name"] + (f"_q{args.verify_qlen}" if args.verify_qlen else "")
         out = args.pmc_out or os.path.join(ROOT, "profiles", f"traffic_{name}.json")
         rec = summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], out,
-                            args.copy_ref_mib or 1024, name, args.pmc_commands)
+                            args.copy_ref_mib or 1024, name, args.pmc_commands,
+                            kind="verify" if args.verify_qlen else "decode")
         print(json.dumps(rec), flush=True)
         return 0
 
@@ -306,7 +345,11 @@ def main() -> int:
     t_gen = time.time()
     case = W.make_config(args.config)
     gen_s = time.time() - t_gen
-    rig = Rig(case)
+    Q = args.verify_qlen
+    if Q < 0 or Q > 4:
+        print("--verify-qlen must be 0..4", file=sys.stderr)
+        return 2
+    rig = Rig(case, qlen=Q)
     dev = "cuda:0"
     B, Hq, D, S = case.batch, case.num_q_heads, case.head_dim, case.num_splits
     Hkv, P = case.num_kv_heads, case.page_size
@@ -357,30 +400,44 @@ def main() -> int:
     graph_step_us = time_graphs(capture(step_fn), R)
     graph_attn_us = time_graphs(capture(attn), R)
 
-    nbytes = W.algorithmic_bytes(case)
+    nbytes = W.verify_algorithmic_bytes(case, [Q] * B) if Q else W.algorithmic_bytes(case)
     achieved = nbytes / (attn_us_mean * 1e-6) / 1e9
     value = nbytes / (ms_per_step * 1e-3) / 1e9
-    workload = case.name
-    traffic = _traffic_for("decode_attention.hip", workload)
+    workload = case.name + (f"_q{Q}" if Q else "")
+    traffic = _traffic_for("verify" if Q else "decode", workload)
 
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
         cores = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
-        oracle.case_attention(case)           # untimed (page-in)
+        if Q:
+            q_rows, cu_q = W.verify_queries(case, [Q] * B)
+            pt_o, _, _ = oracle.case_page_table(case)
+
+            def run_oracle():
+                oracle.verify_attention(q_rows, case.k_pages, case.v_pages, pt_o, case.seq_lens,
+                                        cu_q, num_kv_heads=Hkv, page_size=P, scale=case.scale,
+                                        kv_dtype=case.kv_dtype, k_scales=case.k_scales,
+                                        v_scales=case.v_scales)
+        else:
+            def run_oracle():
+                oracle.case_attention(case)
+        run_oracle()                          # untimed (page-in)
         ts = []
         for _ in range(max(1, args.cpu_reps)):
             t0 = time.perf_counter()
-            oracle.case_attention(case)
+            run_oracle()
             ts.append(time.perf_counter() - t0)
         t_med = float(np.median(ts))
+        what = f"{Q}-token decode" if Q else "decode-attention"
         cpu = {"value": round(nbytes / t_med / 1e9, 4), "unit": "GB/s", "cores": cores,
                "kind": "oracle",
-               "sample": f"whole {workload} decode-attention call (fp64 C oracle, OpenMP), "
+               "sample": f"whole {workload} {what} call (fp64 C oracle, OpenMP), "
                          f"median of {len(ts)} reps, {t_med * 1e6:.0f} us per call"}
 
     rec = {
-        "metric": "decode-attn us/call + achieved HBM GB/s (% of peak), B=32 ctx=8K",
+        "metric": ("decode-attn us/call + achieved HBM GB/s (% of peak), B=32 ctx=8K" if not Q else
+                   f"{Q}-token verify decode us/call + achieved HBM GB/s (% of peak)"),
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -396,12 +453,15 @@ def main() -> int:
                    "ragged": bool(np.any(case.seq_lens != case.seq_lens[0])),
                    "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D, "page_size": P,
                    "num_pages": case.num_pages, "num_splits": S, "kv_dtype": case.kv_dtype,
-                   "step": "page-table build + split-K decode attention (library defaults)"},
+                   "query_tokens_per_request": Q or 1,
+                   "step": ("page-table build + split-K decode attention (library defaults)"
+                            if not Q else "metadata build (page table, cu_seqlens_q) + "
+                            "multi-token split-K decode attention")},
         "us_per_call": round(attn_us_mean, 3),
         "pct_of_peak": round(100.0 * achieved / PEAK_HBM_GBS, 2),
         "graph_step_us": round(graph_step_us, 3),
         "graph_attn_us": round(graph_attn_us, 3),
-        "context_h200_graph_attn_us": H200_GRAPH_US.get(case.name),
+        "context_h200_graph_attn_us": None if Q else H200_GRAPH_US.get(case.name),
         "algorithmic_bytes": int(nbytes),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),

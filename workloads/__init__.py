@@ -345,3 +345,18 @@ def algorithmic_bytes(case: DecodeCase) -> int:
     qo = 2 * case.batch * case.num_q_heads * case.head_dim * 2
     lse = case.batch * case.num_q_heads * 4
     return kv + qo + lse + pages * 4 + case.batch * 4
+
+
+def verify_algorithmic_bytes(case: DecodeCase, q_lens) -> int:
+    """Bytes a multi-token decode call must move: K/V (+ scales) of exactly
+    the L_b tokens, the query rows, out (bf16) and lse (fp32) rows, the
+    page-table entries in use, seq_lens and cu_seqlens_q."""
+    q_lens = np.asarray(q_lens, dtype=np.int64)
+    P = case.page_size
+    toks = int(np.sum(case.seq_lens.astype(np.int64)))
+    pages = int(sum(-(-int(L) // P) for L in case.seq_lens))
+    rows = int(q_lens.sum())
+    kv = toks * case.kv_bytes_per_token()
+    qo = 2 * rows * case.num_q_heads * case.head_dim * 2
+    lse = rows * case.num_q_heads * 4
+    return kv + qo + lse + pages * 4 + case.batch * 4 + (case.batch + 1) * 4
