@@ -208,6 +208,10 @@ void decode_kernel(DecodeParams p,
     constexpr int D = kHeadDim, P = kPageSize;
     constexpr bool QUANT = KV != 0;        // 1-byte codes + scales, f16 arithmetic
     constexpr bool I8 = KV == 1;
+    // K/V are read once: bf16 streams them past the caches (measured 3%
+    // faster at batch 32 / 8K); 1-byte codes, whose kv blocks share an XCD,
+    // keep the default policy (streaming measured 3% slower there).
+    constexpr int KV_POLICY = QUANT ? 0 : kStreaming;
     const int lane = threadIdx.x & 63;
     // wave index is uniform per wave; say so, so that page ids, buffer
     // descriptors and loop bounds live in scalar registers
@@ -376,11 +380,11 @@ void decode_kernel(DecodeParams p,
             if constexpr (!QUANT) {
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
-                    kr[t][c] = buf_ld16(r, k_lane + 64 * c, 16 * t * row_bytes);
+                    kr[t][c] = buf_ld16<KV_POLICY>(r, k_lane + 64 * c, 16 * t * row_bytes);
             } else {
 #pragma unroll
                 for (int c2 = 0; c2 < 2; ++c2)
-                    kr8[t][c2] = buf_ld16(r, k_lane + 64 * c2, 16 * t * row_bytes);
+                    kr8[t][c2] = buf_ld16<KV_POLICY>(r, k_lane + 64 * c2, 16 * t * row_bytes);
             }
         }
         if constexpr (QUANT) {
@@ -397,9 +401,9 @@ void decode_kernel(DecodeParams p,
 #pragma unroll
         for (int i = 8 * half; i < 8 * half + 8; ++i) {
             if constexpr (!QUANT)
-                vr16[i] = buf_ld16(r, v_lane, 4 * i * row_bytes);
+                vr16[i] = buf_ld16<KV_POLICY>(r, v_lane, 4 * i * row_bytes);
             else
-                vr8[i] = buf_ld8(r, v_lane, 4 * i * row_bytes);
+                vr8[i] = buf_ld8<KV_POLICY>(r, v_lane, 4 * i * row_bytes);
         }
         if (QUANT && half == 1) {
             const auto rs = rsrc(p.v_scales, page, (int64_t)P * p.hkv, kvh, 4,

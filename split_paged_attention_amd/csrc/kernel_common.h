@@ -17,6 +17,8 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));   // store operand
 // Cache-policy immediate of buffer accesses for system-scope coherence
 // (sc0 sc1): stores write through to memory, loads bypass the caches.
 constexpr int kSysCoherent = 17;
+// Cache-policy immediate for data read once (nt, streaming).
+constexpr int kStreaming = 2;
 
 // Raw buffer loads, bit-cast to plain structs at once: reading lanes of the
 // builtins' vector results through a local vector variable was seen to

@@ -56,6 +56,9 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
     constexpr int D = kHeadDim, P = kPageSize, NW = kVerifyWaves;
     constexpr bool QUANT = KV != 0;
     constexpr bool I8 = KV == 1;
+    // Default cache policy for K/V (streaming them, which helps the bf16
+    // one-token decode, measured no gain here).
+    constexpr int KV_POLICY = 0;
     constexpr int ES = QUANT ? 1 : 2;            // bytes per element
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -194,11 +197,11 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
             if constexpr (!QUANT) {
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
-                    kr[t][c] = buf_ld16(r, k_lane + 64 * c, 16 * t * row_bytes);
+                    kr[t][c] = buf_ld16<KV_POLICY>(r, k_lane + 64 * c, 16 * t * row_bytes);
             } else {
 #pragma unroll
                 for (int c2 = 0; c2 < 2; ++c2)
-                    kr8[t][c2] = buf_ld16(r, k_lane + 64 * c2, 16 * t * row_bytes);
+                    kr8[t][c2] = buf_ld16<KV_POLICY>(r, k_lane + 64 * c2, 16 * t * row_bytes);
             }
         }
         if constexpr (QUANT) {
@@ -213,9 +216,9 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             if constexpr (!QUANT)
-                vr16[i] = buf_ld16(r, v_lane, 4 * i * row_bytes);
+                vr16[i] = buf_ld16<KV_POLICY>(r, v_lane, 4 * i * row_bytes);
             else
-                vr8[i] = buf_ld8(r, v_lane, 4 * i * row_bytes);
+                vr8[i] = buf_ld8<KV_POLICY>(r, v_lane, 4 * i * row_bytes);
         }
         if constexpr (QUANT) {
             const auto rs = rsrc(p.v_scales, page, (int64_t)P * p.hkv, kvh, 4,
