@@ -353,3 +353,35 @@ def test_hip_graph_replay_matches_eager():
         step()   # eager work between replays
         torch.cuda.synchronize()
     assert int(counters_view(ws, B, Hq, c.num_kv_heads, D, S).abs().sum()) == 0
+
+
+# ---------------------------------------------------------------- other batch and head shapes
+
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8"])
+@pytest.mark.parametrize("producer", PRODUCERS)
+@pytest.mark.parametrize("batch", [72, 100])
+def test_large_ragged_batches(batch, producer, kv):
+    """More than 64 requests (natural request order instead of longest
+    first); 72 is a multiple of 8 (request-major XCD placement for 1-byte
+    codes), 100 is not."""
+    lens = W._gen(batch, 99).integers(1, 2001, size=batch).tolist()
+    c = small_case(lens, kv=kv, S=8, seed=batch)
+    print(f"[case] batch {batch} ragged {kv} {producer}", flush=True)
+    out, lse = DevCase(c).attention(producer=producer)
+    o_ref, l_ref = oracle.case_attention(c)
+    compare_attention(out, lse, o_ref, l_ref, label=f"batch {batch} {kv} {producer}")
+
+
+@pytest.mark.parametrize("Hkv", [1, 2, 6, 16])
+@pytest.mark.parametrize("kv", ["bf16", "int8"])
+def test_other_kv_head_counts(Hkv, kv):
+    """Group size 4 with 1, 2, 6 or 16 kv heads (head-grouped needs an even
+    count; one kv head takes the page-split producer)."""
+    c = small_case([700, 64, 1500, 9], kv=kv, S=4, Hkv=Hkv)
+    print(f"[case] Hkv={Hkv} {kv}", flush=True)
+    d = DevCase(c)
+    o_ref, l_ref = oracle.case_attention(c)
+    for producer in (["page_split"] if Hkv % 2 else PRODUCERS):
+        for merge in ("fused", "separate"):
+            out, lse = d.attention(producer=producer, merge=merge)
+            compare_attention(out, lse, o_ref, l_ref, label=f"Hkv {Hkv} {kv} {producer} {merge}")

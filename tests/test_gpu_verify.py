@@ -111,3 +111,59 @@ def test_verify_single_token_rows_match_decode_within_tolerance():
     out, lse = run_verify(c, q_rows, cu, max_q_len=1)
     o_ref, l_ref = oracle_verify(c, q_rows, cu)
     compare_attention(out, lse, o_ref, l_ref, label="verify q1")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("batch", [72, 37])
+def test_verify_large_batches(batch, kv):
+    rng = W._gen(batch, 98)
+    lens = rng.integers(4, 1500, size=batch).tolist()
+    qlens = rng.integers(0, 5, size=batch).tolist()
+    c = small_case(lens, kv=kv, S=6, seed=batch)
+    q_rows, cu = W.verify_queries(c, qlens)
+    print(f"[case] verify batch {batch} {kv}", flush=True)
+    out, lse = run_verify(c, q_rows, cu)
+    o_ref, l_ref = oracle_verify(c, q_rows, cu)
+    compare_attention(out, lse, o_ref, l_ref, label=f"verify batch {batch} {kv}")
+
+
+def test_verify_graph_replay_matches_eager():
+    """Captured once, replayed with the query rows changed in place: every
+    replay equals an eager call on the same inputs, bit for bit."""
+    c = small_case([300, 1200, 64, 900], kv="bf16", S=4)
+    q_rows, cu = W.verify_queries(c, [4, 2, 3, 1])
+    d = DevCase(c)
+    q = bf16_dev(q_rows)
+    cu_d = torch.from_numpy(cu).cuda()
+    T = q.shape[0]
+    ws = torch.empty(spa.verify_workspace_bytes(T, 32, 8, 128, 4), dtype=torch.uint8, device="cuda")
+    out = torch.empty((T, 32, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, 32), dtype=torch.float32, device="cuda")
+
+    def call(o, l):
+        spa.paged_verify_attention(q, d.k, d.v, d.page_list, d.seq_lens, cu_d, 4, float(c.scale),
+                                   workspace=ws, out=o, lse=l)
+
+    print("[case] verify graph replay", flush=True)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call(out, lse)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(out, lse)
+    rng = np.random.default_rng(3)
+    for rep in range(3):
+        new = W.f32_to_bf16_bits(rng.standard_normal(q_rows.shape).astype(np.float32))
+        q.copy_(bf16_dev(new))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        o_g, l_g = out.clone(), lse.clone()
+        o_e = torch.empty_like(out)
+        l_e = torch.empty_like(lse)
+        call(o_e, l_e)
+        torch.cuda.synchronize()
+        assert torch.equal(o_g.view(torch.int16), o_e.view(torch.int16)) and torch.equal(l_g, l_e)
