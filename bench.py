@@ -293,6 +293,70 @@ def ablation(args) -> int:
     return 0
 
 
+def policy_sweep(args) -> int:
+    """Producer x merge choice across decode shapes (batch 1-32, context
+    1K-8K, 4/8/16 splits; 32 query / 8 KV heads, head_dim 128, 64-token pages
+    drawn at random from a 4096-page pool): microseconds per call from HIP
+    graphs of 10 calls each, for both producers with both merges and for the
+    library's default.  One JSON line; a progress line per shape on stderr."""
+    import itertools
+
+    import torch
+
+    import split_paged_attention_amd as spa
+    kv = args.policy_sweep
+    dev = "cuda:0"
+    g = torch.Generator(device=dev)
+    g.manual_seed(3)
+    P, Hq, Hkv, D, pool = 64, 32, 8, 128, 4096
+    if kv == "bf16":
+        k = torch.randn(pool, P, Hkv, D, device=dev, generator=g).to(torch.bfloat16)
+        ks = vs = None
+    else:
+        k = torch.randint(-127, 128, (pool, P, Hkv, D), device=dev, generator=g,
+                          dtype=torch.int8)
+        if kv == "fp8":
+            k = k.view(torch.uint8) & 0xF7   # finite e4m3 codes (no NaN pattern)
+        ks = torch.rand(pool, P, Hkv, device=dev, generator=g) * 0.02 + 0.001
+        vs = ks.clone()
+    v = k.clone()
+    variants = [("page_split", "fused"), ("page_split", "separate"),
+                ("head_grouped", "fused"), ("head_grouped", "separate"), (None, None)]
+    rows = []
+    for B, L, S in itertools.product([1, 2, 4, 8, 16, 32], [1024, 2048, 4096, 8192], [4, 8, 16]):
+        npg = B * (L // P)
+        q = torch.randn(B, Hq, D, device=dev, generator=g).to(torch.bfloat16)
+        pt = torch.randperm(pool, device=dev, generator=g)[:npg].to(torch.int32)
+        pt = pt.view(B, L // P).contiguous()
+        sl = torch.full((B,), L, dtype=torch.int32, device=dev)
+        ws = spa.new_workspace(B, Hq, Hkv, D, S, device=dev)
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+        us = []
+        for prod, merge in variants:
+            def call(i, prod=prod, merge=merge):
+                spa.paged_decode_attention(q, k, v, pt, sl, S, 0.0884, kv_dtype=kv,
+                                           k_scales=ks, v_scales=vs, workspace=ws, out=out,
+                                           lse=lse, producer=prod, merge=merge)
+
+            def ten(i, call=call):
+                for j in range(10):
+                    call(j)
+            us.append(time_graphs(capture(ten), 10) / 10)
+        best = min(range(4), key=lambda i: us[i])
+        rows.append({"batch": B, "context": L, "splits": S, "waves": B * Hkv * S,
+                     "page_split_fused_us": round(us[0], 2),
+                     "page_split_separate_us": round(us[1], 2),
+                     "head_grouped_fused_us": round(us[2], 2),
+                     "head_grouped_separate_us": round(us[3], 2),
+                     "default_us": round(us[4], 2),
+                     "best": "/".join(variants[best])})
+        print(f"[policy] {rows[-1]}", file=sys.stderr, flush=True)
+    print(json.dumps({"policy_sweep": kv, "unit": "us per call (graph replay)", "rows": rows}),
+          flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -311,6 +375,8 @@ def main() -> int:
     ap.add_argument("--ablation", action="store_true",
                     help="launch-gap ablation over workloads instead of the bench line")
     ap.add_argument("--ablation-configs", default="1,2,3,4,5")
+    ap.add_argument("--policy-sweep", choices=["bf16", "int8", "fp8"], default=None,
+                    help="time both producers and merges over a grid of decode shapes")
     ap.add_argument("--verify-qlen", type=int, default=0,
                     help="multi-token decode with this many query tokens per request (1..4)")
     args = ap.parse_args()
@@ -342,6 +408,8 @@ def main() -> int:
     spa.lib()  # fail loudly if the HIP library is missing
     if args.ablation:
         return ablation(args)
+    if args.policy_sweep:
+        return policy_sweep(args)
     t_gen = time.time()
     case = W.make_config(args.config)
     gen_s = time.time() - t_gen

@@ -218,22 +218,23 @@ spa_status spa_paged_decode_attention(const void *q, const void *k_pages, const 
     p.counters = reinterpret_cast<int32_t *>(ws + w.cnt_off);
     p.out = static_cast<uint16_t *>(out);
     p.lse = lse;
-    spa::DecodeMode mode = spa::default_mode(batch, num_kv_heads, num_splits);
+    const int kv_type = kv_dtype == SPA_KV_INT8  ? spa::kKvInt8
+                        : kv_dtype == SPA_KV_FP8 ? spa::kKvFp8
+                                                 : spa::kKvBf16;
+    spa::DecodeMode mode =
+        spa::default_mode(batch, num_kv_heads, num_splits, kv_type, page_table_stride);
     if (flags & SPA_DECODE_HEAD_GROUPED) mode = spa::DecodeMode::kHeadGrouped;
     if (flags & SPA_DECODE_PAGE_SPLIT) mode = spa::DecodeMode::kPageSplit;
     if (!spa::mode_supported(mode, num_kv_heads)) return SPA_ERR_UNSUPPORTED;
-    // Default merge: fused into the producer launch for page-split grids;
-    // a second launch after head-grouped grids, whose splits all finish
-    // together, so a merge inside the launch would run after every split.
-    bool fused = mode == spa::DecodeMode::kPageSplit;
+    // Default merge (measured): fused into the producer launch for
+    // page-split grids of up to 8 splits; a second launch for more splits,
+    // where the last arrival's merge of all of them sits on the critical
+    // path, and after head-grouped grids, whose splits all finish together.
+    bool fused = mode == spa::DecodeMode::kPageSplit && num_splits <= 8;
     if (flags & SPA_DECODE_SEPARATE_MERGE) fused = false;
     if (flags & SPA_DECODE_FUSED_MERGE) fused = true;
     return hip_status(
-        spa::launch_decode(p,
-                           kv_dtype == SPA_KV_INT8 ? spa::kKvInt8
-                           : kv_dtype == SPA_KV_FP8 ? spa::kKvFp8
-                                                    : spa::kKvBf16,
-                           mode, fused, stream));
+        spa::launch_decode(p, kv_type, mode, fused, stream));
 }
 
 size_t spa_verify_workspace_bytes(int32_t total_q, int32_t num_q_heads, int32_t num_kv_heads,

@@ -812,8 +812,16 @@ hipError_t launch_nw(const DecodeParams &p, bool fused, hipStream_t stream) {
 // waves, for grids too small to fill the GPU otherwise).
 constexpr int kNwHeadGrouped = 2;
 constexpr int kNwPageSplit = 4;
-// One wave per (request, kv head, split) fills 2 waves per SIMD from here on.
-constexpr int64_t kHeadGroupedMinWaves = 2048;
+// Producer choice, from a sweep over batch 1-32 x context 1K-8K x 4/8/16
+// splits (32 query / 8 kv heads).  bf16: head grouped from 512 (request,
+// kv head, split) triples up, page split below.  1-byte codes: a head-grouped
+// wave reads half the bytes per token, so it needs more of them in flight --
+// head grouped from 2048 triples, or from 1024 when a split spans at most 4
+// pages; page split otherwise.
+constexpr int64_t kHeadGroupedMinWaves = 512;
+constexpr int64_t kHeadGroupedMinWavesQuant = 2048;
+constexpr int64_t kHeadGroupedMinWavesQuantShort = 1024;
+constexpr int64_t kShortSplitPages = 4;
 
 template <int KV>
 hipError_t launch_kv(const DecodeParams &p, DecodeMode mode, bool fused, hipStream_t stream) {
@@ -836,10 +844,19 @@ hipError_t launch_decode(const DecodeParams &p, int kv_type, DecodeMode mode, bo
                               p.splits, p.out, p.lse, stream);
 }
 
-DecodeMode default_mode(int batch, int hkv, int splits) {
+DecodeMode default_mode(int batch, int hkv, int splits, int kv_type, int64_t pt_width) {
+    if (hkv % kNwHeadGrouped != 0) return DecodeMode::kPageSplit;
     const int64_t waves = (int64_t)batch * hkv * splits;
-    if (hkv % kNwHeadGrouped == 0 && waves >= kHeadGroupedMinWaves) return DecodeMode::kHeadGrouped;
-    return DecodeMode::kPageSplit;
+    bool grouped;
+    if (kv_type == kKvBf16) {
+        grouped = waves >= kHeadGroupedMinWaves;
+    } else {
+        // the page table's width bounds the pages of any request
+        const int64_t split_pages = (pt_width + splits - 1) / splits;
+        grouped = waves >= kHeadGroupedMinWavesQuant ||
+                  (waves >= kHeadGroupedMinWavesQuantShort && split_pages <= kShortSplitPages);
+    }
+    return grouped ? DecodeMode::kHeadGrouped : DecodeMode::kPageSplit;
 }
 
 bool mode_supported(DecodeMode mode, int hkv) {

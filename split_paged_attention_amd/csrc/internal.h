@@ -83,7 +83,7 @@ hipError_t launch_build_metadata(const MetadataParams &p, hipStream_t stream);
 // Producer workgroup shape (same arithmetic per split, different rounding of
 // the in-workgroup combination, so one shape always uses one mode).
 enum class DecodeMode { kPageSplit, kHeadGrouped };
-DecodeMode default_mode(int batch, int hkv, int splits);
+DecodeMode default_mode(int batch, int hkv, int splits, int kv_type, int64_t pt_width);
 bool mode_supported(DecodeMode mode, int hkv);
 
 // kv_type: kKvBf16, kKvInt8 or kKvFp8 pages.  fused: merge in the last
