@@ -208,14 +208,14 @@ void decode_kernel(DecodeParams p,
     constexpr int D = kHeadDim, P = kPageSize;
     constexpr bool QUANT = KV != 0;        // 1-byte codes + scales, f16 arithmetic
     constexpr bool I8 = KV == 1;
-    // bf16 head-grouped: K rows staged through LDS (see ktile); the page-split
+    // Head-grouped: K rows staged through LDS (see ktile); the page-split
     // producer of small grids loads K straight into operand registers, one
     // LDS round trip shorter per page.
-    constexpr bool KSTAGE = !QUANT && HG;
-    // K/V are read once: bf16 streams them past the caches (measured 3%
-    // faster at batch 32 / 8K); 1-byte codes, whose kv blocks share an XCD,
-    // keep the default policy (streaming measured 3% slower there).
-    constexpr int KV_POLICY = QUANT ? 0 : kStreaming;
+    constexpr bool KSTAGE = HG;
+    // K/V are read once, so they stream past the caches (non-temporal
+    // loads: a plain paged read of the same layout runs 12% faster so, and
+    // the producer 3% (bf16) to 12% (1-byte codes) at batch 32 / 8K).
+    constexpr int KV_POLICY = kStreaming;
     const int lane = threadIdx.x & 63;
     // wave index is uniform per wave; say so, so that page ids, buffer
     // descriptors and loop bounds live in scalar registers
@@ -343,13 +343,14 @@ void decode_kernel(DecodeParams p,
     __shared__ uint32_t pbuf[NW][8][4][4];          // [wave][pair u][phase r][head]
     __shared__ float sm_m[NW][4], sm_l[NW][4];
     __shared__ float sm_acc[HG ? 1 : NW][4][D];     // page split: waves' states
-    // bf16 head-grouped: the page's K rows, staged per wave: loaded as whole
-    // 256-byte rows (4 rows per load instruction, which memory serves about
-    // 6% faster than 16 rows x 64 bytes) and read back in the matrix-core
-    // operand layout; rows padded by 16 bytes so the 16 token rows of an
-    // operand read fall in different LDS banks.
-    constexpr int KROW = D + 8;
-    __shared__ __attribute__((aligned(16))) uint16_t ktile[KSTAGE ? NW : 1][KSTAGE ? P : 1][KROW];
+    // Head-grouped: the page's K rows, staged per wave: loaded as whole rows
+    // (bf16: 4 rows of 256 bytes per load instruction, which memory serves
+    // about 6% faster than 16 rows x 64 bytes; 1-byte codes: 8 rows of 128
+    // bytes) and read back in the matrix-core operand layout; rows padded by
+    // 16 bytes so the 16 token rows of an operand read fall in different LDS
+    // banks.
+    constexpr int KROWB = D * (QUANT ? 1 : 2) + 16;   // bytes per staged row
+    __shared__ __attribute__((aligned(16))) uint8_t ktile[KSTAGE ? NW : 1][KSTAGE ? P : 1][KROWB];
     __shared__ int sm_last;
 
     const int32_t *pt_row = page_table + (int64_t)b * p.pt_stride;
@@ -366,16 +367,20 @@ void decode_kernel(DecodeParams p,
     const int row_bytes = row_stride * ES;
     const int k_lane = (n * row_stride + (QUANT ? 16 : 8) * g) * ES;   // byte offsets in a page
     const int v_lane = (vr * row_stride + 8 * vc) * ES;
+    // staged 1-byte K: lane l loads 16 bytes of token row l / 8 of each 8-row
+    // block, at byte 16 (l % 8)
+    const int k8_row = lane >> 3, k8_col = 16 * (lane & 7);
     // A loop iteration handles one page of this wave's page sequence (two
     // pages per iteration for 1-byte codes measured slower: 256 registers).
     uint4 kr[4][4];          // bf16 K (staged: kr[i/4][i%4] = token 4i + vr, dims 8vc ..)
     uint4 vr16[16];          // bf16 V
     uint4 kr8[4][2];         // int8 / e4m3 K codes: [t][c/2], 16 per lane
+                             // (staged: kr8[i/2][i%2] = token 8i + l/8, bytes 16 (l%8) ..)
     uint2 vr8[16];           // int8 / e4m3 V codes
     // Scales of a page: lane l holds token l's (one load per page and
     // tensor); lane (n, g) fetches token 16t + n's with a lane permute when
     // it needs it.  e4m3 value scales are stored times 256.
-    float ksc_tok, vsc_tok;
+    float ksc_tok, vsc_tok, vsc_next;
     const int s_lane64 = lane * p.hkv * 4;
     auto rsrc = [&](const void *base, int64_t page, int64_t elem_per_page, int64_t elem_off,
                     int esize, int nbytes) {
@@ -383,15 +388,26 @@ void decode_kernel(DecodeParams p,
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(ptr), (short)0, nbytes,
                                                  kBufferWord3);
     };
+    auto load_k_scales = [&](int64_t page, int valid_rows) {
+        const auto rs = rsrc(p.k_scales, page, (int64_t)P * p.hkv, kvh, 4, valid_rows * p.hkv * 4);
+        ksc_tok = buf_ldf(rs, s_lane64, 0);
+    };
+    // K codes (and, unstaged, the key scales: staged K is requested before
+    // the current page's scores use the current scales)
     auto load_k = [&](int64_t page, int valid_rows) {
         const auto r = rsrc(p.k_pages, page, (int64_t)P * row_stride, (int64_t)kvh * D, ES,
                             valid_rows * row_bytes);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            if constexpr (KSTAGE) {
+            if constexpr (KSTAGE && !QUANT) {
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
                     kr[t][c] = buf_ld16<KV_POLICY>(r, v_lane, 4 * (4 * t + c) * row_bytes);
+            } else if constexpr (KSTAGE) {
+#pragma unroll
+                for (int c2 = 0; c2 < 2; ++c2)
+                    kr8[t][c2] = buf_ld16<KV_POLICY>(
+                        r, k8_row * row_bytes + k8_col, 8 * (2 * t + c2) * row_bytes);
             } else if constexpr (!QUANT) {
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
@@ -402,11 +418,7 @@ void decode_kernel(DecodeParams p,
                     kr8[t][c2] = buf_ld16<KV_POLICY>(r, k_lane + 64 * c2, 16 * t * row_bytes);
             }
         }
-        if constexpr (QUANT) {
-            const auto rs = rsrc(p.k_scales, page, (int64_t)P * p.hkv, kvh, 4,
-                                 valid_rows * p.hkv * 4);
-            ksc_tok = buf_ldf(rs, s_lane64, 0);
-        }
+        if constexpr (QUANT && !KSTAGE) load_k_scales(page, valid_rows);
     };
     // V in two halves (tokens 0..31, 32..63): P.V consumes the first half's
     // registers first, so the next page's first half can be requested early.
@@ -420,11 +432,12 @@ void decode_kernel(DecodeParams p,
             else
                 vr8[i] = buf_ld8<KV_POLICY>(r, v_lane, 4 * i * row_bytes);
         }
-        if (QUANT && half == 1) {
-            const auto rs = rsrc(p.v_scales, page, (int64_t)P * p.hkv, kvh, 4,
-                                 valid_rows * p.hkv * 4);
-            vsc_tok = buf_ldf(rs, s_lane64, 0) * (I8 ? 1.f : kF8ValueScale);
-        }
+    };
+    // value scales of a page, requested a whole page ahead (with the next
+    // page's K) into vsc_next; vsc_tok takes them at the end of an iteration
+    auto load_v_scales = [&](int64_t page, int valid_rows) {
+        const auto rs = rsrc(p.v_scales, page, (int64_t)P * p.hkv, kvh, 4, valid_rows * p.hkv * 4);
+        vsc_next = buf_ldf(rs, s_lane64, 0);
     };
 
     // Software pipeline over this wave's pages: the next page's K loads are
@@ -449,8 +462,13 @@ void decode_kernel(DecodeParams p,
         int64_t page;
         const int rows = page_rows(pg, page);
         load_k(page, rows);
+        if constexpr (QUANT && KSTAGE) load_k_scales(page, rows);
         load_v_half(page, rows, 0);
         load_v_half(page, rows, 1);
+        if constexpr (QUANT) {
+            load_v_scales(page, rows);
+            vsc_tok = vsc_next * (I8 ? 1.f : kF8ValueScale);
+        }
     }
     for (; pg < pg1; pg += PSTEP) {
         int64_t page_next;
@@ -462,22 +480,40 @@ void decode_kernel(DecodeParams p,
         if constexpr (KSTAGE) {
             // K rows into the wave's LDS tile; the registers then take the
             // next page's K at once
-            uint16_t(*kt)[KROW] = ktile[wave];
+            uint8_t(*kt)[KROWB] = ktile[wave];
+            if constexpr (!QUANT) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-                *reinterpret_cast<uint4 *>(&kt[4 * i + vr][8 * vc]) = kr[i >> 2][i & 3];
+                for (int i = 0; i < 16; ++i)
+                    *reinterpret_cast<uint4 *>(&kt[4 * i + vr][16 * vc]) = kr[i >> 2][i & 3];
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    *reinterpret_cast<uint4 *>(&kt[8 * i + k8_row][k8_col]) = kr8[i >> 1][i & 1];
+            }
             __asm__ volatile("" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
             load_k(page_next, valid_next);
+            if constexpr (QUANT) load_v_scales(page_next, valid_next);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 sacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                if constexpr (!QUANT) {
 #pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        qa[c], *reinterpret_cast<const bf16x8_t *>(&kt[16 * t + n][32 * c + 8 * g]),
-                        sacc[t], 0, 0, 0);
+                    for (int c = 0; c < 4; ++c)
+                        sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            qa[c],
+                            *reinterpret_cast<const bf16x8_t *>(&kt[16 * t + n][64 * c + 16 * g]),
+                            sacc[t], 0, 0, 0);
+                } else {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const uint2 h = *reinterpret_cast<const uint2 *>(
+                            &kt[16 * t + n][64 * (c >> 1) + 16 * g + 8 * (c & 1)]);
+                        sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            qa16[c], I8 ? i8x8_to_f16(h) : e4m3x8_to_f16(h), sacc[t], 0, 0, 0);
+                    }
+                }
             }
         } else if constexpr (!QUANT) {
 #pragma unroll
@@ -516,6 +552,12 @@ void decode_kernel(DecodeParams p,
             // keep the prefetch after the last read of the K registers it reuses
             __builtin_amdgcn_sched_barrier(0);
             load_k(page_next, valid_next);
+            if constexpr (QUANT) load_v_scales(page_next, valid_next);
+            __builtin_amdgcn_sched_barrier(0);
+        } else if constexpr (QUANT) {
+            // the scores have read this page's key scales
+            __builtin_amdgcn_sched_barrier(0);
+            load_k_scales(page_next, valid_next);
             __builtin_amdgcn_sched_barrier(0);
         }
 
@@ -634,6 +676,7 @@ void decode_kernel(DecodeParams p,
         __builtin_amdgcn_sched_barrier(0);
         load_v_half(page_next, valid_next, 1);
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (QUANT) vsc_tok = vsc_next * (I8 ? 1.f : kF8ValueScale);
     }
     if constexpr (I8) {
         // remove the 1152 bias carried by every f16 value code
