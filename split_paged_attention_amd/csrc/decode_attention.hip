@@ -200,6 +200,9 @@ __device__ __forceinline__ void st_sys(float *p, float v) {
 //             NW waves read the same token rows of the same pages together.
 // KV: 0 = bf16 pages, 1 = int8 codes, 2 = e4m3 codes (1 and 2 with fp32
 // scales per token and kv head).
+// One stashed split state: 4 heads x D accumulators, then 4 maxima and 4 sums.
+constexpr int kStashFloats = kGroup * kHeadDim + 2 * kGroup;
+
 template <int KV, int NW, bool FUSED, bool HG>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_kernel(DecodeParams p,
@@ -234,6 +237,14 @@ void decode_kernel(DecodeParams p,
     // batch 32 / 8K, 2% slower for bf16).  Otherwise the S splits of a group
     // share an XCD.
     const int S = p.splits;
+    // A head-grouped workgroup with the separate merge walks `walk`
+    // consecutive splits (S a multiple of it), one page pipeline across the
+    // split boundaries, writing each split's state as it completes: grids
+    // larger than the GPU's resident workgroups then run in one round, and
+    // the later splits skip the workgroup start (request ranking, page-id
+    // and first-page latency).  Each split's arithmetic is unchanged.
+    const int walk = (HG && !FUSED && p.split_walk > 1) ? p.split_walk : 1;
+    const int SG = S / walk;                        // split groups per kv group
     const int kv_per_grp = HG ? NW : 1;             // kv heads per workgroup
     const int grp_per_b = p.hkv / kv_per_grp;
     const int ngroups = p.batch * grp_per_b;
@@ -242,16 +253,17 @@ void decode_kernel(DecodeParams p,
         const int bid = blockIdx.x;
         const int xcd = bid & 7, slot = bid >> 3;
         if (QUANT && (p.batch & 7) == 0) {
-            j = slot % S;
-            const int rest = slot / S;
+            j = slot % SG;
+            const int rest = slot / SG;
             grp = ((rest / grp_per_b) * 8 + xcd) * grp_per_b + rest % grp_per_b;
         } else if ((ngroups & 7) == 0) {
-            grp = (slot / S) * 8 + xcd;
-            j = slot % S;
+            grp = (slot / SG) * 8 + xcd;
+            j = slot % SG;
         } else {
-            grp = bid / S;
-            j = bid % S;
+            grp = bid / SG;
+            j = bid % SG;
         }
+        j *= walk;                                  // first split of this workgroup
     }
     // Requests are taken longest first (rank r = r-th longest, ties by
     // index), so that in a ragged batch the long splits start early instead
@@ -284,7 +296,13 @@ void decode_kernel(DecodeParams p,
     const int pages = (L + P - 1) / P;
     const int pps = (pages + S - 1) / S;
     const int pg0 = min(j * pps, pages);
-    const int pg1 = min(pg0 + pps, pages);
+    const int pg1 = min(j * pps + walk * pps, pages);   // end of this workgroup's pages
+    int jcur = j;                                        // split being accumulated
+    int split_end = min(pg0 + pps, pages);               // its end page
+    // Head-grouped walks: states of completed splits before the last, per
+    // wave (walk - 1) x kStashFloats floats of dynamic LDS.
+    extern __shared__ __attribute__((aligned(16))) float stash[];
+    int nstash = 0;
     const int row_stride = p.hkv * D;           // elements between consecutive token rows
 
     // A operand: row i of the MFMA is query head (kvh*4 + (i & 3)).  The
@@ -438,6 +456,67 @@ void decode_kernel(DecodeParams p,
     auto load_v_scales = [&](int64_t page, int valid_rows) {
         const auto rs = rsrc(p.v_scales, page, (int64_t)P * p.hkv, kvh, 4, valid_rows * p.hkv * 4);
         vsc_next = buf_ldf(rs, s_lane64, 0);
+    };
+
+    // Partial-state writes: write-through stores in the fused mode (read back
+    // by another workgroup in this launch), plain stores otherwise.
+    auto put = [&](float *ptr, float v) {
+        if constexpr (FUSED) st_sys(ptr, v);
+        else *ptr = v;
+    };
+    // Wave state of a finished split: the int8 value bias removed, l summed
+    // over the 16 lanes of a row, acc over the 4 token phases.
+    auto reduce_state = [&]() {
+        if constexpr (I8) {
+            // remove the 1152 bias carried by every f16 value code
+#pragma unroll
+            for (int h = 0; h < 4; ++h)
+#pragma unroll
+                for (int d = 0; d < 8; ++d) acc[h][d] = __builtin_fmaf(-kI8Bias, psum[h], acc[h][d]);
+        }
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            lpart[h] = row_sum16(lpart[h]);
+#pragma unroll
+            for (int d = 0; d < 8; ++d) {
+                float x = acc[h][d];
+                x += __shfl_xor(x, 16);
+                x += __shfl_xor(x, 32);
+                acc[h][d] = x;
+            }
+        }
+    };
+    auto reset_state = [&]() {
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            m[h] = kNegInf;
+            lpart[h] = 0.f;
+            psum[h] = 0.f;
+#pragma unroll
+            for (int d = 0; d < 8; ++d) acc[h][d] = 0.f;
+        }
+    };
+    // Head-grouped: the reduced state of this wave's kv head as split jw's
+    // partial state.
+    // Head-grouped: the empty state (no tokens) as split jw's partial state.
+    auto store_empty = [&](int jw) {
+        const int64_t idx0 = ((int64_t)b * p.hq + kvh * kGroup) * S + jw;
+        const int off = (vr * S * D + 8 * vc) * 4;   // bytes from this wave's first row
+        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+        if constexpr (FUSED) {
+            const auto r = __builtin_amdgcn_make_buffer_rsrc(p.part_acc + idx0 * D, (short)0,
+                                                             (3 * S + 1) * D * 4, kBufferWord3);
+            buf_st16<kSysCoherent>(z, r, off);
+            buf_st16<kSysCoherent>(z, r, off + 16);
+        } else {
+            char *base = reinterpret_cast<char *>(p.part_acc + idx0 * D) + off;
+            *reinterpret_cast<uint4 *>(base) = z;
+            *reinterpret_cast<uint4 *>(base + 16) = z;
+        }
+        if (lane < 4) {
+            put(p.part_max + idx0 + (int64_t)lane * S, kNegInf);
+            put(p.part_sum + idx0 + (int64_t)lane * S, 0.f);
+        }
     };
 
     // Software pipeline over this wave's pages: the next page's K loads are
@@ -677,66 +756,92 @@ void decode_kernel(DecodeParams p,
         load_v_half(page_next, valid_next, 1);
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (QUANT) vsc_tok = vsc_next * (I8 ? 1.f : kF8ValueScale);
-    }
-    if constexpr (I8) {
-        // remove the 1152 bias carried by every f16 value code
+        if constexpr (HG) {
+            if (pg + 1 == split_end) {
+                // split jcur complete: write its state (a split before the
+                // workgroup's last goes to the LDS stash, written out after
+                // the loop: stores between the page loads measured 5 us per
+                // split boundary), start the next one
+                reduce_state();
+                if (!FUSED && pg + 1 < pg1) {
+                    float *st = stash + (wave * (walk - 1) + nstash) * kStashFloats;
+                    float v8[8];
 #pragma unroll
-        for (int h = 0; h < 4; ++h)
+                    for (int d = 0; d < 8; ++d)
+                        v8[d] = vr == 0 ? acc[0][d] : vr == 1 ? acc[1][d] : vr == 2 ? acc[2][d] : acc[3][d];
+                    *reinterpret_cast<float4 *>(st + vr * D + 8 * vc) =
+                        make_float4(v8[0], v8[1], v8[2], v8[3]);
+                    *reinterpret_cast<float4 *>(st + vr * D + 8 * vc + 4) =
+                        make_float4(v8[4], v8[5], v8[6], v8[7]);
+                    if (lane == 0) {
 #pragma unroll
-            for (int d = 0; d < 8; ++d) acc[h][d] = __builtin_fmaf(-kI8Bias, psum[h], acc[h][d]);
-    }
-
-    // ---- wave epilogue: l over the 16 lanes of a row; acc over the 4 token phases
+                        for (int h = 0; h < 4; ++h) {
+                            st[4 * D + h] = m[h];
+                            st[4 * D + 4 + h] = lpart[h];
+                        }
+                    }
+                    ++nstash;
+                } else
+                {
+                    const int jw = jcur;
+                    // One wave = one kv head: write its split state straight from
+                    // registers.  After the butterfly every lane holds the reduced sums
+                    // for its 8 dims, so lane group r publishes head r: two 16-byte
+                    // stores per lane cover the wave's 4 heads x 128 dims.
+                    const int64_t idx0 = ((int64_t)b * p.hq + kvh * kGroup) * S + jw;
+                    float v8[8];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-        lpart[h] = row_sum16(lpart[h]);
+                    for (int d = 0; d < 8; ++d)
+                        v8[d] = vr == 0 ? acc[0][d] : vr == 1 ? acc[1][d] : vr == 2 ? acc[2][d] : acc[3][d];
+                    const uint4 lo = make_uint4(__float_as_uint(v8[0]), __float_as_uint(v8[1]),
+                                                __float_as_uint(v8[2]), __float_as_uint(v8[3]));
+                    const uint4 hi = make_uint4(__float_as_uint(v8[4]), __float_as_uint(v8[5]),
+                                                __float_as_uint(v8[6]), __float_as_uint(v8[7]));
+                    const int off = (vr * S * D + 8 * vc) * 4;   // bytes from this wave's first row
+                    if constexpr (FUSED) {
+                        const auto r = __builtin_amdgcn_make_buffer_rsrc(p.part_acc + idx0 * D, (short)0,
+                                                                         (3 * S + 1) * D * 4, kBufferWord3);
+                        buf_st16<kSysCoherent>(lo, r, off);
+                        buf_st16<kSysCoherent>(hi, r, off + 16);
+                    } else {
+                        char *base = reinterpret_cast<char *>(p.part_acc + idx0 * D) + off;
+                        *reinterpret_cast<uint4 *>(base) = lo;
+                        *reinterpret_cast<uint4 *>(base + 16) = hi;
+                    }
+                    if (lane == 0) {
 #pragma unroll
-        for (int d = 0; d < 8; ++d) {
-            float x = acc[h][d];
-            x += __shfl_xor(x, 16);
-            x += __shfl_xor(x, 32);
-            acc[h][d] = x;
+                        for (int h = 0; h < 4; ++h) {
+                            put(p.part_max + idx0 + (int64_t)h * S, m[h] == kNegInf ? kNegInf : m[h] * kLn2);
+                            put(p.part_sum + idx0 + (int64_t)h * S, lpart[h]);
+                        }
+                    }
+                }
+                reset_state();
+                ++jcur;
+                split_end = min(split_end + pps, pages);
+            }
         }
     }
-    // Partial-state writes: write-through stores in the fused mode (read back
-    // by another workgroup in this launch), plain stores otherwise.
-    auto put = [&](float *ptr, float v) {
-        if constexpr (FUSED) st_sys(ptr, v);
-        else *ptr = v;
-    };
     if constexpr (HG) {
-        // One wave = one kv head: write its split state straight from
-        // registers.  After the butterfly every lane holds the reduced sums
-        // for its 8 dims, so lane group r publishes head r: two 16-byte
-        // stores per lane cover the wave's 4 heads x 128 dims.
-        const int64_t idx0 = ((int64_t)b * p.hq + kvh * kGroup) * S + j;
-        float v8[8];
-#pragma unroll
-        for (int d = 0; d < 8; ++d)
-            v8[d] = vr == 0 ? acc[0][d] : vr == 1 ? acc[1][d] : vr == 2 ? acc[2][d] : acc[3][d];
-        const uint4 lo = make_uint4(__float_as_uint(v8[0]), __float_as_uint(v8[1]),
-                                    __float_as_uint(v8[2]), __float_as_uint(v8[3]));
-        const uint4 hi = make_uint4(__float_as_uint(v8[4]), __float_as_uint(v8[5]),
-                                    __float_as_uint(v8[6]), __float_as_uint(v8[7]));
-        const int off = (vr * S * D + 8 * vc) * 4;   // bytes from this wave's first row
-        if constexpr (FUSED) {
-            const auto r = __builtin_amdgcn_make_buffer_rsrc(p.part_acc + idx0 * D, (short)0,
-                                                             (3 * S + 1) * D * 4, kBufferWord3);
-            buf_st16<kSysCoherent>(lo, r, off);
-            buf_st16<kSysCoherent>(hi, r, off + 16);
-        } else {
-            char *base = reinterpret_cast<char *>(p.part_acc + idx0 * D) + off;
-            *reinterpret_cast<uint4 *>(base) = lo;
-            *reinterpret_cast<uint4 *>(base + 16) = hi;
-        }
-        if (lane == 0) {
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-                put(p.part_max + idx0 + (int64_t)h * S, m[h] == kNegInf ? kNegInf : m[h] * kLn2);
-                put(p.part_sum + idx0 + (int64_t)h * S, lpart[h]);
+        // splits of this workgroup with no pages (past the context): empty
+        // states (the others were written at their last page)
+        for (int jw = jcur; jw < j + walk; ++jw) store_empty(jw);
+        // the stashed splits j .. j + nstash - 1 (separate merge only)
+        for (int k = 0; k < (FUSED ? 0 : nstash); ++k) {
+            const float *st = stash + (wave * (walk - 1) + k) * kStashFloats;
+            const int64_t idx0 = ((int64_t)b * p.hq + kvh * kGroup) * S + j + k;
+            char *base = reinterpret_cast<char *>(p.part_acc + idx0 * D) + (vr * S * D + 8 * vc) * 4;
+            *reinterpret_cast<float4 *>(base) = *reinterpret_cast<const float4 *>(st + vr * D + 8 * vc);
+            *reinterpret_cast<float4 *>(base + 16) =
+                *reinterpret_cast<const float4 *>(st + vr * D + 8 * vc + 4);
+            if (lane < 4) {
+                const float mk = st[4 * D + lane];
+                p.part_max[idx0 + (int64_t)lane * S] = mk == kNegInf ? kNegInf : mk * kLn2;
+                p.part_sum[idx0 + (int64_t)lane * S] = st[4 * D + 4 + lane];
             }
         }
     } else {
+        reduce_state();
         if (lane == 0) {
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
@@ -834,16 +939,74 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t *__restrict__ p
         ptr[i] = 0u;
 }
 
+// A device attribute of the current device (cached per device), or
+// fallback if it cannot be read.
+template <hipDeviceAttribute_t ATTR>
+int device_attr(int fallback) {
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return fallback;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, ATTR, dev) != hipSuccess || n <= 0) n = fallback;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+int cu_count() { return device_attr<hipDeviceAttributeMultiprocessorCount>(256); }
+
+// Splits one bf16 head-grouped workgroup walks (separate merge), from a
+// sweep over batch 8-32 x context 1K-8K x 4/8/16 splits: fewer, longer page
+// streams read faster.  Walks first cut the grid to one round of resident
+// workgroups (4 per CU); splits of at least 4 pages then walk on down to one
+// workgroup per CU (batch 32 / 8K / 16 splits: 187 us with one split per
+// workgroup, 168 us walking 8); shorter splits stop at one round, their
+// boundaries costing more than the longer streams save.  1-byte codes walk
+// one split: their waves move half the bytes per page and lose with fewer
+// of them.
+constexpr int kMaxSplitWalk = 8;
+constexpr int kLongSplitPages = 4;
+int split_walk_for(const DecodeParams &p, bool quant, int nw) {
+    if (quant) return 1;
+    const int64_t wgs = (int64_t)p.batch * (p.hkv / nw) * p.splits;
+    const int64_t split_pages = (p.pt_stride + p.splits - 1) / p.splits;   // bound from the table
+    const int64_t cus = cu_count();
+    int w = 1;
+    auto can_double = [&] { return 2 * w <= kMaxSplitWalk && p.splits % (2 * w) == 0; };
+    while (can_double() && wgs / w > 4 * cus) w *= 2;
+    while (can_double() && split_pages >= kLongSplitPages && wgs / (2 * w) >= cus) w *= 2;
+    return w;
+}
+
 template <int KV, int NW, bool HG>
-hipError_t launch_nw(const DecodeParams &p, bool fused, hipStream_t stream) {
+hipError_t launch_nw(const DecodeParams &p_in, bool fused, hipStream_t stream) {
+    DecodeParams p = p_in;
+    p.split_walk = (HG && !fused) ? split_walk_for(p, KV != 0, NW) : 1;
+    if (p.split_walk > 1) {
+        // the stash must fit beside the kernel's static LDS
+        static const size_t static_lds = [] {
+            hipFuncAttributes a{};
+            return hipFuncGetAttributes(&a, reinterpret_cast<const void *>(
+                                                &decode_kernel<KV, NW, false, HG>)) == hipSuccess
+                       ? a.sharedSizeBytes
+                       : (size_t)65536;
+        }();
+        const size_t max_lds =
+            (size_t)device_attr<hipDeviceAttributeMaxSharedMemoryPerBlock>(65536);
+        while (p.split_walk > 1 &&
+               static_lds + (size_t)NW * (p.split_walk - 1) * kStashFloats * sizeof(float) > max_lds)
+            p.split_walk /= 2;
+    }
     const int kv_per_grp = HG ? NW : 1;
-    const unsigned grid = (unsigned)(p.batch * (p.hkv / kv_per_grp) * p.splits);
+    const unsigned grid = (unsigned)(p.batch * (p.hkv / kv_per_grp) * (p.splits / p.split_walk));
+    // LDS stash for the states of all but the last split of a walk
+    const size_t stash_bytes = (size_t)NW * (p.split_walk - 1) * kStashFloats * sizeof(float);
     if (fused)
         hipLaunchKernelGGL((decode_kernel<KV, NW, true, HG>), dim3(grid), dim3(NW * 64), 0, stream,
                            p, p.page_table, p.seq_lens);
     else
-        hipLaunchKernelGGL((decode_kernel<KV, NW, false, HG>), dim3(grid), dim3(NW * 64), 0, stream,
-                           p, p.page_table, p.seq_lens);
+        hipLaunchKernelGGL((decode_kernel<KV, NW, false, HG>), dim3(grid), dim3(NW * 64),
+                           (unsigned)stash_bytes, stream, p, p.page_table, p.seq_lens);
     return hipGetLastError();
 }
 
@@ -859,12 +1022,12 @@ constexpr int kNwPageSplit = 4;
 // splits (32 query / 8 kv heads).  bf16: head grouped from 512 (request,
 // kv head, split) triples up, page split below.  1-byte codes: a head-grouped
 // wave reads half the bytes per token, so it needs more of them in flight --
-// head grouped from 2048 triples, or from 1024 when a split spans at most 4
+// head grouped from 2048 triples, or from 1024 when a split spans at most 16
 // pages; page split otherwise.
 constexpr int64_t kHeadGroupedMinWaves = 512;
 constexpr int64_t kHeadGroupedMinWavesQuant = 2048;
 constexpr int64_t kHeadGroupedMinWavesQuantShort = 1024;
-constexpr int64_t kShortSplitPages = 4;
+constexpr int64_t kShortSplitPages = 16;
 
 template <int KV>
 hipError_t launch_kv(const DecodeParams &p, DecodeMode mode, bool fused, hipStream_t stream) {

@@ -372,6 +372,28 @@ def test_large_ragged_batches(batch, producer, kv):
     compare_attention(out, lse, o_ref, l_ref, label=f"batch {batch} {kv} {producer}")
 
 
+@pytest.mark.parametrize("S", [16, 8])
+def test_split_walk_ragged(S):
+    """bf16 head-grouped grids large enough that a workgroup walks several
+    consecutive splits (states of all but the last kept in LDS until the
+    workgroup ends): ragged lengths with empty requests, exact page
+    multiples and splits past the context inside a walk.  Checked against
+    the oracle, and bit-exactly against the fused launch, whose workgroups
+    take one split each."""
+    rng = W._gen(64, 7)
+    lens = rng.integers(1, 4097, size=64)
+    lens[:8] = [0, 1, 63, 64, 65, 4096, 4095, 129]
+    c = small_case(lens.tolist(), kv="bf16", S=S, seed=64 + S)
+    print(f"[case] split walk S={S} batch 64 ragged", flush=True)
+    d = DevCase(c)
+    o_ref, l_ref = oracle.case_attention(c)
+    o1, l1 = d.attention(producer="head_grouped", merge="separate")
+    compare_attention(o1, l1, o_ref, l_ref, label=f"walk S={S}")
+    o2, l2 = d.attention(producer="head_grouped", merge="fused")
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
 @pytest.mark.parametrize("Hkv", [1, 2, 6, 16])
 @pytest.mark.parametrize("kv", ["bf16", "int8"])
 def test_other_kv_head_counts(Hkv, kv):
