@@ -939,6 +939,39 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t *__restrict__ p
         ptr[i] = 0u;
 }
 
+template <int KV, int NW, bool HG>
+hipError_t launch_nw(const DecodeParams &p_in, bool fused, hipStream_t stream) {
+    DecodeParams p = p_in;
+    p.split_walk = (HG && !fused) ? split_walk_for(p, KV != 0, NW) : 1;
+    if (p.split_walk > 1) {
+        // the stash must fit beside the kernel's static LDS
+        static const size_t static_lds = [] {
+            hipFuncAttributes a{};
+            return hipFuncGetAttributes(&a, reinterpret_cast<const void *>(
+                                                &decode_kernel<KV, NW, false, HG>)) == hipSuccess
+                       ? a.sharedSizeBytes
+                       : (size_t)65536;
+        }();
+        const size_t max_lds = max_lds_per_block();
+        while (p.split_walk > 1 &&
+               static_lds + (size_t)NW * (p.split_walk - 1) * kStashFloats * sizeof(float) > max_lds)
+            p.split_walk /= 2;
+    }
+    const int kv_per_grp = HG ? NW : 1;
+    const unsigned grid = (unsigned)(p.batch * (p.hkv / kv_per_grp) * (p.splits / p.split_walk));
+    // LDS stash for the states of all but the last split of a walk
+    const size_t stash_bytes = (size_t)NW * (p.split_walk - 1) * kStashFloats * sizeof(float);
+    if (fused)
+        hipLaunchKernelGGL((decode_kernel<KV, NW, true, HG>), dim3(grid), dim3(NW * 64), 0, stream,
+                           p, p.page_table, p.seq_lens);
+    else
+        hipLaunchKernelGGL((decode_kernel<KV, NW, false, HG>), dim3(grid), dim3(NW * 64),
+                           (unsigned)stash_bytes, stream, p, p.page_table, p.seq_lens);
+    return hipGetLastError();
+}
+
+}  // namespace
+
 // A device attribute of the current device (cached per device), or
 // fallback if it cannot be read.
 template <hipDeviceAttribute_t ATTR>
@@ -954,6 +987,9 @@ int device_attr(int fallback) {
     return cached[dev];
 }
 int cu_count() { return device_attr<hipDeviceAttributeMultiprocessorCount>(256); }
+size_t max_lds_per_block() {
+    return (size_t)device_attr<hipDeviceAttributeMaxSharedMemoryPerBlock>(65536);
+}
 
 // Splits one bf16 head-grouped workgroup walks (separate merge), from a
 // sweep over batch 8-32 x context 1K-8K x 4/8/16 splits: fewer, longer page
@@ -978,39 +1014,6 @@ int split_walk_for(const DecodeParams &p, bool quant, int nw) {
     return w;
 }
 
-template <int KV, int NW, bool HG>
-hipError_t launch_nw(const DecodeParams &p_in, bool fused, hipStream_t stream) {
-    DecodeParams p = p_in;
-    p.split_walk = (HG && !fused) ? split_walk_for(p, KV != 0, NW) : 1;
-    if (p.split_walk > 1) {
-        // the stash must fit beside the kernel's static LDS
-        static const size_t static_lds = [] {
-            hipFuncAttributes a{};
-            return hipFuncGetAttributes(&a, reinterpret_cast<const void *>(
-                                                &decode_kernel<KV, NW, false, HG>)) == hipSuccess
-                       ? a.sharedSizeBytes
-                       : (size_t)65536;
-        }();
-        const size_t max_lds =
-            (size_t)device_attr<hipDeviceAttributeMaxSharedMemoryPerBlock>(65536);
-        while (p.split_walk > 1 &&
-               static_lds + (size_t)NW * (p.split_walk - 1) * kStashFloats * sizeof(float) > max_lds)
-            p.split_walk /= 2;
-    }
-    const int kv_per_grp = HG ? NW : 1;
-    const unsigned grid = (unsigned)(p.batch * (p.hkv / kv_per_grp) * (p.splits / p.split_walk));
-    // LDS stash for the states of all but the last split of a walk
-    const size_t stash_bytes = (size_t)NW * (p.split_walk - 1) * kStashFloats * sizeof(float);
-    if (fused)
-        hipLaunchKernelGGL((decode_kernel<KV, NW, true, HG>), dim3(grid), dim3(NW * 64), 0, stream,
-                           p, p.page_table, p.seq_lens);
-    else
-        hipLaunchKernelGGL((decode_kernel<KV, NW, false, HG>), dim3(grid), dim3(NW * 64),
-                           (unsigned)stash_bytes, stream, p, p.page_table, p.seq_lens);
-    return hipGetLastError();
-}
-
-}  // namespace
 
 // Producer shapes.  Head-grouped: 2 kv heads per workgroup, each wave walks
 // all pages of its split (long per-wave streams, row-aligned reads).

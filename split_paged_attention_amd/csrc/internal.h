@@ -85,6 +85,10 @@ hipError_t launch_build_metadata(const MetadataParams &p, hipStream_t stream);
 // the in-workgroup combination, so one shape always uses one mode).
 enum class DecodeMode { kPageSplit, kHeadGrouped };
 DecodeMode default_mode(int batch, int hkv, int splits, int kv_type, int64_t pt_width);
+// Splits one head-grouped workgroup walks (bf16 only; 1 for 1-byte codes),
+// and the device's LDS limit per workgroup.
+int split_walk_for(const DecodeParams &p, bool quant, int nw);
+size_t max_lds_per_block();
 bool mode_supported(DecodeMode mode, int hkv);
 
 // kv_type: kKvBf16, kKvInt8 or kKvFp8 pages.  fused: merge in the last

@@ -30,6 +30,9 @@ namespace spa {
 namespace {
 
 constexpr int kVerifyWaves = 2;   // kv heads per workgroup, one per wave
+// One stashed split state of a wave: 32 accumulators per lane (64 lanes),
+// then the 16 rows' maxima and sums.
+constexpr int kVerifyStashFloats = 32 * 64 + 32;
 
 // Transposed LDS read of 4 16-bit elements (see the addressing in the kernel).
 __device__ __forceinline__ uint64_t tr_read(const uint16_t *p) {
@@ -72,6 +75,12 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
     // a multiple of 8, all kv blocks and splits of a request share an XCD;
     // otherwise the S splits of a group do when the group count allows.
     const int S = p.splits;
+    // bf16: a workgroup may walk `walk` consecutive splits (S a multiple of
+    // it) with one page pipeline, as the one-token decode does: the states
+    // of all but the last wait in dynamic LDS until the workgroup ends, each
+    // split's arithmetic unchanged.
+    const int walk = (!QUANT && p.split_walk > 1) ? p.split_walk : 1;
+    const int SG = S / walk;
     const int grp_per_b = p.hkv / NW;
     const int ngroups = p.batch * grp_per_b;
     int grp, j;
@@ -79,16 +88,17 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
         const int bid = blockIdx.x;
         const int xcd = bid & 7, slot = bid >> 3;
         if (QUANT && (p.batch & 7) == 0) {
-            j = slot % S;
-            const int rest = slot / S;
+            j = slot % SG;
+            const int rest = slot / SG;
             grp = ((rest / grp_per_b) * 8 + xcd) * grp_per_b + rest % grp_per_b;
         } else if ((ngroups & 7) == 0) {
-            grp = (slot / S) * 8 + xcd;
-            j = slot % S;
+            grp = (slot / SG) * 8 + xcd;
+            j = slot % SG;
         } else {
-            grp = bid / S;
-            j = bid % S;
+            grp = bid / SG;
+            j = bid % SG;
         }
+        j *= walk;                                  // first split of this workgroup
     }
     const int b = grp / grp_per_b;
     const int kvh = (grp - b * grp_per_b) * NW + wave;
@@ -105,7 +115,11 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
     const int pages = (L + P - 1) / P;
     const int pps = (pages + S - 1) / S;
     const int pg0 = min(j * pps, pages);
-    const int pg1 = min(pg0 + pps, pages);
+    const int pg1 = min(j * pps + walk * pps, pages);   // end of this workgroup's pages
+    int jcur = j;                                        // split being accumulated
+    int split_end = min(pg0 + pps, pages);               // its end page
+    extern __shared__ __attribute__((aligned(16))) float vstash[];
+    int nstash = 0;
     const int row_stride = p.hkv * D;
     const int vis = L - nq + g + 1;             // query token g sees tokens < vis
 
@@ -161,9 +175,10 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
 #pragma unroll
     for (int blk = 0; blk < 8; ++blk) acc[blk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // Per-wave LDS tiles, 16-bit elements, token-major: V[64 tokens][128
-    // dims] (bf16, or f16 values of the codes) and P[64 tokens][16 rows].
-    __shared__ __attribute__((aligned(16))) uint16_t vbuf[NW][P][D];
+    // Per-wave LDS tiles, 16-bit elements, token-major: half a page of V
+    // (32 tokens x 128 dims, bf16 or the f16 values of the codes; the two
+    // halves take turns) and P[64 tokens][16 rows].
+    __shared__ __attribute__((aligned(16))) uint16_t vbuf[NW][P / 2][D];
     __shared__ __attribute__((aligned(16))) uint16_t pbuf[NW][P][16];
     uint16_t(*vt)[D] = vbuf[wave];
     uint16_t(*pt16)[16] = pbuf[wave];
@@ -210,17 +225,17 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
             ksc_tok = buf_ldf(rs, s_lane64, 0);
         }
     };
-    auto load_v = [&](int64_t page, int valid_rows) {
+    auto load_v = [&](int64_t page, int valid_rows, int half) {
         const auto r = rsrc(p.v_pages, page, (int64_t)P * row_stride, (int64_t)kvh * D, ES,
                             valid_rows * row_bytes);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 8 * half; i < 8 * half + 8; ++i) {
             if constexpr (!QUANT)
                 vr16[i] = buf_ld16<KV_POLICY>(r, v_lane, 4 * i * row_bytes);
             else
                 vr8[i] = buf_ld8<KV_POLICY>(r, v_lane, 4 * i * row_bytes);
         }
-        if constexpr (QUANT) {
+        if (QUANT && half == 0) {
             const auto rs = rsrc(p.v_scales, page, (int64_t)P * p.hkv, kvh, 4,
                                  valid_rows * p.hkv * 4);
             vsc_tok = buf_ldf(rs, s_lane64, 0) * (I8 ? 1.f : kF8ValueScale);
@@ -237,22 +252,10 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
         return ok ? min(P, L - i * P) : 0;
     };
 
-    int pg = pg0;
-    if (pg < pg1) {
-        int64_t page;
-        const int rows = page_rows(pg, page);
-        load_k(page, rows);
-        load_v(page, rows);
-    }
-    for (; pg < pg1; ++pg) {
-        int64_t page_next;
-        const int valid_next = page_rows(pg + 1, page_next);
-        const int valid = min(P, L - pg * P);
-
-        // ---- this page's V into LDS (token 4i + g, dims 8n ..); its registers
-        // then take the next page's V
+    // V rows 32 half .. 32 half + 31 of the page into the half-page tile
+    auto put_v_half = [&](int half) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 8 * half; i < 8 * half + 8; ++i) {
             uint4 w;
             if constexpr (!QUANT) {
                 w = vr16[i];
@@ -270,11 +273,29 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
                                                      c.y, 1.f / kF8ValueScale, true)));
             }
-            *reinterpret_cast<uint4 *>(&vt[4 * i + g][8 * n]) = w;
+            *reinterpret_cast<uint4 *>(&vt[4 * (i - 8 * half) + g][8 * n]) = w;
         }
+    };
+
+    int pg = pg0;
+    if (pg < pg1) {
+        int64_t page;
+        const int rows = page_rows(pg, page);
+        load_k(page, rows);
+        load_v(page, rows, 0);
+        load_v(page, rows, 1);
+    }
+    for (; pg < pg1; ++pg) {
+        int64_t page_next;
+        const int valid_next = page_rows(pg + 1, page_next);
+        const int valid = min(P, L - pg * P);
+
+        // ---- the first half of this page's V into the LDS tile (token 4i + g,
+        // dims 8n ..); its registers then take the next page's first half
+        put_v_half(0);
         const float vsc_cur = vsc_tok;
         __builtin_amdgcn_sched_barrier(0);
-        load_v(page_next, valid_next);
+        load_v(page_next, valid_next, 0);
         __builtin_amdgcn_sched_barrier(0);
 
         // ---- S = Q K^T: lane (n, g) gets s[token g, head h][KV token 16t + n]
@@ -355,13 +376,24 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
         }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
+            if (kb == 1) {
+                // the first half's reads are issued (LDS ops of a wave run in
+                // order): the second half takes the tile, and its registers
+                // the next page's second half
+                __asm__ volatile("" ::: "memory");
+                put_v_half(1);
+                __asm__ volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+                load_v(page_next, valid_next, 1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
             const int r0 = 32 * kb + tr_row;
             const uint64_t a_lo = tr_read(&pt16[r0][tr_col]);
             const uint64_t a_hi = tr_read(&pt16[r0 + 4][tr_col]);
 #pragma unroll
             for (int blk = 0; blk < 8; ++blk) {
-                const uint64_t b_lo = tr_read(&vt[r0][16 * blk + tr_col]);
-                const uint64_t b_hi = tr_read(&vt[r0 + 4][16 * blk + tr_col]);
+                const uint64_t b_lo = tr_read(&vt[tr_row][16 * blk + tr_col]);
+                const uint64_t b_hi = tr_read(&vt[tr_row + 4][16 * blk + tr_col]);
                 if constexpr (!QUANT)
                     acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                         join_bf16x8(a_lo, a_hi), join_bf16x8(b_lo, b_hi), acc[blk], 0, 0, 0);
@@ -372,12 +404,34 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
         }
         // the next page's V overwrites the tile only after these reads
         __asm__ volatile("" ::: "memory");
+        if (!QUANT && pg + 1 == split_end && pg + 1 < pg1) {
+            // split jcur complete and not this workgroup's last: its state
+            // into the LDS stash, then start the next one
+            float *st = vstash + (wave * (walk - 1) + nstash) * kVerifyStashFloats;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const float l = row_sum16(lpart[h]);
+#pragma unroll
+                for (int blk = 0; blk < 8; ++blk) st[(blk * 4 + h) * 64 + lane] = acc[blk][h];
+                if (n == 0) {
+                    st[32 * 64 + 4 * g + h] = m[h];
+                    st[32 * 64 + 16 + 4 * g + h] = l;
+                }
+                m[h] = kNegInf;
+                lpart[h] = 0.f;
+            }
+#pragma unroll
+            for (int blk = 0; blk < 8; ++blk) acc[blk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            ++nstash;
+            ++jcur;
+            split_end = min(split_end + pps, pages);
+        }
     }
     // ---- partial state of query token g: l over the 16 lanes of its group
 #pragma unroll
     for (int h = 0; h < 4; ++h) lpart[h] = row_sum16(lpart[h]);
     if (g < nq) {
-        const int64_t row0 = ((int64_t)(q0 + g) * p.hq + kvh * kGroup) * S + j;
+        const int64_t row0 = ((int64_t)(q0 + g) * p.hq + kvh * kGroup) * S + jcur;
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
             const int64_t idx = row0 + (int64_t)h * S;
@@ -390,13 +444,66 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
             }
         }
     }
+    if (g < nq) {
+        // splits of this workgroup past the context: empty states
+        for (int jw = jcur + 1; jw < j + walk; ++jw) {
+            const int64_t row0 = ((int64_t)(q0 + g) * p.hq + kvh * kGroup) * S + jw;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const int64_t idx = row0 + (int64_t)h * S;
+                float *dst = p.part_acc + idx * D + n;
+#pragma unroll
+                for (int blk = 0; blk < 8; ++blk) dst[16 * blk] = 0.f;
+                if (n == 0) {
+                    p.part_max[idx] = kNegInf;
+                    p.part_sum[idx] = 0.f;
+                }
+            }
+        }
+        // the stashed splits j .. j + nstash - 1
+        for (int k = 0; k < nstash; ++k) {
+            const float *st = vstash + (wave * (walk - 1) + k) * kVerifyStashFloats;
+            const int64_t row0 = ((int64_t)(q0 + g) * p.hq + kvh * kGroup) * S + j + k;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const int64_t idx = row0 + (int64_t)h * S;
+                float *dst = p.part_acc + idx * D + n;
+#pragma unroll
+                for (int blk = 0; blk < 8; ++blk) dst[16 * blk] = st[(blk * 4 + h) * 64 + lane];
+                if (n == 0) {
+                    const float mk = st[32 * 64 + 4 * g + h];
+                    p.part_max[idx] = mk == kNegInf ? kNegInf : mk * kLn2;
+                    p.part_sum[idx] = st[32 * 64 + 16 + 4 * g + h];
+                }
+            }
+        }
+    }
 }
 
 template <int KV>
-hipError_t launch_verify_kv(const DecodeParams &p, hipStream_t stream) {
-    const unsigned grid = (unsigned)(p.batch * (p.hkv / kVerifyWaves) * p.splits);
-    hipLaunchKernelGGL((verify_kernel<KV>), dim3(grid), dim3(kVerifyWaves * 64), 0, stream, p,
-                       p.page_table, p.seq_lens, p.cu_seqlens_q);
+hipError_t launch_verify_kv(const DecodeParams &p_in, hipStream_t stream) {
+    DecodeParams p = p_in;
+    p.split_walk = split_walk_for(p, KV != 0, kVerifyWaves);
+    if (p.split_walk > 1) {
+        // the stash must fit beside the kernel's static LDS
+        static const size_t static_lds = [] {
+            hipFuncAttributes a{};
+            return hipFuncGetAttributes(&a, reinterpret_cast<const void *>(&verify_kernel<KV>)) ==
+                           hipSuccess
+                       ? a.sharedSizeBytes
+                       : (size_t)65536;
+        }();
+        const size_t max_lds = max_lds_per_block();
+        while (p.split_walk > 1 && static_lds + (size_t)kVerifyWaves * (p.split_walk - 1) *
+                                                     kVerifyStashFloats * sizeof(float) > max_lds)
+            p.split_walk /= 2;
+    }
+    const unsigned grid =
+        (unsigned)(p.batch * (p.hkv / kVerifyWaves) * (p.splits / p.split_walk));
+    const size_t stash_bytes =
+        (size_t)kVerifyWaves * (p.split_walk - 1) * kVerifyStashFloats * sizeof(float);
+    hipLaunchKernelGGL((verify_kernel<KV>), dim3(grid), dim3(kVerifyWaves * 64),
+                       (unsigned)stash_bytes, stream, p, p.page_table, p.seq_lens, p.cu_seqlens_q);
     return hipGetLastError();
 }
 

@@ -127,6 +127,26 @@ def test_verify_large_batches(batch, kv):
     compare_attention(out, lse, o_ref, l_ref, label=f"verify batch {batch} {kv}")
 
 
+@pytest.mark.parametrize("S", [16, 8])
+def test_verify_split_walk_ragged(S):
+    """bf16 grids large enough that a workgroup walks several consecutive
+    splits (states of all but the last held in LDS until the workgroup
+    ends): 64 ragged requests with 0-4 query rows, an empty context, exact
+    page multiples and splits past the context inside a walk."""
+    rng = W._gen(64, 11)
+    lens = rng.integers(4, 4097, size=64)
+    lens[:6] = [4, 64, 65, 4096, 4095, 129]
+    qlens = rng.integers(0, 5, size=64)
+    qlens[:4] = [4, 0, 1, 4]
+    qlens = np.minimum(qlens, lens).tolist()
+    c = small_case(lens.tolist(), kv="bf16", S=S, seed=80 + S)
+    q_rows, cu = W.verify_queries(c, qlens)
+    print(f"[case] verify split walk S={S} batch 64 ragged", flush=True)
+    out, lse = run_verify(c, q_rows, cu)
+    o_ref, l_ref = oracle_verify(c, q_rows, cu)
+    compare_attention(out, lse, o_ref, l_ref, label=f"verify walk S={S}")
+
+
 def test_verify_graph_replay_matches_eager():
     """Captured once, replayed with the query rows changed in place: every
     replay equals an eager call on the same inputs, bit for bit."""
