@@ -6,7 +6,10 @@
  * with hipMalloc, or a PyTorch tensor's data pointer) unless stated
  * otherwise; every size is in elements unless stated otherwise.  The caller
  * owns every buffer, the workspace included; the library allocates nothing
- * and keeps no state between calls.  All calls are asynchronous on the
+ * and keeps no state between calls beyond a per-thread last-HIP-error code
+ * and a read-only cache of device properties (compute units and LDS per
+ * workgroup of each device, the kernels' static LDS), filled on first use
+ * and used to size launches.  All calls are asynchronous on the
  * given stream, perform no host synchronisation and no memset, and may be
  * captured into a HIP graph.
  *
@@ -198,14 +201,19 @@ spa_status spa_workspace_reset(void *workspace, size_t bytes, hipStream_t stream
  * by log-sum-exp in split order, either inside the producer launch by the
  * last split workgroup to arrive, or by a second launch -- same arithmetic,
  * bit-identical output.  With flags == 0 the library picks the producer
- * shape from batch * num_kv_heads * num_splits (the same sizes always give
- * the same choice, so results are reproducible) and the merge placement that
- * is faster for it.  L == 0 gives out = 0 and lse = -inf.  Contradictory
- * flags (both merges, both producers) are SPA_ERR_INVALID_ARGUMENT.
+ * shape from batch, num_kv_heads, num_splits, kv_dtype and
+ * page_table_stride (the same sizes always give the same choice, so results
+ * are reproducible) and the merge placement that is faster for it; a bf16
+ * head-grouped workgroup with the separate merge may also take several
+ * consecutive splits, sized from the device's compute units (the per-split
+ * arithmetic, and so the result, is unchanged).  L == 0 gives out = 0 and
+ * lse = -inf.  Contradictory flags (both merges, both producers) are
+ * SPA_ERR_INVALID_ARGUMENT.
  *
  * Supported: head_dim 128, page_size 64, num_q_heads == 4 * num_kv_heads,
- * kv_dtype bf16, int8 or fp8, 1 <= num_splits <= 1024 (SPA_DECODE_HEAD_GROUPED
- * also needs an even num_kv_heads); otherwise SPA_ERR_UNSUPPORTED.  workspace: spa_decode_workspace_bytes(...) bytes,
+ * kv_dtype bf16, int8 or fp8, 1 <= num_splits <= 1024
+ * (SPA_DECODE_HEAD_GROUPED also needs an even num_kv_heads); otherwise
+ * SPA_ERR_UNSUPPORTED.  workspace: spa_decode_workspace_bytes(...) bytes,
  * 16-byte aligned, zeroed before first use (see spa_workspace_reset);
  * concurrent calls must not share a workspace.  batch == 0 returns SPA_OK
  * without launching.
@@ -242,7 +250,8 @@ size_t spa_verify_workspace_bytes(int32_t total_q, int32_t num_q_heads, int32_t 
  *   s_t = scale * q[row, h, :] . k_t,  query head h reads kv head h / 4;
  * a row that sees no token gets out = 0 and lse = -inf.  Split-K as in
  * spa_paged_decode_attention (same page partition, split states merged in
- * split order by a second launch).
+ * split order by a second launch; with bf16 KV a workgroup may take several
+ * consecutive splits, which leaves the result unchanged).
  *
  *   q           [total_q, num_q_heads, head_dim] bf16, contiguous, 16-byte aligned
  *   cu_seqlens_q [batch + 1] int32 (device), non-decreasing, cu[0] >= 0,
