@@ -412,11 +412,13 @@ void decode_kernel(DecodeParams p,
     };
     // K codes (and, unstaged, the key scales: staged K is requested before
     // the current page's scores use the current scales)
-    auto load_k = [&](int64_t page, int valid_rows) {
+    // (rows 16 t0 .. 16 t1 - 1 of the page: staged K goes out in two halves)
+    auto load_k = [&](int64_t page, int valid_rows, int t0 = 0, int t1 = 4) {
         const auto r = rsrc(p.k_pages, page, (int64_t)P * row_stride, (int64_t)kvh * D, ES,
                             valid_rows * row_bytes);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
+            if (t < t0 || t >= t1) continue;
             if constexpr (KSTAGE && !QUANT) {
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
@@ -571,7 +573,7 @@ void decode_kernel(DecodeParams p,
             }
             __asm__ volatile("" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
-            load_k(page_next, valid_next);
+            load_k(page_next, valid_next, 0, 2);
             if constexpr (QUANT) load_v_scales(page_next, valid_next);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -640,6 +642,13 @@ void decode_kernel(DecodeParams p,
             __builtin_amdgcn_sched_barrier(0);
         }
 
+        if constexpr (KSTAGE) {
+            // the next page's K rows 32..63 (rows 0..31 went out with the tile
+            // write): spread over the page, the requests measured 1% faster
+            __builtin_amdgcn_sched_barrier(0);
+            load_k(page_next, valid_next, 2, 4);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         // ---- online softmax (base 2)
         float alpha[4], pv[4][4];
 #pragma unroll
