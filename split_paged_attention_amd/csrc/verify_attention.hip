@@ -90,7 +90,12 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
         if (QUANT && (p.batch & 7) == 0) {
             j = slot % SG;
             const int rest = slot / SG;
-            grp = ((rest / grp_per_b) * 8 + xcd) * grp_per_b + rest % grp_per_b;
+            // ranks dealt to the XCDs in serpentine order (0..7, then 7..0,
+            // ...), so each XCD's share of a ragged batch sums to about the
+            // same length
+            const int row = rest / grp_per_b;
+            const int rank = row * 8 + ((row & 1) ? 7 - xcd : xcd);
+            grp = rank * grp_per_b + rest % grp_per_b;
         } else if ((ngroups & 7) == 0) {
             grp = (slot / SG) * 8 + xcd;
             j = slot % SG;
