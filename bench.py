@@ -111,7 +111,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, out_path: str, copy_mib: int, 
     rec["write_scale"] = wscale
     total = 0.0
     producer = ("verify", "verify_kernel") if kind == "verify" else ("decode", "decode_kernel")
-    for short, pat in (producer, ("split_merge", "split_merge_kernel"),
+    for short, pat in (producer, ("split_merge", "split_merge"),
                        ("metadata", "build_metadata_kernel")):
         f = _per_dispatch(fr, "FETCH_SIZE", lambda k, pat=pat: pat in k)
         w = _per_dispatch(wr, "WRITE_SIZE", lambda k, pat=pat: pat in k)
