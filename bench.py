@@ -2,16 +2,19 @@
 
 One step = the whole hot path on one batch: the page table / cache_seqlens /
 cu_seqlens_k build (one launch) followed by one split-K paged-attention decode
-call with the library's default choices (producer plus log-sum-exp merge; at
-the default workload the head-grouped producer and a second, merge launch).
+with the library's default choices (producer plus log-sum-exp merge).  Where
+the default plan is two launches (at the default workload: the head-grouped
+producer, then the merge), the step makes them through the producer entry
+point and the merge entry point, which launch exactly those kernels.
 Default workload: batch 32, context 8192, 32 query / 8 KV heads, head_dim 128,
 bf16 K/V in 64-token pages scattered over a 4096-page pool, 16 splits --
 lmdeploy's headline H200 shape.
 
 Timing: W untimed warm-up steps, then exactly K steps between two device
 synchronisations; HIP events on the launch stream bracket every attention
-call, giving its average duration (both launches of the call, and the gap
-between them, fall inside).  Two copies of the KV pool alternate so that
+call (both launches and the gap between them fall inside) and, for a
+two-launch plan, the producer launch alone: the roofline figure is the
+algorithmic bytes over the producer's average duration.  Two copies of the KV pool alternate so that
 consecutive steps do not read the same addresses.  A HIP-graph replay of the
 step is timed as well (the pages quote CUDA-graph latency).  The fp64 CPU
 oracle is timed on the host beside it.
@@ -53,9 +56,10 @@ def _source_hash(kind: str) -> str:
     return h.hexdigest()
 
 
-def _traffic_for(kind: str, workload: str):
-    """HBM bytes per call from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources; else None."""
+def _traffic_for(kind: str, workload: str, producer_only: bool = False):
+    """HBM bytes per call (or per producer launch) from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel sources;
+    else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -63,6 +67,9 @@ def _traffic_for(kind: str, workload: str):
         rec = json.load(open(path))
         if rec.get("kernel_source_sha256") != _source_hash(kind):
             return None
+        if producer_only:
+            k = rec["kernels"]["verify" if kind == "verify" else "decode"]
+            return int(k["fetch_bytes"]) + int(k["write_bytes"])
         return int(rec["hbm_bytes_per_launch"])
     except Exception:
         return None
@@ -130,6 +137,89 @@ def summarize_pmc(fetch_dir: str, write_dir: str, out_path: str, copy_mib: int, 
     return rec
 
 
+def summarize_trace(trace_dir: str, warmup: int, steps: int) -> dict:
+    """Per-kernel durations from a rocprofv3 --kernel-trace run of this bench:
+    the average over the K timed steps (decode dispatches warmup ..
+    warmup + steps - 1, in start order) and over all dispatches."""
+    import csv
+    import glob
+    import statistics
+    rows = []
+    for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    out = {}
+    for short, pat in (("producer", "decode_kernel"), ("verify_producer", "verify_kernel"),
+                       ("split_merge", "split_merge_kernel"),
+                       ("metadata", "build_metadata_kernel")):
+        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+             for r in rows if pat in r["Kernel_Name"]]
+        if not d:
+            continue
+        names = sorted(set(r["Kernel_Name"] for r in rows if pat in r["Kernel_Name"]))
+        timed = d[warmup:warmup + steps] if short != "metadata" else d[1 + warmup:1 + warmup + steps]
+        out[short] = {"kernel": names, "dispatches": len(d),
+                      "timed_steps_avg_us": round(statistics.mean(timed), 3) if timed else None,
+                      "all_avg_us": round(statistics.mean(d), 3)}
+    return out
+
+
+class HipEvents:
+    """Timing events of the HIP runtime torch has loaded, created with
+    hipEventDisableSystemFence: recording one then costs no system-scope cache
+    writeback and invalidation, which with torch's default events slowed the
+    next kernel (the producer by about 5% at batch 32 / 8K).  Elapsed times
+    are read only after a device synchronisation."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        path = None
+        with open("/proc/self/maps") as fh:
+            for line in fh:
+                if "libamdhip64.so" in line:
+                    path = line.split()[-1]
+                    break
+        if path is None:
+            raise RuntimeError("the HIP runtime is not loaded (import torch and use the GPU first)")
+        self.ct = ctypes
+        self.hip = ctypes.CDLL(path)
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.events = []
+
+    def new(self):
+        ev = self.ct.c_void_p()
+        rc = self.hip.hipEventCreateWithFlags(self.ct.byref(ev), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        self.events.append(ev)
+        return ev
+
+    def record(self, ev):
+        import torch
+        rc = self.hip.hipEventRecord(ev, self.ct.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def ms(self, a, b) -> float:
+        f = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(f), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(f.value)
+
+    def close(self):
+        for ev in self.events:
+            self.hip.hipEventDestroy(ev)
+        self.events = []
+
+
 class Rig:
     """Device copies of one workload and the calls of one step on them."""
 
@@ -184,6 +274,16 @@ class Rig:
         self.spa = spa
         self.merge = None
         self.producer = None
+        # one-token decode with a two-launch default plan: the step can run
+        # the producer and the merge as two entry points (same kernels as
+        # the one call), so that events can bracket the producer alone
+        self.two_launch = (not qlen and spa.decode_default_flags(
+            B, case.num_kv_heads, S, case.kv_dtype, case.max_seq_pages)
+            & spa.SPA_DECODE_SEPARATE_MERGE) != 0
+        if self.two_launch:
+            self.p_acc = torch.empty((B, Hq, S, D), dtype=torch.float32, device=dev)
+            self.p_max = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+            self.p_sum = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
         self.k1()                     # attention reads the page table this builds
         torch.cuda.synchronize()
 
@@ -215,6 +315,20 @@ class Rig:
                                         producer=self.producer)
 
 
+    def producer_pass(self, i):
+        """spa_paged_decode_partials: the producer launch of a two-launch call."""
+        c = self.case
+        k, v, ks, vs = self.copies[i % 2]
+        self.spa.paged_decode_partials(self.q, k, v, self.pt, self.sl, c.num_splits,
+                                       float(c.scale), kv_dtype=c.kv_dtype, k_scales=ks,
+                                       v_scales=vs, partial_acc=self.p_acc,
+                                       partial_max=self.p_max, partial_sum=self.p_sum)
+
+    def merge_pass(self):
+        """spa_split_merge over the producer's split states."""
+        self.spa.split_merge(self.p_acc, self.p_max, self.p_sum, out=self.out, lse=self.lse)
+
+
 def capture(fn):
     """Two HIP graphs of fn(0) and fn(1), after a warm-up on a side stream."""
     import torch
@@ -234,10 +348,12 @@ def capture(fn):
     return gl
 
 
-def time_graphs(gl, R):
-    """Microseconds per replay over R back-to-back replays between two events."""
+def time_graphs(gl, R, warm=200):
+    """Microseconds per replay over R back-to-back replays between two events,
+    after `warm` untimed replays (the clocks settle after about 10 ms of
+    sustained work)."""
     import torch
-    for i in range(20):
+    for i in range(warm):
         gl[i % 2].replay()
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -249,7 +365,7 @@ def time_graphs(gl, R):
     return a.elapsed_time(b) * 1e3 / R
 
 
-def time_eager(fn, K, warmup=10):
+def time_eager(fn, K, warmup=200):
     """Per-call microseconds (mean, median) from events around each of K calls."""
     import numpy as np
     import torch
@@ -342,7 +458,7 @@ def policy_sweep(args) -> int:
             def ten(i, call=call):
                 for j in range(10):
                     call(j)
-            us.append(time_graphs(capture(ten), 10) / 10)
+            us.append(time_graphs(capture(ten), 10, warm=20) / 10)
         best = min(range(4), key=lambda i: us[i])
         rows.append({"batch": B, "context": L, "splits": S, "waves": B * Hkv * S,
                      "page_split_fused_us": round(us[0], 2),
@@ -360,8 +476,11 @@ def policy_sweep(args) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed steps first: the GPU clocks settle after about 10 ms of "
+                         "sustained work (durations rise about 12%% after an idle period, "
+                         "then recover)")
     ap.add_argument("--config", type=int, default=4, help="workload 1..5 (4 = headline)")
     ap.add_argument("--graph-replays", type=int, default=200)
     ap.add_argument("--cpu-reps", type=int, default=3)
@@ -370,6 +489,9 @@ def main() -> int:
                     help="after timing, run device copies of this size (counter scaling)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs into a traffic record and exit")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR", default=None,
+                    help="per-kernel averages over the timed steps of a rocprofv3 "
+                         "--kernel-trace run of this bench (same --steps/--warmup), then exit")
     ap.add_argument("--pmc-out", default=None)
     ap.add_argument("--pmc-commands", nargs="*", default=[])
     ap.add_argument("--ablation", action="store_true",
@@ -380,6 +502,11 @@ def main() -> int:
     ap.add_argument("--verify-qlen", type=int, default=0,
                     help="multi-token decode with this many query tokens per request (1..4)")
     args = ap.parse_args()
+
+    if args.summarize_trace:
+        print(json.dumps(summarize_trace(args.summarize_trace, args.warmup, args.steps)),
+              flush=True)
+        return 0
 
     if args.summarize_pmc:
         import workloads as W
@@ -423,30 +550,49 @@ def main() -> int:
     Hkv, P = case.num_kv_heads, case.page_size
     k1, attn = rig.k1, rig.attn
 
-    for i in range(args.warmup):
+    # One step: the metadata build, then the decode call.  Where the
+    # library's default plan is two launches (producer, then merge), the step
+    # makes them as the two entry points that launch exactly those kernels,
+    # and an event between them times the producer -- the dominant kernel --
+    # on its own; otherwise the call is one launch and its events time it.
+    two = rig.two_launch
+
+    hev = HipEvents()
+
+    def step(i, ev=None):
         k1()
-        attn(i)
+        if ev is not None:
+            hev.record(ev[0])
+        if two:
+            rig.producer_pass(i)
+            if ev is not None:
+                hev.record(ev[1])
+            rig.merge_pass()
+        else:
+            attn(i)
+        if ev is not None:
+            hev.record(ev[2])
+
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
 
     K = args.steps
-    ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    evs = [[hev.new() for _ in range(3)] for _ in range(K)]
+    t_start, t_end = hev.new(), hev.new()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    t_start.record()
+    hev.record(t_start)
     for i in range(K):
-        k1()
-        ev_s[i].record()
-        attn(i)
-        ev_e[i].record()
-    t_end.record()
+        step(i, evs[i])
+    hev.record(t_end)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_per_step = t_start.elapsed_time(t_end) / K
-    attn_us = [ev_s[i].elapsed_time(ev_e[i]) * 1e3 for i in range(K)]
-    attn_us_mean = float(np.mean(attn_us))
+    ms_per_step = hev.ms(t_start, t_end) / K
+    attn_us_mean = float(np.mean([hev.ms(e[0], e[2]) * 1e3 for e in evs]))
+    kernel_us_mean = (float(np.mean([hev.ms(e[0], e[1]) * 1e3 for e in evs])) if two
+                      else attn_us_mean)
+    hev.close()
 
     if args.copy_ref_mib > 0:
         # device copies of a known size, for scaling the memory counters
@@ -465,14 +611,14 @@ def main() -> int:
         attn(i)
 
     R = max(1, args.graph_replays)
-    graph_step_us = time_graphs(capture(step_fn), R)
-    graph_attn_us = time_graphs(capture(attn), R)
+    graph_step_us = time_graphs(capture(step_fn), R, warm=min(200, 10 * R))
+    graph_attn_us = time_graphs(capture(attn), R, warm=min(200, 10 * R))
 
     nbytes = W.verify_algorithmic_bytes(case, [Q] * B) if Q else W.algorithmic_bytes(case)
-    achieved = nbytes / (attn_us_mean * 1e-6) / 1e9
+    achieved = nbytes / (kernel_us_mean * 1e-6) / 1e9
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     workload = case.name + (f"_q{Q}" if Q else "")
-    traffic = _traffic_for("verify" if Q else "decode", workload)
+    traffic = _traffic_for("verify" if Q else "decode", workload, producer_only=two)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -522,10 +668,13 @@ def main() -> int:
                    "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D, "page_size": P,
                    "num_pages": case.num_pages, "num_splits": S, "kv_dtype": case.kv_dtype,
                    "query_tokens_per_request": Q or 1,
-                   "step": ("page-table build + split-K decode attention (library defaults)"
+                   "step": (("page-table build + split-K decode attention (library default "
+                             "plan: producer launch, then merge launch)") if two else
+                            "page-table build + split-K decode attention (library defaults)"
                             if not Q else "metadata build (page table, cu_seqlens_q) + "
                             "multi-token split-K decode attention")},
         "us_per_call": round(attn_us_mean, 3),
+        "producer_us": round(kernel_us_mean, 3) if two else None,
         "pct_of_peak": round(100.0 * achieved / PEAK_HBM_GBS, 2),
         "graph_step_us": round(graph_step_us, 3),
         "graph_attn_us": round(graph_attn_us, 3),
@@ -533,7 +682,9 @@ def main() -> int:
         "algorithmic_bytes": int(nbytes),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": traffic},
+                     "traffic": traffic,
+                     "kernel": ("producer launch (events around spa_paged_decode_partials)"
+                                if two else "the call's launches (events around the call)")},
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 4),
         "gen_s": round(gen_s, 2),

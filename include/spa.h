@@ -229,6 +229,58 @@ spa_status spa_paged_decode_attention(const void *q, const void *k_pages, const 
                                       void *out, float *lse, hipStream_t stream);
 
 /*
+ * The launch plan spa_paged_decode_attention takes with flags == 0 for these
+ * sizes: one producer flag (SPA_DECODE_HEAD_GROUPED or SPA_DECODE_PAGE_SPLIT)
+ * or'ed with one merge flag (SPA_DECODE_FUSED_MERGE or
+ * SPA_DECODE_SEPARATE_MERGE).  Passing the result back as flags gives the
+ * same launches.  The choice depends on these arguments only (and, for the
+ * splits a bf16 head-grouped workgroup walks, on the current device's
+ * compute units).  0 for sizes spa_paged_decode_attention would reject as
+ * invalid or unsupported.
+ */
+uint32_t spa_decode_default_flags(int32_t batch, int32_t num_kv_heads, int32_t num_splits,
+                                  spa_kv_dtype kv_dtype, int64_t page_table_stride);
+
+/*
+ * The producer pass of split-K decode alone (lmdeploy PR "use PDL for paged
+ * attention", Changes: the split-K producer writes per-split scratch that a
+ * reducer reads): the same per-split state spa_paged_decode_attention forms
+ * before its merge, written to caller buffers in the layout spa_split_merge
+ * reads.  spa_paged_decode_partials followed by spa_split_merge on the same
+ * stream gives bit for bit the output of spa_paged_decode_attention with the
+ * same producer flag and SPA_DECODE_SEPARATE_MERGE.  It is also the
+ * per-device step of a context split across devices: each device forms the
+ * states of its own splits, and one merge combines them after the exchange.
+ *
+ * For request b, query head h and split j (pages cut as in
+ * spa_paged_decode_attention), over the split's tokens t:
+ *   partial_max[b,h,j]   = m_j = max_t s_t               (natural-log units)
+ *   partial_sum[b,h,j]   = sum_t exp(s_t - m_j)
+ *   partial_acc[b,h,j,:] = sum_t exp(s_t - m_j) v_t      (not divided by the sum)
+ * and (-inf, 0, 0) for a split with no tokens.
+ *
+ *   partial_acc [batch, num_q_heads, num_splits, head_dim] fp32, 16-byte aligned (output)
+ *   partial_max, partial_sum [batch, num_q_heads, num_splits] fp32 (outputs)
+ *   other arguments as in spa_paged_decode_attention.
+ *
+ * flags: 0 (the producer spa_paged_decode_attention would choose), or
+ * SPA_DECODE_HEAD_GROUPED or SPA_DECODE_PAGE_SPLIT; a merge flag is
+ * SPA_ERR_INVALID_ARGUMENT.  No workspace: the partial buffers are the
+ * scratch, owned by the caller, and need no zeroing.  Supported set and
+ * errors as in spa_paged_decode_attention; batch == 0 returns SPA_OK
+ * without launching.
+ */
+spa_status spa_paged_decode_partials(const void *q, const void *k_pages, const void *v_pages,
+                                     const float *k_scales, const float *v_scales,
+                                     const int32_t *page_table, int64_t page_table_stride,
+                                     const int32_t *seq_lens, int32_t batch,
+                                     int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t page_size, int32_t num_pages,
+                                     int32_t num_splits, float scale, spa_kv_dtype kv_dtype,
+                                     uint32_t flags, float *partial_acc, float *partial_max,
+                                     float *partial_sum, hipStream_t stream);
+
+/*
  * Bytes of workspace spa_paged_verify_attention needs: the per-split state
  * of every (query row, head) (fp32 accumulator [total_q, Hq, S, D], fp32 max
  * and sum [total_q, Hq, S]), 256-byte aligned regions.  0 for invalid sizes.

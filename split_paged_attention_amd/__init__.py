@@ -90,6 +90,12 @@ def lib():
                                              _I32, _I32, _I32, _I32, _F32, _ST, _U32, _P, _SZ,
                                              _P, _P, _P]
     L.spa_paged_decode_attention.restype = _ST
+    L.spa_decode_default_flags.argtypes = [_I32, _I32, _I32, _ST, _I64]
+    L.spa_decode_default_flags.restype = _U32
+    L.spa_paged_decode_partials.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _P, _I32, _I32, _I32,
+                                            _I32, _I32, _I32, _I32, _F32, _ST, _U32, _P, _P, _P,
+                                            _P]
+    L.spa_paged_decode_partials.restype = _ST
     L.spa_verify_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32, _I32]
     L.spa_verify_workspace_bytes.restype = _SZ
     L.spa_paged_verify_attention.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _P, _P, _I32, _I32,
@@ -264,26 +270,9 @@ def new_workspace(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int
 
 # ---------------------------------------------------------------- attention
 
-def paged_decode_attention(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
-                           page_table: torch.Tensor, seq_lens: torch.Tensor, num_splits: int,
-                           scale: float, *, kv_dtype: str = "bf16",
-                           k_scales: Optional[torch.Tensor] = None,
-                           v_scales: Optional[torch.Tensor] = None,
-                           workspace: Optional[torch.Tensor] = None,
-                           out: Optional[torch.Tensor] = None,
-                           lse: Optional[torch.Tensor] = None,
-                           separate_merge: bool = False,
-                           merge: Optional[str] = None,
-                           producer: Optional[str] = None,
-                           stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """spa_paged_decode_attention.  q [B, Hq, D] bf16; k/v_pages
-    [num_pages, P, Hkv, D] bf16, int8, or e4m3 codes (uint8 or
-    float8_e4m3fn) for kv_dtype "fp8"; k/v_scales [num_pages, P, Hkv] fp32
-    for int8 and fp8; page_table [B, stride] int32; seq_lens [B] int32.
-    Returns (out [B, Hq, D] bf16, lse [B, Hq] fp32).
-
-    merge: None (library default), "fused" or "separate" (``separate_merge=True``
-    is the same as "separate"); producer: None, "head_grouped" or "page_split"."""
+def _decode_inputs(q, k_pages, v_pages, page_table, seq_lens, kv_dtype, k_scales, v_scales):
+    """Checks of the decode inputs; returns (B, Hq, D, num_pages, P, Hkv, kv enum,
+    k_scales, v_scales)."""
     _need(q, "q", torch.bfloat16)
     if q.dim() != 3:
         raise ValueError("q must be [batch, num_q_heads, head_dim]")
@@ -314,6 +303,35 @@ def paged_decode_attention(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torc
     _need(seq_lens, "seq_lens", torch.int32)
     if seq_lens.shape != (B,):
         raise ValueError("seq_lens must be [batch]")
+    return B, Hq, D, num_pages, P, Hkv, kvd, k_scales, v_scales
+
+
+_PRODUCER_FLAGS = {None: 0, "head_grouped": SPA_DECODE_HEAD_GROUPED,
+                   "page_split": SPA_DECODE_PAGE_SPLIT}
+
+
+def paged_decode_attention(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
+                           page_table: torch.Tensor, seq_lens: torch.Tensor, num_splits: int,
+                           scale: float, *, kv_dtype: str = "bf16",
+                           k_scales: Optional[torch.Tensor] = None,
+                           v_scales: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None,
+                           out: Optional[torch.Tensor] = None,
+                           lse: Optional[torch.Tensor] = None,
+                           separate_merge: bool = False,
+                           merge: Optional[str] = None,
+                           producer: Optional[str] = None,
+                           stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """spa_paged_decode_attention.  q [B, Hq, D] bf16; k/v_pages
+    [num_pages, P, Hkv, D] bf16, int8, or e4m3 codes (uint8 or
+    float8_e4m3fn) for kv_dtype "fp8"; k/v_scales [num_pages, P, Hkv] fp32
+    for int8 and fp8; page_table [B, stride] int32; seq_lens [B] int32.
+    Returns (out [B, Hq, D] bf16, lse [B, Hq] fp32).
+
+    merge: None (library default), "fused" or "separate" (``separate_merge=True``
+    is the same as "separate"); producer: None, "head_grouped" or "page_split"."""
+    B, Hq, D, num_pages, P, Hkv, kvd, k_scales, v_scales = _decode_inputs(
+        q, k_pages, v_pages, page_table, seq_lens, kv_dtype, k_scales, v_scales)
     if workspace is None:
         workspace = new_workspace(B, Hq, Hkv, D, num_splits, device=q.device, stream=stream)
     _need(workspace, "workspace", torch.uint8)
@@ -328,8 +346,7 @@ def paged_decode_attention(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torc
             raise ValueError("separate_merge=True contradicts merge=" + repr(merge))
         merge = "separate"
     flags = {None: 0, "fused": SPA_DECODE_FUSED_MERGE, "separate": SPA_DECODE_SEPARATE_MERGE}[merge]
-    flags |= {None: 0, "head_grouped": SPA_DECODE_HEAD_GROUPED,
-              "page_split": SPA_DECODE_PAGE_SPLIT}[producer]
+    flags |= _PRODUCER_FLAGS[producer]
     st = lib().spa_paged_decode_attention(
         _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(k_scales), _ptr(v_scales), _ptr(page_table),
         page_table.stride(0), _ptr(seq_lens), B, Hq, Hkv, D, P, num_pages, int(num_splits),
@@ -337,6 +354,53 @@ def paged_decode_attention(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torc
         _stream(stream))
     _check(st, "spa_paged_decode_attention")
     return out, lse
+
+
+def decode_default_flags(batch: int, num_kv_heads: int, num_splits: int, kv_dtype: str,
+                         page_table_stride: int) -> int:
+    """spa_decode_default_flags: the producer | merge flags of the plan
+    paged_decode_attention takes by default (0 for rejected sizes)."""
+    kvd = {"bf16": SPA_KV_BF16, "int8": SPA_KV_INT8, "fp8": SPA_KV_FP8}[kv_dtype]
+    return int(lib().spa_decode_default_flags(batch, num_kv_heads, num_splits, kvd,
+                                              page_table_stride))
+
+
+def paged_decode_partials(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
+                          page_table: torch.Tensor, seq_lens: torch.Tensor, num_splits: int,
+                          scale: float, *, kv_dtype: str = "bf16",
+                          k_scales: Optional[torch.Tensor] = None,
+                          v_scales: Optional[torch.Tensor] = None,
+                          partial_acc: Optional[torch.Tensor] = None,
+                          partial_max: Optional[torch.Tensor] = None,
+                          partial_sum: Optional[torch.Tensor] = None,
+                          producer: Optional[str] = None,
+                          stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """spa_paged_decode_partials: the producer pass alone.  Inputs as in
+    paged_decode_attention; returns (partial_acc [B, Hq, S, D], partial_max
+    [B, Hq, S], partial_sum [B, Hq, S]), fp32, the layout split_merge reads."""
+    B, Hq, D, num_pages, P, Hkv, kvd, k_scales, v_scales = _decode_inputs(
+        q, k_pages, v_pages, page_table, seq_lens, kv_dtype, k_scales, v_scales)
+    S = int(num_splits)
+    if partial_acc is None:
+        partial_acc = torch.empty((B, Hq, S, D), dtype=torch.float32, device=q.device)
+    if partial_max is None:
+        partial_max = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    if partial_sum is None:
+        partial_sum = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    _need(partial_acc, "partial_acc", torch.float32)
+    _need(partial_max, "partial_max", torch.float32)
+    _need(partial_sum, "partial_sum", torch.float32)
+    if (tuple(partial_acc.shape) != (B, Hq, S, D) or tuple(partial_max.shape) != (B, Hq, S)
+            or tuple(partial_sum.shape) != (B, Hq, S)):
+        raise ValueError("partial_acc must be [batch, num_q_heads, num_splits, head_dim] and "
+                         "partial_max/partial_sum [batch, num_q_heads, num_splits]")
+    st = lib().spa_paged_decode_partials(
+        _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(k_scales), _ptr(v_scales), _ptr(page_table),
+        page_table.stride(0), _ptr(seq_lens), B, Hq, Hkv, D, P, num_pages, S, float(scale), kvd,
+        _PRODUCER_FLAGS[producer], _ptr(partial_acc), _ptr(partial_max), _ptr(partial_sum),
+        _stream(stream))
+    _check(st, "spa_paged_decode_partials")
+    return partial_acc, partial_max, partial_sum
 
 
 def verify_workspace_bytes(total_q: int, num_q_heads: int, num_kv_heads: int, head_dim: int,

@@ -37,6 +37,95 @@ spa_status hip_status(hipError_t e) {
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+int kv_type_of(spa_kv_dtype d) {
+    return d == SPA_KV_INT8 ? spa::kKvInt8 : d == SPA_KV_FP8 ? spa::kKvFp8 : spa::kKvBf16;
+}
+
+// Launch plan of a decode call: KV type, producer shape, merge placement.
+struct DecodePlan {
+    int kv_type;
+    spa::DecodeMode mode;
+    bool fused;
+};
+
+// The plan flags == 0 selects.  Merge (measured): fused into the producer
+// launch for page-split grids of up to 8 splits; a second launch for more
+// splits, where the last arrival's merge of all of them sits on the
+// critical path, and after head-grouped grids, whose splits all finish
+// together.
+DecodePlan default_plan(int32_t batch, int32_t hkv, int32_t splits, int kv_type,
+                        int64_t pt_stride) {
+    DecodePlan plan{};
+    plan.kv_type = kv_type;
+    plan.mode = spa::default_mode(batch, hkv, splits, kv_type, pt_stride);
+    plan.fused = plan.mode == spa::DecodeMode::kPageSplit && splits <= 8;
+    return plan;
+}
+
+// Checks shared by the one-token decode entry points (everything but the
+// outputs and scratch) and the parameters and plan they lead to.
+// producer_only: a merge flag is an error (the caller merges).
+spa_status decode_setup(const void *q, const void *k_pages, const void *v_pages,
+                        const float *k_scales, const float *v_scales, const int32_t *page_table,
+                        int64_t page_table_stride, const int32_t *seq_lens, int32_t batch,
+                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t page_size, int32_t num_pages, int32_t num_splits, float scale,
+                        spa_kv_dtype kv_dtype, uint32_t flags, bool producer_only,
+                        spa::DecodeParams *p, DecodePlan *plan) {
+    if (batch < 0 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 || page_size < 1 ||
+        num_pages < 1 || num_splits < 1 || page_table_stride < 1)
+        return SPA_ERR_INVALID_ARGUMENT;
+    if (num_q_heads % num_kv_heads != 0) return SPA_ERR_INVALID_ARGUMENT;
+    if (kv_dtype != SPA_KV_BF16 && kv_dtype != SPA_KV_INT8 && kv_dtype != SPA_KV_FP8)
+        return SPA_ERR_INVALID_ARGUMENT;
+    const bool quant = kv_dtype != SPA_KV_BF16;
+    const uint32_t merge_flags = SPA_DECODE_SEPARATE_MERGE | SPA_DECODE_FUSED_MERGE;
+    const uint32_t known = merge_flags | SPA_DECODE_HEAD_GROUPED | SPA_DECODE_PAGE_SPLIT;
+    if ((flags & ~known) != 0) return SPA_ERR_INVALID_ARGUMENT;
+    if (producer_only && (flags & merge_flags) != 0) return SPA_ERR_INVALID_ARGUMENT;
+    if ((flags & SPA_DECODE_SEPARATE_MERGE) && (flags & SPA_DECODE_FUSED_MERGE))
+        return SPA_ERR_INVALID_ARGUMENT;
+    if ((flags & SPA_DECODE_HEAD_GROUPED) && (flags & SPA_DECODE_PAGE_SPLIT))
+        return SPA_ERR_INVALID_ARGUMENT;
+    if (!isfinite(scale)) return SPA_ERR_INVALID_ARGUMENT;
+    if (head_dim != spa::kHeadDim || page_size != spa::kPageSize ||
+        num_q_heads != spa::kGroup * num_kv_heads || num_splits > 1024)
+        return SPA_ERR_UNSUPPORTED;
+    // grid = batch * kv_heads * splits workgroups must fit a 32-bit grid
+    if ((int64_t)batch * num_kv_heads * num_splits > (int64_t)INT32_MAX)
+        return SPA_ERR_UNSUPPORTED;
+    *plan = default_plan(batch, num_kv_heads, num_splits, kv_type_of(kv_dtype),
+                         page_table_stride);
+    if (flags & SPA_DECODE_HEAD_GROUPED) plan->mode = spa::DecodeMode::kHeadGrouped;
+    if (flags & SPA_DECODE_PAGE_SPLIT) plan->mode = spa::DecodeMode::kPageSplit;
+    if (flags & SPA_DECODE_SEPARATE_MERGE) plan->fused = false;
+    if (flags & SPA_DECODE_FUSED_MERGE) plan->fused = true;
+    if (producer_only) plan->fused = false;
+    if (batch == 0) return SPA_OK;
+    if (!spa::mode_supported(plan->mode, num_kv_heads)) return SPA_ERR_UNSUPPORTED;
+    if (!q || !k_pages || !v_pages || !page_table || !seq_lens) return SPA_ERR_INVALID_ARGUMENT;
+    if (quant && (!k_scales || !v_scales)) return SPA_ERR_INVALID_ARGUMENT;
+    if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) ||
+        !aligned(page_table, 4) || !aligned(seq_lens, 4) ||
+        (quant && (!aligned(k_scales, 4) || !aligned(v_scales, 4))))
+        return SPA_ERR_INVALID_ARGUMENT;
+    p->q = q;
+    p->k_pages = k_pages;
+    p->v_pages = v_pages;
+    p->k_scales = k_scales;
+    p->v_scales = v_scales;
+    p->page_table = page_table;
+    p->pt_stride = page_table_stride;
+    p->seq_lens = seq_lens;
+    p->batch = batch;
+    p->hq = num_q_heads;
+    p->hkv = num_kv_heads;
+    p->splits = num_splits;
+    p->num_pages = num_pages;
+    p->qk_scale_log2 = scale * 1.4426950408889634f;
+    return SPA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -54,7 +143,7 @@ const char *spa_status_string(spa_status status) {
 
 int spa_last_hip_error(void) { return g_last_hip_error; }
 
-int spa_abi_version(void) { return 1; }
+int spa_abi_version(void) { return 2; }
 
 spa_status spa_build_metadata(
     const int32_t *req_to_token, int64_t req_to_token_stride, int32_t pool_size,
@@ -162,79 +251,66 @@ spa_status spa_paged_decode_attention(const void *q, const void *k_pages, const 
                                       int32_t num_splits, float scale, spa_kv_dtype kv_dtype,
                                       uint32_t flags, void *workspace, size_t workspace_bytes,
                                       void *out, float *lse, hipStream_t stream) {
-    if (batch < 0 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 || page_size < 1 ||
-        num_pages < 1 || num_splits < 1 || page_table_stride < 1)
-        return SPA_ERR_INVALID_ARGUMENT;
-    if (num_q_heads % num_kv_heads != 0) return SPA_ERR_INVALID_ARGUMENT;
-    if (kv_dtype != SPA_KV_BF16 && kv_dtype != SPA_KV_INT8 && kv_dtype != SPA_KV_FP8)
-        return SPA_ERR_INVALID_ARGUMENT;
-    const bool quant = kv_dtype != SPA_KV_BF16;
-    const uint32_t known = SPA_DECODE_SEPARATE_MERGE | SPA_DECODE_FUSED_MERGE |
-                           SPA_DECODE_HEAD_GROUPED | SPA_DECODE_PAGE_SPLIT;
-    if ((flags & ~known) != 0) return SPA_ERR_INVALID_ARGUMENT;
-    if ((flags & SPA_DECODE_SEPARATE_MERGE) && (flags & SPA_DECODE_FUSED_MERGE))
-        return SPA_ERR_INVALID_ARGUMENT;
-    if ((flags & SPA_DECODE_HEAD_GROUPED) && (flags & SPA_DECODE_PAGE_SPLIT))
-        return SPA_ERR_INVALID_ARGUMENT;
-    if (!isfinite(scale)) return SPA_ERR_INVALID_ARGUMENT;
-    if (head_dim != spa::kHeadDim || page_size != spa::kPageSize ||
-        num_q_heads != spa::kGroup * num_kv_heads || num_splits > 1024)
-        return SPA_ERR_UNSUPPORTED;
-    // grid = batch * kv_heads * splits workgroups must fit a 32-bit grid
-    if ((int64_t)batch * num_kv_heads * num_splits > (int64_t)INT32_MAX)
-        return SPA_ERR_UNSUPPORTED;
-    if (batch == 0) return SPA_OK;
-    if (!q || !k_pages || !v_pages || !page_table || !seq_lens || !out || !workspace)
-        return SPA_ERR_INVALID_ARGUMENT;
-    if (quant && (!k_scales || !v_scales)) return SPA_ERR_INVALID_ARGUMENT;
-    if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) ||
-        !aligned(workspace, 16) || !aligned(out, 2) || !aligned(page_table, 4) ||
-        !aligned(seq_lens, 4) || (lse && !aligned(lse, 4)) ||
-        (quant && (!aligned(k_scales, 4) || !aligned(v_scales, 4))))
+    spa::DecodeParams p{};
+    DecodePlan plan{};
+    spa_status st = decode_setup(q, k_pages, v_pages, k_scales, v_scales, page_table,
+                                 page_table_stride, seq_lens, batch, num_q_heads, num_kv_heads,
+                                 head_dim, page_size, num_pages, num_splits, scale, kv_dtype,
+                                 flags, /*producer_only=*/false, &p, &plan);
+    if (st != SPA_OK || batch == 0) return st;
+    if (!out || !workspace) return SPA_ERR_INVALID_ARGUMENT;
+    if (!aligned(workspace, 16) || !aligned(out, 2) || (lse && !aligned(lse, 4)))
         return SPA_ERR_INVALID_ARGUMENT;
     const spa::WorkspaceLayout w =
         spa::workspace_layout(batch, num_q_heads, num_kv_heads, head_dim, num_splits);
     if (workspace_bytes < w.total) return SPA_ERR_WORKSPACE_TOO_SMALL;
 
     char *ws = static_cast<char *>(workspace);
-    spa::DecodeParams p{};
-    p.q = q;
-    p.k_pages = k_pages;
-    p.v_pages = v_pages;
-    p.k_scales = k_scales;
-    p.v_scales = v_scales;
-    p.page_table = page_table;
-    p.pt_stride = page_table_stride;
-    p.seq_lens = seq_lens;
-    p.batch = batch;
-    p.hq = num_q_heads;
-    p.hkv = num_kv_heads;
-    p.splits = num_splits;
-    p.num_pages = num_pages;
-    p.qk_scale_log2 = scale * 1.4426950408889634f;
     p.part_acc = reinterpret_cast<float *>(ws + w.acc_off);
     p.part_max = reinterpret_cast<float *>(ws + w.max_off);
     p.part_sum = reinterpret_cast<float *>(ws + w.sum_off);
     p.counters = reinterpret_cast<int32_t *>(ws + w.cnt_off);
     p.out = static_cast<uint16_t *>(out);
     p.lse = lse;
-    const int kv_type = kv_dtype == SPA_KV_INT8  ? spa::kKvInt8
-                        : kv_dtype == SPA_KV_FP8 ? spa::kKvFp8
-                                                 : spa::kKvBf16;
-    spa::DecodeMode mode =
-        spa::default_mode(batch, num_kv_heads, num_splits, kv_type, page_table_stride);
-    if (flags & SPA_DECODE_HEAD_GROUPED) mode = spa::DecodeMode::kHeadGrouped;
-    if (flags & SPA_DECODE_PAGE_SPLIT) mode = spa::DecodeMode::kPageSplit;
-    if (!spa::mode_supported(mode, num_kv_heads)) return SPA_ERR_UNSUPPORTED;
-    // Default merge (measured): fused into the producer launch for
-    // page-split grids of up to 8 splits; a second launch for more splits,
-    // where the last arrival's merge of all of them sits on the critical
-    // path, and after head-grouped grids, whose splits all finish together.
-    bool fused = mode == spa::DecodeMode::kPageSplit && num_splits <= 8;
-    if (flags & SPA_DECODE_SEPARATE_MERGE) fused = false;
-    if (flags & SPA_DECODE_FUSED_MERGE) fused = true;
-    return hip_status(
-        spa::launch_decode(p, kv_type, mode, fused, stream));
+    return hip_status(spa::launch_decode(p, plan.kv_type, plan.mode, plan.fused, stream));
+}
+
+uint32_t spa_decode_default_flags(int32_t batch, int32_t num_kv_heads, int32_t num_splits,
+                                  spa_kv_dtype kv_dtype, int64_t page_table_stride) {
+    if (batch < 0 || num_kv_heads < 1 || num_splits < 1 || num_splits > 1024 ||
+        page_table_stride < 1 || (int64_t)batch * num_kv_heads * num_splits > (int64_t)INT32_MAX)
+        return 0u;
+    if (kv_dtype != SPA_KV_BF16 && kv_dtype != SPA_KV_INT8 && kv_dtype != SPA_KV_FP8) return 0u;
+    const DecodePlan plan = default_plan(batch, num_kv_heads, num_splits, kv_type_of(kv_dtype),
+                                         page_table_stride);
+    return (plan.mode == spa::DecodeMode::kHeadGrouped ? SPA_DECODE_HEAD_GROUPED
+                                                       : SPA_DECODE_PAGE_SPLIT) |
+           (plan.fused ? SPA_DECODE_FUSED_MERGE : SPA_DECODE_SEPARATE_MERGE);
+}
+
+spa_status spa_paged_decode_partials(const void *q, const void *k_pages, const void *v_pages,
+                                     const float *k_scales, const float *v_scales,
+                                     const int32_t *page_table, int64_t page_table_stride,
+                                     const int32_t *seq_lens, int32_t batch,
+                                     int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t page_size, int32_t num_pages,
+                                     int32_t num_splits, float scale, spa_kv_dtype kv_dtype,
+                                     uint32_t flags, float *partial_acc, float *partial_max,
+                                     float *partial_sum, hipStream_t stream) {
+    spa::DecodeParams p{};
+    DecodePlan plan{};
+    spa_status st = decode_setup(q, k_pages, v_pages, k_scales, v_scales, page_table,
+                                 page_table_stride, seq_lens, batch, num_q_heads, num_kv_heads,
+                                 head_dim, page_size, num_pages, num_splits, scale, kv_dtype,
+                                 flags, /*producer_only=*/true, &p, &plan);
+    if (st != SPA_OK || batch == 0) return st;
+    if (!partial_acc || !partial_max || !partial_sum) return SPA_ERR_INVALID_ARGUMENT;
+    if (!aligned(partial_acc, 16) || !aligned(partial_max, 4) || !aligned(partial_sum, 4))
+        return SPA_ERR_INVALID_ARGUMENT;
+    p.part_acc = partial_acc;
+    p.part_max = partial_max;
+    p.part_sum = partial_sum;
+    return hip_status(spa::launch_decode_producer(p, plan.kv_type, plan.mode, stream));
 }
 
 size_t spa_verify_workspace_bytes(int32_t total_q, int32_t num_q_heads, int32_t num_kv_heads,

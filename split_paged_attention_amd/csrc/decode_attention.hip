@@ -1053,15 +1053,23 @@ hipError_t launch_kv(const DecodeParams &p, DecodeMode mode, bool fused, hipStre
     return launch_nw<KV, kNwPageSplit, false>(p, fused, stream);
 }
 
+namespace {
+hipError_t launch_producer(const DecodeParams &p, int kv_type, DecodeMode mode, bool fused,
+                           hipStream_t stream) {
+    if (kv_type == kKvInt8) return launch_kv<1>(p, mode, fused, stream);
+    if (kv_type == kKvFp8) return launch_kv<2>(p, mode, fused, stream);
+    return launch_kv<0>(p, mode, fused, stream);
+}
+}  // namespace
+
+hipError_t launch_decode_producer(const DecodeParams &p, int kv_type, DecodeMode mode,
+                                  hipStream_t stream) {
+    return launch_producer(p, kv_type, mode, /*fused=*/false, stream);
+}
+
 hipError_t launch_decode(const DecodeParams &p, int kv_type, DecodeMode mode, bool fused,
                          hipStream_t stream) {
-    hipError_t err;
-    if (kv_type == kKvInt8)
-        err = launch_kv<1>(p, mode, fused, stream);
-    else if (kv_type == kKvFp8)
-        err = launch_kv<2>(p, mode, fused, stream);
-    else
-        err = launch_kv<0>(p, mode, fused, stream);
+    const hipError_t err = launch_producer(p, kv_type, mode, fused, stream);
     if (err != hipSuccess || fused) return err;
     return launch_split_merge(p.part_acc, p.part_max, p.part_sum, p.batch * p.hq, kHeadDim,
                               p.splits, p.out, p.lse, stream);

@@ -96,6 +96,9 @@ bool mode_supported(DecodeMode mode, int hkv);
 constexpr int kKvBf16 = 0, kKvInt8 = 1, kKvFp8 = 2;
 hipError_t launch_decode(const DecodeParams &p, int kv_type, DecodeMode mode, bool fused,
                          hipStream_t stream);
+// The producer alone (separate-merge form): split states to p.part_*.
+hipError_t launch_decode_producer(const DecodeParams &p, int kv_type, DecodeMode mode,
+                                  hipStream_t stream);
 
 // Multi-token decode producer (2 kv heads per workgroup) + split merge over
 // total_q * hq rows; partial state rows are query rows.

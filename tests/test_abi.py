@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
     for n in declared_functions():
         assert n in exported, n
         assert hasattr(L, n)
-    assert L.spa_abi_version() == 1
+    assert L.spa_abi_version() == 2
 
 
 def test_status_strings():
@@ -111,6 +111,60 @@ def test_workspace_reset_checks():
     assert L.spa_workspace_reset(None, 0, None) == spa.SPA_OK
     assert L.spa_workspace_reset(None, 16, None) == spa.SPA_ERR_INVALID_ARGUMENT
     assert L.spa_workspace_reset(FAKE, 6, None) == spa.SPA_ERR_INVALID_ARGUMENT
+
+
+def _partials(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ks=None, vs=None, pt=FAKE, pts=128, sl=FAKE, B=1, Hq=32,
+             Hkv=8, D=128, P=64, npg=16, S=4, scale=0.088, kvd=0, flags=0, acc=FAKE, mx=FAKE,
+             sm=FAKE)
+    a.update(kw)
+    return spa.lib().spa_paged_decode_partials(
+        a["q"], a["k"], a["v"], a["ks"], a["vs"], a["pt"], a["pts"], a["sl"], a["B"], a["Hq"],
+        a["Hkv"], a["D"], a["P"], a["npg"], a["S"], a["scale"], a["kvd"], a["flags"], a["acc"],
+        a["mx"], a["sm"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(flags=spa.SPA_DECODE_SEPARATE_MERGE), spa.SPA_ERR_INVALID_ARGUMENT),   # merge flags
+    (dict(flags=spa.SPA_DECODE_FUSED_MERGE), spa.SPA_ERR_INVALID_ARGUMENT),      # are the caller's
+    (dict(flags=12), spa.SPA_ERR_INVALID_ARGUMENT),           # both producer shapes
+    (dict(flags=16), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(acc=None), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(mx=None), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(sm=None), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(acc=ctypes.c_void_p(0x100004)), spa.SPA_ERR_INVALID_ARGUMENT),   # acc needs 16 B
+    (dict(mx=FAKE_ODD), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(kvd=1), spa.SPA_ERR_INVALID_ARGUMENT),              # int8 without scales
+    (dict(scale=math.inf), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(D=64), spa.SPA_ERR_UNSUPPORTED),
+    (dict(Hq=12, Hkv=3, flags=spa.SPA_DECODE_HEAD_GROUPED), spa.SPA_ERR_UNSUPPORTED),
+    (dict(S=1025), spa.SPA_ERR_UNSUPPORTED),
+    (dict(B=0), spa.SPA_OK),                                  # no launch
+    (dict(B=0, acc=None, q=None), spa.SPA_OK),
+])
+def test_partials_argument_checks(kw, code):
+    assert _partials(**kw) == code
+
+
+def test_default_flags():
+    f = spa.decode_default_flags
+    HG, PS = spa.SPA_DECODE_HEAD_GROUPED, spa.SPA_DECODE_PAGE_SPLIT
+    SEP, FUS = spa.SPA_DECODE_SEPARATE_MERGE, spa.SPA_DECODE_FUSED_MERGE
+    assert f(32, 8, 16, "bf16", 128) == HG | SEP        # batch 32 / 8K: 4096 triples
+    assert f(1, 8, 4, "bf16", 16) == PS | FUS           # batch 1 / 1K, 4 splits
+    assert f(1, 8, 16, "bf16", 128) == PS | SEP         # more than 8 splits: second launch
+    assert f(8, 8, 4, "bf16", 16) == PS | FUS           # 256 triples
+    assert f(16, 8, 4, "bf16", 16) == HG | SEP          # 512 triples
+    assert f(32, 8, 16, "int8", 128) == HG | SEP        # 4096 triples
+    assert f(8, 8, 16, "fp8", 128) == HG | SEP          # 1024 triples, 8-page splits
+    assert f(8, 8, 4, "fp8", 128) == PS | FUS           # 256 triples
+    assert f(32, 3, 16, "bf16", 128) == PS | SEP        # odd kv heads: page split only
+    # every result is exactly one producer and one merge flag
+    for args in [(1, 8, 1, "bf16", 1), (64, 8, 8, "int8", 32), (4, 2, 1024, "fp8", 128)]:
+        v = f(*args)
+        assert bin(v & (HG | PS)).count("1") == 1 and bin(v & (SEP | FUS)).count("1") == 1
+    assert f(-1, 8, 4, "bf16", 16) == 0 and f(1, 8, 0, "bf16", 16) == 0
+    assert f(1, 8, 1025, "bf16", 16) == 0 and f(1, 8, 4, "bf16", 0) == 0
 
 
 def _meta(**kw):
