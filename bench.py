@@ -11,10 +11,13 @@ bf16 K/V in 64-token pages scattered over a 4096-page pool, 16 splits --
 lmdeploy's headline H200 shape.
 
 Timing: W untimed warm-up steps, then exactly K steps between two device
-synchronisations; HIP events on the launch stream bracket every attention
-call (both launches and the gap between them fall inside) and, for a
-two-launch plan, the producer launch alone: the roofline figure is the
-algorithmic bytes over the producer's average duration.  Two copies of the KV pool alternate so that
+synchronisations (events on the launch stream bracket the run; `value` and
+ms_per_step come from them).  Then K more of the same steps with HIP events
+around every attention call (both launches and the gap between them fall
+inside) and, for a two-launch plan, around the producer launch alone: the
+roofline figure is the algorithmic bytes over the producer's average
+duration.  These events are kept out of the timed steps because an event
+between two launches idles the GPU for about 4 us.  Two copies of the KV pool alternate so that
 consecutive steps do not read the same addresses.  A HIP-graph replay of the
 step is timed as well (the pages quote CUDA-graph latency).  The fp64 CPU
 oracle is timed on the host beside it.
@@ -140,7 +143,8 @@ def summarize_pmc(fetch_dir: str, write_dir: str, out_path: str, copy_mib: int, 
 def summarize_trace(trace_dir: str, warmup: int, steps: int) -> dict:
     """Per-kernel durations from a rocprofv3 --kernel-trace run of this bench:
     the average over the K timed steps (decode dispatches warmup ..
-    warmup + steps - 1, in start order) and over all dispatches."""
+    warmup + steps - 1, in start order), over the K steps that follow them
+    with per-launch events, and over all dispatches."""
     import csv
     import glob
     import statistics
@@ -158,9 +162,12 @@ def summarize_trace(trace_dir: str, warmup: int, steps: int) -> dict:
         if not d:
             continue
         names = sorted(set(r["Kernel_Name"] for r in rows if pat in r["Kernel_Name"]))
-        timed = d[warmup:warmup + steps] if short != "metadata" else d[1 + warmup:1 + warmup + steps]
+        o = 1 if short == "metadata" else 0     # the rig's own first page-table build
+        timed = d[o + warmup:o + warmup + steps]
+        evented = d[o + warmup + steps:o + warmup + 2 * steps]
         out[short] = {"kernel": names, "dispatches": len(d),
                       "timed_steps_avg_us": round(statistics.mean(timed), 3) if timed else None,
+                      "event_steps_avg_us": round(statistics.mean(evented), 3) if evented else None,
                       "all_avg_us": round(statistics.mean(d), 3)}
     return out
 
@@ -577,18 +584,26 @@ def main() -> int:
         step(i)
     torch.cuda.synchronize()
 
+    # The K timed steps: events only around the whole run (an event between
+    # two launches leaves the GPU idle for about 4 us, so per-launch events
+    # would inflate the step time).
     K = args.steps
-    evs = [[hev.new() for _ in range(3)] for _ in range(K)]
     t_start, t_end = hev.new(), hev.new()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     hev.record(t_start)
     for i in range(K):
-        step(i, evs[i])
+        step(i)
     hev.record(t_end)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_per_step = hev.ms(t_start, t_end) / K
+    # Then K more of the same steps with events around each decode call and
+    # around its producer launch: the per-call and per-kernel durations.
+    evs = [[hev.new() for _ in range(3)] for _ in range(K)]
+    for i in range(K):
+        step(K + i, evs[i])
+    torch.cuda.synchronize()
     attn_us_mean = float(np.mean([hev.ms(e[0], e[2]) * 1e3 for e in evs]))
     kernel_us_mean = (float(np.mean([hev.ms(e[0], e[1]) * 1e3 for e in evs])) if two
                       else attn_us_mean)
