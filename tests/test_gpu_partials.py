@@ -99,9 +99,9 @@ def test_partials_split_walk_bit_identical():
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
 
 
-@pytest.mark.parametrize("cfg", [4, 5])
+@pytest.mark.parametrize("cfg", [4, 5, 6])
 def test_headline_partials_then_merge_equal_default_call(cfg):
-    """The full batch-32 workloads (8K bf16; ragged int8), in the launch
+    """The full batch-32 workloads (8K bf16; ragged int8; 8K fp8), in the launch
     configuration the benchmark times: producer entry point, then the merge
     entry point, against the default one-call decode."""
     c = config_case(cfg)
