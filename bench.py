@@ -490,7 +490,9 @@ def main() -> int:
                          "then recover)")
     ap.add_argument("--config", type=int, default=4, help="workload 1..5 (4 = headline)")
     ap.add_argument("--graph-replays", type=int, default=200)
-    ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--cpu-reps", type=int, default=40,
+                    help="timed oracle calls for cpu_baseline (about 10 s of host work at the "
+                         "headline shape)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="after timing, run device copies of this size (counter scaling)")
