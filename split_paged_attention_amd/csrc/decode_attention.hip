@@ -204,7 +204,7 @@ __device__ __forceinline__ void st_sys(float *p, float v) {
 constexpr int kStashFloats = kGroup * kHeadDim + 2 * kGroup;
 
 template <int KV, int NW, bool FUSED, bool HG>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(KV != 0 && HG ? 3 : 2)))
 void decode_kernel(DecodeParams p,
                                                         const int32_t *__restrict__ page_table,
                                                         const int32_t *__restrict__ seq_lens) {
@@ -372,7 +372,14 @@ void decode_kernel(DecodeParams p,
     // bytes) and read back in the matrix-core operand layout; rows padded by
     // 16 bytes so the 16 token rows of an operand read fall in different LDS
     // banks.
-    constexpr int KROWB = D * (QUANT ? 1 : 2) + 16;   // bytes per staged row
+    // Staged 1-byte codes skip the registers: buffer loads write the rows
+    // straight into the tile (16 bytes per lane, lane-linear in LDS), which
+    // frees the 32 registers a page of K would hold and lets 3 waves share a
+    // SIMD.  The rows are then unpadded; instead 16-byte chunk h of row r sits
+    // at chunk h ^ (r & 7), so the 16 rows of an operand read still spread
+    // over the banks.
+    constexpr bool KDMA = QUANT && KSTAGE;
+    constexpr int KROWB = KDMA ? D : D * (QUANT ? 1 : 2) + 16;   // bytes per staged row
     __shared__ __attribute__((aligned(16))) uint8_t ktile[KSTAGE ? NW : 1][KSTAGE ? P : 1][KROWB];
     __shared__ int sm_last;
 
@@ -392,7 +399,11 @@ void decode_kernel(DecodeParams p,
     const int v_lane = (vr * row_stride + 8 * vc) * ES;
     // staged 1-byte K: lane l loads 16 bytes of token row l / 8 of each 8-row
     // block, at byte 16 (l % 8)
-    const int k8_row = lane >> 3, k8_col = 16 * (lane & 7);
+    const int k8_row = lane >> 3;
+    // direct-to-LDS 1-byte K: lane l writes tile bytes 16 l .. of an 8-row
+    // block, i.e. row l / 8, chunk l % 8, which holds the row's chunk
+    // (l % 8) ^ (l / 8)
+    const int k8_dma = k8_row * row_bytes + (((lane & 7) ^ k8_row) << 4);
     // A loop iteration handles one page of this wave's page sequence (two
     // pages per iteration for 1-byte codes measured slower: 256 registers).
     uint4 kr[4][4];          // bf16 K (staged: kr[i/4][i%4] = token 4i + vr, dims 8vc ..)
@@ -430,9 +441,11 @@ void decode_kernel(DecodeParams p,
                     kr[t][c] = buf_ld16<KV_POLICY>(r, v_lane, 4 * (4 * t + c) * row_bytes);
             } else if constexpr (KSTAGE) {
 #pragma unroll
-                for (int c2 = 0; c2 < 2; ++c2)
-                    kr8[t][c2] = buf_ld16<KV_POLICY>(
-                        r, k8_row * row_bytes + k8_col, 8 * (2 * t + c2) * row_bytes);
+                for (int c2 = 0; c2 < 2; ++c2) {
+                    const int blk = 2 * t + c2;          // rows 8 blk .. 8 blk + 7
+                    buf_ld16_lds<KV_POLICY>(r, &ktile[wave][8 * blk][0], k8_dma,
+                                            8 * blk * row_bytes);
+                }
             } else if constexpr (!QUANT) {
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
@@ -572,13 +585,15 @@ void decode_kernel(DecodeParams p,
                 for (int i = 0; i < 16; ++i)
                     *reinterpret_cast<uint4 *>(&kt[4 * i + vr][16 * vc]) = kr[i >> 2][i & 3];
             } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    *reinterpret_cast<uint4 *>(&kt[8 * i + k8_row][k8_col]) = kr8[i >> 1][i & 1];
+                // this page's rows were written by the loads issued after the
+                // previous page's scores; the loads issued after them are the
+                // two V halves (16 instructions), so vmcnt <= 16 means the K
+                // rows are in the tile
+                __asm__ volatile("s_waitcnt vmcnt(16)" ::: "memory");
             }
             __asm__ volatile("" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
-            load_k(page_next, valid_next, 0, 2);
+            if constexpr (!QUANT) load_k(page_next, valid_next, 0, 2);
             if constexpr (QUANT) load_v_scales(page_next, valid_next);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -595,7 +610,7 @@ void decode_kernel(DecodeParams p,
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
                         const uint2 h = *reinterpret_cast<const uint2 *>(
-                            &kt[16 * t + n][64 * (c >> 1) + 16 * g + 8 * (c & 1)]);
+                            &kt[16 * t + n][(((4 * (c >> 1) + g) ^ (n & 7)) << 4) + 8 * (c & 1)]);
                         sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                             qa16[c], I8 ? i8x8_to_f16(h) : e4m3x8_to_f16(h), sacc[t], 0, 0, 0);
                     }
@@ -647,7 +662,14 @@ void decode_kernel(DecodeParams p,
             __builtin_amdgcn_sched_barrier(0);
         }
 
-        if constexpr (KSTAGE) {
+        if constexpr (KDMA) {
+            // the next page's K rows go into the tile once this page's
+            // operand reads have returned
+            __builtin_amdgcn_sched_barrier(0);
+            __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            load_k(page_next, valid_next, 0, 4);
+            __builtin_amdgcn_sched_barrier(0);
+        } else if constexpr (KSTAGE) {
             // the next page's K rows 32..63 (rows 0..31 went out with the tile
             // write): spread over the page, the requests measured 1% faster
             __builtin_amdgcn_sched_barrier(0);

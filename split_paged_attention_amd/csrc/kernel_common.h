@@ -40,6 +40,15 @@ template <int AUX = 0>
 __device__ __forceinline__ float buf_ldf(__amdgpu_buffer_rsrc_t r, int off, int soff) {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, AUX));
 }
+// 16 bytes per lane straight into LDS: lane l's bytes land at lds + 16 l
+// (lds is uniform); bytes past the resource's range arrive as zeros.
+// Completion is counted by vmcnt like any other load.
+template <int AUX = 0>
+__device__ __forceinline__ void buf_ld16_lds(__amdgpu_buffer_rsrc_t r, void *lds, int off,
+                                             int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16,
+                                             off, soff, 0, AUX);
+}
 
 // Word 3 of a gfx9 buffer resource for raw (untyped, unswizzled) access:
 // data format field = 32-bit, so dword loads of any width are range checked
