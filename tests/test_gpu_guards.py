@@ -86,3 +86,33 @@ def test_lengths_clamped_to_the_page_table(kv, producer):
     compare_attention(out, lse, o_ref, l_ref, label=f"clamped lengths {kv} {producer}")
     assert np.isneginf(lse.cpu().numpy()[1]).all()
     assert not torch.any(out[1].float() != 0)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8"])
+def test_multi_token_bad_page_ids_read_as_zero_pages(kv):
+    """The same guard in the multi-token decode kernel (up to 4 query rows
+    per request, causal among them)."""
+    c = guarded_case(kv)
+    print(f"[case] multi-token bad page ids {kv}", flush=True)
+    npg = c.num_pages
+    pt = c.page_list.copy()
+    bad = [(0, 2, -3), (2, 5, npg), (2, 23, 2**31 - 1), (3, 0, -(2**31))]
+    for b, i, v in bad:
+        assert i < -(-int(c.seq_lens[b]) // c.page_size)
+        pt[b, i] = v
+    pt_ref = pt.copy()
+    for b, i, v in bad:
+        pt_ref[b, i] = npg
+    q_rows, cu = W.verify_queries(c, [4, 1, 3, 2])
+    o_ref, l_ref = oracle.verify_attention(
+        q_rows, with_zero_page(c.k_pages), with_zero_page(c.v_pages), pt_ref, c.seq_lens, cu,
+        num_kv_heads=8, page_size=64, scale=c.scale, kv_dtype=kv,
+        k_scales=None if kv == "bf16" else with_zero_page(c.k_scales),
+        v_scales=None if kv == "bf16" else with_zero_page(c.v_scales))
+    d = DevCase(c)
+    qd = torch.from_numpy(np.ascontiguousarray(q_rows).view(np.int16)).cuda().view(torch.bfloat16)
+    out, lse = spa.paged_verify_attention(qd, d.k, d.v, torch.from_numpy(pt).cuda(), d.seq_lens,
+                                          torch.from_numpy(cu).cuda(), c.num_splits,
+                                          float(c.scale), max_q_len=4, kv_dtype=kv,
+                                          k_scales=d.ks, v_scales=d.vs)
+    compare_attention(out, lse, o_ref, l_ref, label=f"multi-token bad ids {kv}")
