@@ -64,7 +64,8 @@ const char *spa_status_string(spa_status status);
 /* hipError_t of the last call on this host thread that returned SPA_ERR_HIP. */
 int spa_last_hip_error(void);
 
-/* ABI revision of this header; bumped on any signature change. */
+/* ABI revision of this header; bumped on any change of a signature or of a
+ * buffer layout (3: the workspace counter region moved to offset 0). */
 int spa_abi_version(void);
 
 /*
@@ -157,18 +158,27 @@ spa_status spa_build_metadata(
     int64_t swa_out_len, hipStream_t stream);
 
 /*
- * Bytes of workspace spa_paged_decode_attention needs: the per-split partial
- * state (fp32 accumulator [B, Hq, S, D], fp32 max and sum [B, Hq, S]) plus
- * one int32 arrival counter per (batch row, kv head).  0 for invalid sizes.
+ * Bytes of workspace spa_paged_decode_attention needs.  Layout (every
+ * region 256-byte aligned): a counter region of 65536 bytes at offset 0 --
+ * its first batch * num_kv_heads int32 are the arrival counters of a fused
+ * call, one per (batch row, kv head) -- then the per-split partial state
+ * (fp32 accumulator [B, Hq, S, D], fp32 max and sum [B, Hq, S]).  The
+ * counter region has this one size for every shape, and the multi-token
+ * workspace (spa_verify_workspace_bytes) starts with the same region, so no
+ * call of either kind writes partial state where any call's counters live.
+ * 0 for invalid sizes.
  */
 size_t spa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                   int32_t head_dim, int32_t num_splits);
 
 /*
  * Zero a workspace with a fill kernel (capture-safe; no hipMemset).  A new
- * workspace must be zeroed once before its first use; every successful
- * attention call leaves the counters at zero again, so no reset is needed
- * between calls.  bytes must be a multiple of 4.
+ * workspace must be zeroed once before its first use (at least its first
+ * 65536 bytes, the counter region); every successful attention call leaves
+ * the counters at zero again, so no reset is needed between calls -- also
+ * when one workspace, large enough for each, serves calls of different
+ * shapes and both the one-token and the multi-token decode.  bytes must be
+ * a multiple of 4.
  */
 spa_status spa_workspace_reset(void *workspace, size_t bytes, hipStream_t stream);
 
@@ -213,7 +223,9 @@ spa_status spa_workspace_reset(void *workspace, size_t bytes, hipStream_t stream
  * Supported: head_dim 128, page_size 64, num_q_heads == 4 * num_kv_heads,
  * kv_dtype bf16, int8 or fp8, 1 <= num_splits <= 1024
  * (SPA_DECODE_HEAD_GROUPED also needs an even num_kv_heads); otherwise
- * SPA_ERR_UNSUPPORTED.  workspace: spa_decode_workspace_bytes(...) bytes,
+ * SPA_ERR_UNSUPPORTED.  The fused merge needs batch * num_kv_heads <= 16384
+ * (the counter region): above that the default plan merges in a second
+ * launch and SPA_DECODE_FUSED_MERGE is SPA_ERR_UNSUPPORTED.  workspace: spa_decode_workspace_bytes(...) bytes,
  * 16-byte aligned, zeroed before first use (see spa_workspace_reset);
  * concurrent calls must not share a workspace.  batch == 0 returns SPA_OK
  * without launching.
@@ -281,9 +293,11 @@ spa_status spa_paged_decode_partials(const void *q, const void *k_pages, const v
                                      float *partial_sum, hipStream_t stream);
 
 /*
- * Bytes of workspace spa_paged_verify_attention needs: the per-split state
- * of every (query row, head) (fp32 accumulator [total_q, Hq, S, D], fp32 max
- * and sum [total_q, Hq, S]), 256-byte aligned regions.  0 for invalid sizes.
+ * Bytes of workspace spa_paged_verify_attention needs: the 65536-byte
+ * counter region of the decode workspace (unused here, never written), then
+ * the per-split state of every (query row, head) (fp32 accumulator
+ * [total_q, Hq, S, D], fp32 max and sum [total_q, Hq, S]), 256-byte aligned
+ * regions.  0 for invalid sizes.
  */
 size_t spa_verify_workspace_bytes(int32_t total_q, int32_t num_q_heads, int32_t num_kv_heads,
                                   int32_t head_dim, int32_t num_splits);
@@ -296,7 +310,8 @@ size_t spa_verify_workspace_bytes(int32_t total_q, int32_t num_q_heads, int32_t 
  *
  * Request b owns query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 (n_b of
  * them, 0 <= n_b <= max_q_len) and seq_lens[b] = L_b cached tokens, whose
- * last n_b are the query tokens' own.  Query token i (row cu_seqlens_q[b] +
+ * last n_b are the query tokens' own (a speculative-decoding step with k
+ * draft tokens verifies n_b = k + 1 rows).  Query token i (row cu_seqlens_q[b] +
  * i) attends tokens 0 .. L_b - n_b + i:
  *   out[row, h, :] = softmax_t(s_t) . v_t,  lse[row, h] = ln sum_t exp(s_t),
  *   s_t = scale * q[row, h, :] . k_t,  query head h reads kv head h / 4;
@@ -312,13 +327,20 @@ size_t spa_verify_workspace_bytes(int32_t total_q, int32_t num_q_heads, int32_t 
  *   lse         [total_q, num_q_heads] fp32 (output, may be NULL)
  *   other arguments as in spa_paged_decode_attention.
  *
- * Supported: max_q_len 1..4 (n_b above 4 computes only the first 4 rows of
- * the request), head_dim 128, page_size 64, num_q_heads == 4 *
+ * max_q_len (host side, 1..64) bounds n_b: one workgroup takes up to 8 query
+ * tokens of a request (4 when max_q_len <= 4) and reads the request's K and
+ * V once for all of them; a larger max_q_len cuts each request's rows into
+ * chunks of 8, each reading K and V again.  A request whose device data
+ * holds more rows than max_q_len has its first max_q_len rows computed with
+ * the causal limits of all n_b rows, and the rest written as out = 0,
+ * lse = -inf.
+ *
+ * Supported: max_q_len 1..64, head_dim 128, page_size 64, num_q_heads == 4 *
  * num_kv_heads with num_kv_heads even, bf16 / int8 / fp8 KV, 1 <= num_splits
- * <= 1024.  Rows not covered by cu_seqlens_q, and the rows of a request
- * whose span leaves [0, total_q), are left unspecified (never written
- * outside the output).  The workspace needs no zeroing.  batch == 0 or
- * total_q == 0 returns SPA_OK without launching.
+ * <= 1024; otherwise SPA_ERR_UNSUPPORTED.  Rows not covered by cu_seqlens_q,
+ * and the rows of a request whose span leaves [0, total_q), are left
+ * unspecified (never written outside the output).  The workspace needs no
+ * zeroing.  batch == 0 or total_q == 0 returns SPA_OK without launching.
  */
 spa_status spa_paged_verify_attention(const void *q, const void *k_pages, const void *v_pages,
                                       const float *k_scales, const float *v_scales,

@@ -12,14 +12,14 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 WorkspaceLayout workspace_layout(int64_t batch, int64_t hq, int64_t hkv, int64_t head_dim,
                                  int64_t splits) {
+    (void)hkv;   // the counter region has one size for every shape
     WorkspaceLayout w{};
     const size_t rows = (size_t)batch * (size_t)hq * (size_t)splits;
-    w.acc_off = 0;
+    w.cnt_off = 0;
+    w.acc_off = kCounterRegionBytes;
     w.max_off = align256(w.acc_off + rows * (size_t)head_dim * sizeof(float));
     w.sum_off = align256(w.max_off + rows * sizeof(float));
-    w.cnt_off = align256(w.sum_off + rows * sizeof(float));
-    w.total = align256(w.cnt_off + (size_t)batch * (size_t)hkv * sizeof(int32_t));
-    if (w.total == 0) w.total = 256;   // a valid request never needs 0 bytes
+    w.total = align256(w.sum_off + rows * sizeof(float));
     return w;
 }
 
@@ -58,7 +58,8 @@ DecodePlan default_plan(int32_t batch, int32_t hkv, int32_t splits, int kv_type,
     DecodePlan plan{};
     plan.kv_type = kv_type;
     plan.mode = spa::default_mode(batch, hkv, splits, kv_type, pt_stride);
-    plan.fused = plan.mode == spa::DecodeMode::kPageSplit && splits <= 8;
+    plan.fused = plan.mode == spa::DecodeMode::kPageSplit && splits <= 8 &&
+                 (int64_t)batch * hkv <= spa::kMaxCounterGroups;
     return plan;
 }
 
@@ -101,6 +102,11 @@ spa_status decode_setup(const void *q, const void *k_pages, const void *v_pages,
     if (flags & SPA_DECODE_SEPARATE_MERGE) plan->fused = false;
     if (flags & SPA_DECODE_FUSED_MERGE) plan->fused = true;
     if (producer_only) plan->fused = false;
+    // the fused merge needs one arrival counter per (request, kv head)
+    if (plan->fused && (int64_t)batch * num_kv_heads > spa::kMaxCounterGroups) {
+        if (flags & SPA_DECODE_FUSED_MERGE) return SPA_ERR_UNSUPPORTED;
+        plan->fused = false;
+    }
     if (batch == 0) return SPA_OK;
     if (!spa::mode_supported(plan->mode, num_kv_heads)) return SPA_ERR_UNSUPPORTED;
     if (!q || !k_pages || !v_pages || !page_table || !seq_lens) return SPA_ERR_INVALID_ARGUMENT;
@@ -143,7 +149,7 @@ const char *spa_status_string(spa_status status) {
 
 int spa_last_hip_error(void) { return g_last_hip_error; }
 
-int spa_abi_version(void) { return 2; }
+int spa_abi_version(void) { return 3; }
 
 spa_status spa_build_metadata(
     const int32_t *req_to_token, int64_t req_to_token_stride, int32_t pool_size,
@@ -341,9 +347,11 @@ spa_status spa_paged_verify_attention(const void *q, const void *k_pages, const 
     if (!isfinite(scale)) return SPA_ERR_INVALID_ARGUMENT;
     if (head_dim != spa::kHeadDim || page_size != spa::kPageSize ||
         num_q_heads != spa::kGroup * num_kv_heads || num_splits > 1024 ||
-        max_q_len > spa::kMaxVerifyQueries || !spa::verify_supported(num_kv_heads))
+        max_q_len > spa::kMaxVerifyQueryLen || !spa::verify_supported(num_kv_heads))
         return SPA_ERR_UNSUPPORTED;
-    if ((int64_t)batch * num_kv_heads * num_splits > (int64_t)INT32_MAX ||
+    const int64_t qt = spa::verify_tokens_per_workgroup(max_q_len);
+    const int64_t chunks = (max_q_len + qt - 1) / qt;
+    if ((int64_t)batch * num_kv_heads * num_splits * chunks > (int64_t)INT32_MAX ||
         (int64_t)total_q * num_q_heads > (int64_t)INT32_MAX)
         return SPA_ERR_UNSUPPORTED;
     if (batch == 0 || total_q == 0) return SPA_OK;
@@ -384,11 +392,7 @@ spa_status spa_paged_verify_attention(const void *q, const void *k_pages, const 
     p.lse = lse;
     p.cu_seqlens_q = cu_seqlens_q;
     p.total_q = total_q;
-    return hip_status(spa::launch_verify(p,
-                                         kv_dtype == SPA_KV_INT8 ? spa::kKvInt8
-                                         : kv_dtype == SPA_KV_FP8 ? spa::kKvFp8
-                                                                  : spa::kKvBf16,
-                                         stream));
+    return hip_status(spa::launch_verify(p, kv_type_of(kv_dtype), max_q_len, stream));
 }
 
 spa_status spa_split_merge(const float *partial_acc, const float *partial_max,

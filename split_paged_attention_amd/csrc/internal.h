@@ -12,11 +12,19 @@ namespace spa {
 constexpr int kHeadDim = 128;
 constexpr int kPageSize = 64;
 constexpr int kGroup = 4;       // query heads per kv head
-constexpr int kMaxVerifyQueries = 4;   // query tokens per request, multi-token decode
+// Multi-token decode: query tokens per request the host may declare
+// (max_q_len); one workgroup takes up to 8 of them, more are cut into chunks.
+constexpr int kMaxVerifyQueryLen = 64;
 
-// Workspace layout for a decode call (byte offsets, each region 256-aligned).
+// Workspace layout of the decode and multi-token decode calls (byte
+// offsets, each region 256-aligned).  The counter region comes first and has
+// one size for every shape and entry point, so no call writes partial state
+// where any call's counters live: a workspace shared by calls of different
+// shapes, or by one-token and multi-token calls, keeps its counters at zero.
+constexpr size_t kCounterRegionBytes = 65536;
+constexpr int64_t kMaxCounterGroups = (int64_t)(kCounterRegionBytes / sizeof(int32_t));
 struct WorkspaceLayout {
-    size_t acc_off, max_off, sum_off, cnt_off, total;
+    size_t cnt_off, acc_off, max_off, sum_off, total;
 };
 WorkspaceLayout workspace_layout(int64_t batch, int64_t hq, int64_t hkv, int64_t head_dim,
                                  int64_t splits);
@@ -44,6 +52,8 @@ struct DecodeParams {
     // cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 of total_q
     const int32_t *cu_seqlens_q;
     int32_t total_q;
+    int32_t max_q_len;         // query rows computed per request (more get the empty state)
+    int32_t q_chunks;          // query-token chunks per request (grid dimension)
 };
 
 // cu_seqlens_q handling of the metadata build.
@@ -100,9 +110,11 @@ hipError_t launch_decode(const DecodeParams &p, int kv_type, DecodeMode mode, bo
 hipError_t launch_decode_producer(const DecodeParams &p, int kv_type, DecodeMode mode,
                                   hipStream_t stream);
 
-// Multi-token decode producer (2 kv heads per workgroup) + split merge over
-// total_q * hq rows; partial state rows are query rows.
-hipError_t launch_verify(const DecodeParams &p, int kv_type, hipStream_t stream);
+// Multi-token decode producer (2 kv heads per workgroup, 4 or 8 query tokens
+// of a request per workgroup, more in chunks) + split merge over total_q * hq
+// rows; partial state rows are query rows.
+int verify_tokens_per_workgroup(int max_q_len);
+hipError_t launch_verify(const DecodeParams &p, int kv_type, int max_q_len, hipStream_t stream);
 bool verify_supported(int hkv);
 
 hipError_t launch_split_merge(const float *acc, const float *mx, const float *sum,

@@ -80,15 +80,36 @@ def compare_attention(out_dev, lse_dev, o_ref, l_ref, rows=None, label=""):
     err = np.abs(o - o_ref)
     eo = float(np.max(err)) if o.size else 0.0
     el = float(np.max(np.abs(l[fin] - l_ref[fin]))) if fin.any() else 0.0
-    # The bound cannot be finer than the bf16 output's own spacing: where one
-    # bf16 ulp of the exact value exceeds OUT_ATOL (|o| >= 2), one ulp is allowed.
-    tol = np.maximum(OUT_ATOL, bf16_ulp(o_ref))
+    tol = out_tolerance(o_ref)
     worst = float(np.max(err / tol)) if o.size else 0.0
-    print(f"[parity] {label}: max|out-oracle|={eo:.3e} (max err/tol {worst:.3f}) "
-          f"max|lse-oracle|={el:.3e}", flush=True)
+    # strict: the error where the stated 1e-2 is reachable at all (|o| < 4)
+    small = np.abs(o_ref) < STRICT_BELOW
+    es = float(np.max(err[small])) if small.any() else 0.0
+    print(f"[parity] {label}: max|out-oracle|={eo:.3e} (|o|<4: {es:.3e}; max err/tol "
+          f"{worst:.3f}) max|lse-oracle|={el:.3e}", flush=True)
     assert np.all(err <= tol), f"{label}: out error {eo}, err/tol {worst}"
     assert el <= LSE_ATOL, f"{label}: lse error {el}"
     return eo, el
+
+
+# Per-element gate on a bf16 output against the exact value o.  Below
+# |o| = 4 it is the stated 1e-2: there half a bf16 step is at most 2^-7 =
+# 0.0078, so a correctly rounded output can meet it.  From |o| = 4 on half a
+# step is 2^-6 = 0.0156 and no bf16 value need lie within 1e-2; there the
+# kernel's own bound applies: it forms o' in fp32 and rounds it once, so
+# |bf16(o') - o| <= half a bf16 step at |o'| plus |o' - o|, the pre-rounding
+# slack s = 1e-3 (fp32 accumulation) + 2^-11 |o| (the probabilities of P.V
+# are rounded to f16 for 1-byte KV).
+PRE_ROUND_ABS = 1e-3
+PRE_ROUND_REL = 2.0 ** -11
+STRICT_BELOW = 4.0
+
+
+def out_tolerance(o_ref):
+    ao = np.abs(np.asarray(o_ref, dtype=np.float64))
+    s = PRE_ROUND_ABS + PRE_ROUND_REL * ao
+    return np.where(ao < STRICT_BELOW, OUT_ATOL,
+                    np.maximum(OUT_ATOL, 0.5 * bf16_ulp(ao + s) + s))
 
 
 def bf16_ulp(x):
@@ -97,14 +118,11 @@ def bf16_ulp(x):
     return 2.0 ** (np.floor(np.log2(ax)) - 7)
 
 
-def counters_view(ws: torch.Tensor, batch, hq, hkv, d, splits) -> torch.Tensor:
-    """The arrival-counter region of a decode workspace (layout of the C ABI:
-    acc | max | sum | counters, each 256-byte aligned)."""
-    def a256(x):
-        return (x + 255) & ~255
-    rows = batch * hq * splits
-    acc = rows * d * 4
-    mo = a256(acc)
-    so = a256(mo + rows * 4)
-    co = a256(so + rows * 4)
-    return ws[co:co + batch * hkv * 4].view(torch.int32)
+# The counter region of a decode / multi-token workspace (C ABI layout: a
+# fixed 64 KiB of int32 counters first, then the partial state).
+COUNTER_REGION_BYTES = 65536
+
+
+def counters_view(ws: torch.Tensor) -> torch.Tensor:
+    """The whole arrival-counter region of a workspace, as int32."""
+    return ws[:COUNTER_REGION_BYTES].view(torch.int32)

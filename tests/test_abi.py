@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
     for n in declared_functions():
         assert n in exported, n
         assert hasattr(L, n)
-    assert L.spa_abi_version() == 2
+    assert L.spa_abi_version() == 3
 
 
 def test_status_strings():
@@ -240,7 +240,7 @@ def _verify(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(mq=0), spa.SPA_ERR_INVALID_ARGUMENT),
-    (dict(mq=5), spa.SPA_ERR_UNSUPPORTED),
+    (dict(mq=65), spa.SPA_ERR_UNSUPPORTED),
     (dict(T=-1), spa.SPA_ERR_INVALID_ARGUMENT),
     (dict(cu=None), spa.SPA_ERR_INVALID_ARGUMENT),
     (dict(Hq=12, Hkv=3), spa.SPA_ERR_UNSUPPORTED),            # odd kv heads

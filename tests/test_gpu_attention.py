@@ -10,7 +10,7 @@ import oracle
 import split_paged_attention_amd as spa
 import workloads as W
 from tests.gpu_util import (DevCase, bf16_dev, bits_host, compare_attention, config_case,
-                            counters_view)
+                            counters_view, COUNTER_REGION_BYTES)
 
 pytestmark = pytest.mark.gpu
 
@@ -180,7 +180,7 @@ def test_repeat_bit_identical_and_counters_return_to_zero():
         o, l = d.attention(workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(o.view(torch.int16), o0.view(torch.int16)) and torch.equal(l, l0)
-    assert int(counters_view(ws, B, Hq, c.num_kv_heads, D, S).abs().sum()) == 0
+    assert int(counters_view(ws).abs().sum()) == 0
 
 
 def test_alternating_inputs_share_one_workspace():
@@ -202,15 +202,51 @@ def test_alternating_inputs_share_one_workspace():
         assert torch.equal(l, ref[1]), it
 
 
+def test_one_workspace_serves_every_shape_and_entry_point():
+    """One workspace, sized for the largest call, serves in turn fused
+    decode calls of two batch sizes, a multi-token decode call and a
+    separate-merge call.  The counters sit in a region no call writes partial
+    state to, so every fused call still merges exactly once: each output
+    equals that of the same call on a fresh workspace, bit for bit, and the
+    counters end at zero."""
+    ca = small_case([3000, 700, 65, 1], S=8, seed=41)           # 4 requests
+    cb = small_case([900, 64, 1, 2500, 130, 7, 4000, 12, 640], S=8, seed=42)   # 9
+    print("[case] one workspace: fused decode at two batch sizes + multi-token + separate",
+          flush=True)
+    da, db = DevCase(ca), DevCase(cb)
+    q_rows, cu = W.verify_queries(cb, [3, 1, 1, 4, 2, 0, 4, 1, 2])
+    qv, cuv = bf16_dev(q_rows), torch.from_numpy(cu).cuda()
+    T = q_rows.shape[0]
+
+    def verify(ws):
+        return spa.paged_verify_attention(qv, db.k, db.v, db.page_list, db.seq_lens, cuv, 8,
+                                          float(cb.scale), max_q_len=4, workspace=ws)
+
+    calls = [lambda ws: da.attention(merge="fused", producer="page_split", workspace=ws),
+             lambda ws: db.attention(merge="fused", producer="page_split", workspace=ws),
+             verify,
+             lambda ws: da.attention(merge="separate", producer="head_grouped", workspace=ws),
+             lambda ws: db.attention(merge="fused", producer="head_grouped", workspace=ws)]
+    refs = [f(spa.new_workspace(40, 32, 8, 128, 8)) for f in calls]
+    nbytes = max(spa.decode_workspace_bytes(cb.batch, 32, 8, 128, 8),
+                 spa.verify_workspace_bytes(T, 32, 8, 128, 8))
+    ws = torch.zeros((nbytes,), dtype=torch.uint8, device="cuda")
+    for it in range(3):
+        for k, f in enumerate(calls):
+            o, l = f(ws)
+            torch.cuda.synchronize()
+            assert torch.equal(o.view(torch.int16), refs[k][0].view(torch.int16)), (it, k)
+            assert torch.equal(l, refs[k][1]), (it, k)
+    assert int(counters_view(ws).abs().sum()) == 0
+
+
 def test_nan_poisoned_partials_region_is_never_read_before_write():
     c = small_case([1500, 2, 640], S=8)
     print("[case] NaN-poisoned workspace", flush=True)
     d = DevCase(c)
     B, Hq, D, S = c.batch, c.num_q_heads, c.head_dim, c.num_splits
     ws = spa.new_workspace(B, Hq, c.num_kv_heads, D, S)
-    cnt = counters_view(ws, B, Hq, c.num_kv_heads, D, S)
-    nbytes = cnt.data_ptr() - ws.data_ptr()
-    ws[:nbytes].view(torch.float32).fill_(float("nan"))
+    ws[COUNTER_REGION_BYTES:].view(torch.float32).fill_(float("nan"))
     out, lse = d.attention(workspace=ws)
     o_ref, l_ref = oracle.case_attention(c)
     compare_attention(out, lse, o_ref, l_ref, label="poisoned")
@@ -352,7 +388,7 @@ def test_hip_graph_replay_matches_eager():
         assert torch.equal(lse, l_eager)
         step()   # eager work between replays
         torch.cuda.synchronize()
-    assert int(counters_view(ws, B, Hq, c.num_kv_heads, D, S).abs().sum()) == 0
+    assert int(counters_view(ws).abs().sum()) == 0
 
 
 # ---------------------------------------------------------------- other batch and head shapes
