@@ -515,7 +515,7 @@ def main() -> int:
     ap.add_argument("--policy-sweep", choices=["bf16", "int8", "fp8"], default=None,
                     help="time both producers and merges over a grid of decode shapes")
     ap.add_argument("--verify-qlen", type=int, default=0,
-                    help="multi-token decode with this many query tokens per request (1..4)")
+                    help="multi-token decode with this many query tokens per request (1..64)")
     args = ap.parse_args()
 
     if args.summarize_trace:
@@ -556,8 +556,8 @@ def main() -> int:
     case = W.make_config(args.config)
     gen_s = time.time() - t_gen
     Q = args.verify_qlen
-    if Q < 0 or Q > 4:
-        print("--verify-qlen must be 0..4", file=sys.stderr)
+    if Q < 0 or Q > 64:
+        print("--verify-qlen must be 0..64", file=sys.stderr)
         return 2
     rig = Rig(case, qlen=Q)
     dev = "cuda:0"

@@ -421,7 +421,7 @@ def paged_verify_attention(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torc
                            stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """spa_paged_verify_attention (multi-token decode).  q [total_q, Hq, D]
     bf16; cu_seqlens_q [batch + 1] int32 (request b's query rows
-    cu[b] .. cu[b+1]-1, at most max_q_len of them); the rest as in
+    cu[b] .. cu[b+1]-1, at most max_q_len <= 64 of them); the rest as in
     paged_decode_attention.  Returns (out [total_q, Hq, D] bf16,
     lse [total_q, Hq] fp32)."""
     _need(q, "q", torch.bfloat16)

@@ -1,28 +1,33 @@
 // Multi-token query decode (target verify / draft extend) over the paged KV
 // cache, split-K like the one-token decode.
 //
-// Request b owns query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 (n_b <= 4
-// of them); the last n_b of its L_b cached tokens are those queries' own, so
+// Request b owns query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 (n_b of
+// them); the last n_b of its L_b cached tokens are those queries' own, so
 // query token i sees tokens 0 .. L_b - n_b + i (sglang's fused metadata
 // update prepares cu_seqlens_q for exactly these steps: module docstring and
 // the cumsum branch's Q modes).
 //
-// A workgroup is one (request, block of 2 kv heads, split); wave w is kv head
-// 2*block + w and walks the split's pages.  Per page:
-//   * QK^T on the matrix cores with the 16 MFMA rows = 4 heads x 4 query
-//     tokens (row 4i + h: token i, head h), so all of a request's query
-//     tokens cost what one does; lane group g then holds query token g's
-//     scores and keeps its own online-softmax state, with the causal limit
-//     of token g applied as a mask;
+// A workgroup is one (request, block of 2 kv heads, split, chunk of up to
+// 4 RB query tokens); wave w is kv head 2*block + w and walks the split's
+// pages.  Per page:
+//   * QK^T on the matrix cores in RB blocks of 16 MFMA rows, each 4 heads x
+//     4 query tokens (row 4i + h of block r: token 4r + i, head h), all
+//     blocks sharing every K operand, so the chunk's query tokens read K and
+//     V once; lane group g then holds the scores of query tokens 4r + g and
+//     keeps their online-softmax states, each with its own causal limit as a
+//     mask;
 //   * P.V on the matrix cores too: the page's V goes from registers
 //     (loaded a page ahead) into a per-wave LDS tile, token-major (1-byte
 //     codes converted to exact f16 on the way), the probabilities into a
 //     token-major per-wave LDS tile, and the transposed LDS read
 //     (ds_read_b64_tr_b16) turns both into MFMA operands: O[16 rows][128
 //     dims] += P[16 rows][32 tokens] x V[32 tokens][128 dims], 16 MFMAs per
-//     page, with the output rows in the same lanes as the softmax state.
-// The partial states go to the workspace and the ordinary split merge
-// combines them, one (query row, head) at a time.
+//     page and row block, the V operands shared by the blocks, with the
+//     output rows in the same lanes as the softmax state.
+// A request with more query tokens than one workgroup takes is cut into
+// chunks of 4 RB tokens (a grid dimension); each chunk reads the request's
+// K and V again.  The partial states go to the workspace and the ordinary
+// split merge combines them, one (query row, head) at a time.
 #include "internal.h"
 #include "kernel_common.h"
 
@@ -30,9 +35,10 @@ namespace spa {
 namespace {
 
 constexpr int kVerifyWaves = 2;   // kv heads per workgroup, one per wave
-// One stashed split state of a wave: 32 accumulators per lane (64 lanes),
-// then the 16 rows' maxima and sums.
-constexpr int kVerifyStashFloats = 32 * 64 + 32;
+// One stashed split state of a wave: 32 accumulators per lane (64 lanes) and
+// row block, then the maxima and sums of the RB blocks' 16 rows.
+template <int RB>
+constexpr int verify_stash_floats() { return RB * (32 * 64 + 32); }
 
 // Transposed LDS read of 4 16-bit elements (see the addressing in the kernel).
 __device__ __forceinline__ uint64_t tr_read(const uint16_t *p) {
@@ -52,11 +58,16 @@ __device__ __forceinline__ f16x8_t join_f16x8(uint64_t lo, uint64_t hi) {
 }
 
 // KV: 0 = bf16 pages, 1 = int8 codes, 2 = e4m3 codes (with fp32 scales).
-template <int KV>
-__global__ __launch_bounds__(kVerifyWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+// RB: row blocks of 4 query tokens x 4 heads; a workgroup takes 4 RB tokens.
+// Two blocks hold twice the accumulators, so they run one wave per SIMD.
+template <int KV, int RB>
+__global__ __launch_bounds__(kVerifyWaves * 64) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 2 : 1)))
 void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
                    const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ cu_q) {
     constexpr int D = kHeadDim, P = kPageSize, NW = kVerifyWaves;
+    constexpr int QT = 4 * RB;                   // query tokens per workgroup
+    constexpr int PW = 16 * RB;                  // P tile width: the blocks' MFMA rows
+    constexpr int STASH = verify_stash_floats<RB>();
     constexpr bool QUANT = KV != 0;
     constexpr bool I8 = KV == 1;
     // Default cache policy for K/V (streaming them, which helps the bf16
@@ -65,15 +76,19 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
     constexpr int ES = QUANT ? 1 : 2;            // bytes per element
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // QK layout: lane (n, g) = KV token n of a 16-token block, query token g;
-    // the P.V output has the same rows in the same lanes, with dims 16 blk + n.
-    // V registers: lane (g, n) holds token 4i + g, dims 8n .. 8n+7.
+    // QK layout: lane (n, g) = KV token n of a 16-token block, query token
+    // 4 rb + g of row block rb; the P.V output has the same rows in the same
+    // lanes, with dims 16 blk + n.  V registers: lane (g, n) holds token
+    // 4i + g, dims 8n .. 8n+7.
     const int n = lane & 15, g = lane >> 4;
 
-    // blockIdx -> (group = b * blocks + kv block, split j), placed on the 8
-    // XCDs as in the one-token decode: for 1-byte codes and a batch that is
-    // a multiple of 8, all kv blocks and splits of a request share an XCD;
-    // otherwise the S splits of a group do when the group count allows.
+    // blockIdx -> (query-token chunk, group = b * blocks + kv block, split j).
+    // The chunk is the slowest dimension; within a chunk the workgroups are
+    // placed on the 8 XCDs as in the one-token decode: for 1-byte codes and a
+    // batch that is a multiple of 8, all kv blocks and splits of a request
+    // share an XCD; otherwise the S splits of a group do when the group count
+    // allows.  Both placements need a chunk size that is a multiple of 8, so
+    // the XCD of a block id is that of its offset in the chunk.
     const int S = p.splits;
     // bf16: a workgroup may walk `walk` consecutive splits (S a multiple of
     // it) with one page pipeline, as the one-token decode does: the states
@@ -83,9 +98,10 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
     const int SG = S / walk;
     const int grp_per_b = p.hkv / NW;
     const int ngroups = p.batch * grp_per_b;
+    const int chunk = blockIdx.x / (ngroups * SG);
     int grp, j;
     {
-        const int bid = blockIdx.x;
+        const int bid = blockIdx.x - chunk * ngroups * SG;
         const int xcd = bid & 7, slot = bid >> 3;
         if (QUANT && (p.batch & 7) == 0) {
             j = slot % SG;
@@ -112,8 +128,8 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
     const int q0 = cu_q[b];
     int nq = cu_q[b + 1] - q0;
     if (q0 < 0 || nq < 0 || q0 > p.total_q - nq) nq = 0;
-    nq = min(nq, kMaxVerifyQueries);
-    if (nq == 0) return;   // the whole workgroup
+    const int c0 = chunk * QT;                  // this chunk's first query token
+    const int nqc = min(min(nq, p.max_q_len) - c0, QT);   // its query tokens (none if <= 0)
 
     int L = seq_lens[b];
     L = (int)min((int64_t)max(L, 0), p.pt_stride * P);
@@ -123,75 +139,116 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
     const int pg1 = min(j * pps + walk * pps, pages);   // end of this workgroup's pages
     int jcur = j;                                        // split being accumulated
     int split_end = min(pg0 + pps, pages);               // its end page
+
+    // One (query row, this wave's kv head) state of split jw: acc values of
+    // head h at dims 16 blk + n from av(h, blk), m and l from lane n == 0.
+    auto put_state = [&](int row, int jw, auto av, const float (&mh)[4], const float (&lh)[4]) {
+        const int64_t row0 = ((int64_t)row * p.hq + kvh * kGroup) * S + jw;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            const int64_t idx = row0 + (int64_t)h * S;
+            float *dst = p.part_acc + idx * D + n;
+#pragma unroll
+            for (int blk = 0; blk < 8; ++blk) dst[16 * blk] = av(h, blk);
+            if (n == 0) {
+                p.part_max[idx] = mh[h] == kNegInf ? kNegInf : mh[h] * kLn2;
+                p.part_sum[idx] = lh[h];
+            }
+        }
+    };
+    const float kEmptyM[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+    const float kEmptyL[4] = {0.f, 0.f, 0.f, 0.f};
+    auto zero_acc = [](int, int) { return 0.f; };
+    // Rows past the declared maximum max_q_len (a request with more query
+    // tokens in the device data) get the empty state, so the merge gives
+    // them out = 0 and lse = -inf instead of reading stale workspace.
+    if (chunk == p.q_chunks - 1) {
+        for (int i = p.max_q_len + g; i < nq; i += 4)
+            for (int jw = j; jw < j + walk; ++jw) put_state(q0 + i, jw, zero_acc, kEmptyM, kEmptyL);
+    }
+    if (nqc <= 0) return;   // the whole workgroup
+
     extern __shared__ __attribute__((aligned(16))) float vstash[];
     int nstash = 0;
     const int row_stride = p.hkv * D;
-    const int vis = L - nq + g + 1;             // query token g sees tokens < vis
+    // query token 4 rb + g of this chunk sees tokens < vis[rb]
+    int vis[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) vis[rb] = L - nq + c0 + 4 * rb + g + 1;
 
-    // A operand: row n is head n & 3 of query token n >> 2 (rows of tokens
-    // past n_b repeat the last one and are never stored).  Same contraction
-    // order as the one-token decode.
-    bf16x8_t qa[4];
-    {
-        const int tq = min(n >> 2, nq - 1);
+    // A operand of block rb: row n is head n & 3 of query token 4 rb + n / 4
+    // (rows of tokens past the chunk's last repeat it and are never stored).
+    // Same contraction order as the one-token decode.
+    bf16x8_t qa[RB][4];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const int tq = min(4 * rb + (n >> 2), nqc - 1);
         const uint16_t *qp = reinterpret_cast<const uint16_t *>(p.q) +
-                             ((int64_t)(q0 + tq) * p.hq + kvh * kGroup + (n & 3)) * D;
+                             ((int64_t)(q0 + c0 + tq) * p.hq + kvh * kGroup + (n & 3)) * D;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int d0 = QUANT ? 64 * (c >> 1) + 16 * g + 8 * (c & 1) : 32 * c + 8 * g;
-            qa[c] = *reinterpret_cast<const bf16x8_t *>(qp + d0);
+            qa[rb][c] = *reinterpret_cast<const bf16x8_t *>(qp + d0);
         }
     }
     // 1-byte codes: the query goes to f16, each row scaled by a power of two
-    // putting its largest |q| in [2^14, 2^15) (exact); score row 4g + h is
-    // unscaled with the factor of lane 4g + h.
-    f16x8_t qa16[4];
-    float qscale[4];
+    // putting its largest |q| in [2^14, 2^15) (exact); score row 4g + h of
+    // block rb is unscaled with the factor of lane 4g + h.
+    f16x8_t qa16[RB][4];
+    float qscale[RB][4];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) qscale[h] = p.qk_scale_log2;
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int h = 0; h < 4; ++h) qscale[rb][h] = p.qk_scale_log2;
     if constexpr (QUANT) {
-        float amax = 0.f;
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+        for (int rb = 0; rb < RB; ++rb) {
+            float amax = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)qa[c][e]));
-        amax = fmaxf(amax, __shfl_xor(amax, 16));
-        amax = fmaxf(amax, __shfl_xor(amax, 32));   // lane n: row n, all 128 dims
-        const int sh = amax > 0.f ? 15 - __builtin_amdgcn_frexp_expf(amax) : 0;
-        const float up = __builtin_ldexpf(1.f, sh);
+            for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+                for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)qa[rb][c][e]));
+            amax = fmaxf(amax, __shfl_xor(amax, 16));
+            amax = fmaxf(amax, __shfl_xor(amax, 32));   // lane n: row n, all 128 dims
+            const int sh = amax > 0.f ? 15 - __builtin_amdgcn_frexp_expf(amax) : 0;
+            const float up = __builtin_ldexpf(1.f, sh);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) qa16[c][e] = (_Float16)((float)qa[c][e] * up);
+            for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int h = 0; h < 4; ++h)
-            qscale[h] = p.qk_scale_log2 * __builtin_ldexpf(1.f, -__shfl(sh, 4 * g + h));
+                for (int e = 0; e < 8; ++e) qa16[rb][c][e] = (_Float16)((float)qa[rb][c][e] * up);
+#pragma unroll
+            for (int h = 0; h < 4; ++h)
+                qscale[rb][h] = p.qk_scale_log2 * __builtin_ldexpf(1.f, -__shfl(sh, 4 * g + h));
+        }
     }
 
-    // softmax state of row (query token g, head h); acc[blk][h] = output
-    // row (g, h), dim 16 blk + n (the MFMA output layout)
-    float m[4], lpart[4];
-    f32x4_t acc[8];
+    // softmax state of row (query token 4 rb + g, head h); acc[rb][blk] =
+    // output row (4 rb + g, h), dim 16 blk + n (the MFMA output layout)
+    float m[RB][4], lpart[RB][4];
+    f32x4_t acc[RB][8];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-        m[h] = kNegInf;
-        lpart[h] = 0.f;
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            m[rb][h] = kNegInf;
+            lpart[rb][h] = 0.f;
+        }
+#pragma unroll
+        for (int blk = 0; blk < 8; ++blk) acc[rb][blk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-#pragma unroll
-    for (int blk = 0; blk < 8; ++blk) acc[blk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     // Per-wave LDS tiles, 16-bit elements, token-major: half a page of V
     // (32 tokens x 128 dims, bf16 or the f16 values of the codes; the two
-    // halves take turns) and P[64 tokens][16 rows].
+    // halves take turns) and P[64 tokens][16 RB rows].
     // V rows are padded by 16 elements (32 bytes): the 4 rows a transposed
     // read touches per 16 lanes then sit 8 banks apart instead of on the same
     // banks (bank-conflict cycles per call at batch 32 / 8K / 4 tokens: 16.5M
     // unpadded, 3.9M padded; the call time did not change).
     constexpr int VROW = D + 16;
     __shared__ __attribute__((aligned(16))) uint16_t vbuf[NW][P / 2][VROW];
-    __shared__ __attribute__((aligned(16))) uint16_t pbuf[NW][P][16];
+    __shared__ __attribute__((aligned(16))) uint16_t pbuf[NW][P][PW];
     uint16_t(*vt)[VROW] = vbuf[wave];
-    uint16_t(*pt16)[16] = pbuf[wave];
+    uint16_t(*pt16)[PW] = pbuf[wave];
     // Transposed-read addressing: lane 16G + 4e + qd supplies row 8G + e
     // (+ 4 for the second read), columns 4qd .. 4qd+3; lane 16G + i then
     // receives column i of rows 8G .. 8G+3 (8G+4 .. 8G+7): the MFMA operand
@@ -308,71 +365,86 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
         load_v(page_next, valid_next, 0);
         __builtin_amdgcn_sched_barrier(0);
 
-        // ---- S = Q K^T: lane (n, g) gets s[token g, head h][KV token 16t + n]
-        f32x4_t sacc[4];
+        // ---- S = Q K^T: lane (n, g) gets s[query token 4 rb + g, head h]
+        // [KV token 16t + n] in sacc[rb][t][h]; each K operand feeds every block
+        f32x4_t sacc[RB][4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            sacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) sacc[rb][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 if constexpr (!QUANT) {
-                    sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        qa[c], __builtin_bit_cast(bf16x8_t, kr[t][c]), sacc[t], 0, 0, 0);
+                    const bf16x8_t kb = __builtin_bit_cast(bf16x8_t, kr[t][c]);
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb)
+                        sacc[rb][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rb][c], kb,
+                                                                              sacc[rb][t], 0, 0, 0);
                 } else {
                     const uint4 w = kr8[t][c >> 1];
                     const uint2 h = (c & 1) ? make_uint2(w.z, w.w) : make_uint2(w.x, w.y);
-                    sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                        qa16[c], I8 ? i8x8_to_f16(h) : e4m3x8_to_f16(h), sacc[t], 0, 0, 0);
+                    const f16x8_t kb = I8 ? i8x8_to_f16(h) : e4m3x8_to_f16(h);
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb)
+                        sacc[rb][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa16[rb][c], kb,
+                                                                             sacc[rb][t], 0, 0, 0);
                 }
             }
         }
-        float s[4][4];
+        float s[RB][4][4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int tok = 16 * t + n;
-            const bool ok = tok < valid && pg * P + tok < vis;
             const float kt = QUANT ? lane_value(ksc_tok, tok) : 1.f;
 #pragma unroll
-            for (int h = 0; h < 4; ++h) s[t][h] = ok ? sacc[t][h] * (qscale[h] * kt) : kNegInf;
+            for (int rb = 0; rb < RB; ++rb) {
+                const bool ok = tok < valid && pg * P + tok < vis[rb];
+#pragma unroll
+                for (int h = 0; h < 4; ++h)
+                    s[rb][t][h] = ok ? sacc[rb][t][h] * (qscale[rb][h] * kt) : kNegInf;
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
         load_k(page_next, valid_next);
         __builtin_amdgcn_sched_barrier(0);
 
-        // ---- online softmax (base 2) per (query token g, head h); a row
-        // that has seen no token yet keeps m = -inf and weights 0
-        float alpha[4], pv[4][4];
+        // ---- online softmax (base 2) per (query token, head); a row that
+        // has seen no token yet keeps m = -inf and weights 0
+        float alpha[RB][4], pv[RB][4][4];
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-            float mx = fmaxf(fmaxf(s[0][h], s[1][h]), fmaxf(s[2][h], s[3][h]));
-            mx = row_max16(mx);
-            const float mnew = fmaxf(m[h], mx);
-            const float mref = mnew == kNegInf ? 0.f : mnew;
-            alpha[h] = exp2_fast(m[h] - mref);
-            m[h] = mnew;
-            float rs = 0.f;
+        for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                pv[t][h] = exp2_fast(s[t][h] - mref);
-                rs += pv[t][h];
+            for (int h = 0; h < 4; ++h) {
+                float mx = fmaxf(fmaxf(s[rb][0][h], s[rb][1][h]), fmaxf(s[rb][2][h], s[rb][3][h]));
+                mx = row_max16(mx);
+                const float mnew = fmaxf(m[rb][h], mx);
+                const float mref = mnew == kNegInf ? 0.f : mnew;
+                alpha[rb][h] = exp2_fast(m[rb][h] - mref);
+                m[rb][h] = mnew;
+                float rs = 0.f;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    pv[rb][t][h] = exp2_fast(s[rb][t][h] - mref);
+                    rs += pv[rb][t][h];
+                }
+                lpart[rb][h] = __builtin_fmaf(lpart[rb][h], alpha[rb][h], rs);
             }
-            lpart[h] = __builtin_fmaf(lpart[h], alpha[h], rs);
         }
-        // probabilities of row (g, h) for tokens 16t + n into the P tile
-        // (1-byte codes: value scale folded in, f16)
+        // probabilities of row (4 rb + g, h) for tokens 16t + n into the P
+        // tile, column 16 rb + 4 g + h (1-byte codes: value scale folded in, f16)
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            float a[4];
+            const float vs = QUANT ? lane_value(vsc_cur, 16 * t + n) : 1.f;
 #pragma unroll
-            for (int h = 0; h < 4; ++h) a[h] = pv[t][h];
-            uint2 w;
-            if constexpr (QUANT) {
-                const float vs = lane_value(vsc_cur, 16 * t + n);
-                w = make_uint2(pack_f16x2(a[0] * vs, a[1] * vs), pack_f16x2(a[2] * vs, a[3] * vs));
-            } else {
-                w = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+            for (int rb = 0; rb < RB; ++rb) {
+                const float *a = pv[rb][t];
+                uint2 w;
+                if constexpr (QUANT)
+                    w = make_uint2(pack_f16x2(a[0] * vs, a[1] * vs), pack_f16x2(a[2] * vs, a[3] * vs));
+                else
+                    w = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+                *reinterpret_cast<uint2 *>(&pt16[16 * t + n][16 * rb + 4 * g]) = w;
             }
-            *reinterpret_cast<uint2 *>(&pt16[16 * t + n][4 * g]) = w;
         }
         // LDS ops of one wave complete in order; this only keeps the compiler
         // from moving the reads above the writes.
@@ -380,10 +452,11 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
 
         // ---- O += P V on the matrix cores, 32 tokens per step
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-            for (int blk = 0; blk < 8; ++blk) acc[blk][h] *= alpha[h];
-        }
+            for (int h = 0; h < 4; ++h)
+#pragma unroll
+                for (int blk = 0; blk < 8; ++blk) acc[rb][blk][h] *= alpha[rb][h];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             if (kb == 1) {
@@ -398,18 +471,27 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
                 __builtin_amdgcn_sched_barrier(0);
             }
             const int r0 = 32 * kb + tr_row;
-            const uint64_t a_lo = tr_read(&pt16[r0][tr_col]);
-            const uint64_t a_hi = tr_read(&pt16[r0 + 4][tr_col]);
+            uint64_t a_lo[RB], a_hi[RB];
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                a_lo[rb] = tr_read(&pt16[r0][16 * rb + tr_col]);
+                a_hi[rb] = tr_read(&pt16[r0 + 4][16 * rb + tr_col]);
+            }
 #pragma unroll
             for (int blk = 0; blk < 8; ++blk) {
                 const uint64_t b_lo = tr_read(&vt[tr_row][16 * blk + tr_col]);
                 const uint64_t b_hi = tr_read(&vt[tr_row + 4][16 * blk + tr_col]);
-                if constexpr (!QUANT)
-                    acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        join_bf16x8(a_lo, a_hi), join_bf16x8(b_lo, b_hi), acc[blk], 0, 0, 0);
-                else
-                    acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                        join_f16x8(a_lo, a_hi), join_f16x8(b_lo, b_hi), acc[blk], 0, 0, 0);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    if constexpr (!QUANT)
+                        acc[rb][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            join_bf16x8(a_lo[rb], a_hi[rb]), join_bf16x8(b_lo, b_hi), acc[rb][blk],
+                            0, 0, 0);
+                    else
+                        acc[rb][blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            join_f16x8(a_lo[rb], a_hi[rb]), join_f16x8(b_lo, b_hi), acc[rb][blk],
+                            0, 0, 0);
+                }
             }
         }
         // the next page's V overwrites the tile only after these reads
@@ -417,116 +499,106 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
         if (!QUANT && pg + 1 == split_end && pg + 1 < pg1) {
             // split jcur complete and not this workgroup's last: its state
             // into the LDS stash, then start the next one
-            float *st = vstash + (wave * (walk - 1) + nstash) * kVerifyStashFloats;
+            float *st = vstash + (wave * (walk - 1) + nstash) * STASH;
 #pragma unroll
-            for (int h = 0; h < 4; ++h) {
-                const float l = row_sum16(lpart[h]);
+            for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-                for (int blk = 0; blk < 8; ++blk) st[(blk * 4 + h) * 64 + lane] = acc[blk][h];
-                if (n == 0) {
-                    st[32 * 64 + 4 * g + h] = m[h];
-                    st[32 * 64 + 16 + 4 * g + h] = l;
+                for (int h = 0; h < 4; ++h) {
+                    const float l = row_sum16(lpart[rb][h]);
+#pragma unroll
+                    for (int blk = 0; blk < 8; ++blk)
+                        st[((rb * 8 + blk) * 4 + h) * 64 + lane] = acc[rb][blk][h];
+                    if (n == 0) {
+                        st[RB * 32 * 64 + 16 * rb + 4 * g + h] = m[rb][h];
+                        st[RB * 32 * 64 + 16 * RB + 16 * rb + 4 * g + h] = l;
+                    }
+                    m[rb][h] = kNegInf;
+                    lpart[rb][h] = 0.f;
                 }
-                m[h] = kNegInf;
-                lpart[h] = 0.f;
-            }
 #pragma unroll
-            for (int blk = 0; blk < 8; ++blk) acc[blk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                for (int blk = 0; blk < 8; ++blk) acc[rb][blk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
             ++nstash;
             ++jcur;
             split_end = min(split_end + pps, pages);
         }
     }
-    // ---- partial state of query token g: l over the 16 lanes of its group
+    // ---- partial states of this chunk's query tokens: l over the 16 lanes
+    // of a group; then the walk's splits past the context (empty) and the
+    // stashed splits j .. j + nstash - 1
 #pragma unroll
-    for (int h = 0; h < 4; ++h) lpart[h] = row_sum16(lpart[h]);
-    if (g < nq) {
-        const int64_t row0 = ((int64_t)(q0 + g) * p.hq + kvh * kGroup) * S + jcur;
+    for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-            const int64_t idx = row0 + (int64_t)h * S;
-            float *dst = p.part_acc + idx * D + n;
-#pragma unroll
-            for (int blk = 0; blk < 8; ++blk) dst[16 * blk] = acc[blk][h];
-            if (n == 0) {
-                p.part_max[idx] = m[h] == kNegInf ? kNegInf : m[h] * kLn2;
-                p.part_sum[idx] = lpart[h];
-            }
-        }
-    }
-    if (g < nq) {
-        // splits of this workgroup past the context: empty states
-        for (int jw = jcur + 1; jw < j + walk; ++jw) {
-            const int64_t row0 = ((int64_t)(q0 + g) * p.hq + kvh * kGroup) * S + jw;
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-                const int64_t idx = row0 + (int64_t)h * S;
-                float *dst = p.part_acc + idx * D + n;
-#pragma unroll
-                for (int blk = 0; blk < 8; ++blk) dst[16 * blk] = 0.f;
-                if (n == 0) {
-                    p.part_max[idx] = kNegInf;
-                    p.part_sum[idx] = 0.f;
-                }
-            }
-        }
-        // the stashed splits j .. j + nstash - 1
+        for (int h = 0; h < 4; ++h) lpart[rb][h] = row_sum16(lpart[rb][h]);
+        const int tq = 4 * rb + g;
+        if (tq >= nqc) continue;
+        const int row = q0 + c0 + tq;
+        put_state(row, jcur, [&](int h, int blk) { return acc[rb][blk][h]; }, m[rb], lpart[rb]);
+        for (int jw = jcur + 1; jw < j + walk; ++jw) put_state(row, jw, zero_acc, kEmptyM, kEmptyL);
         for (int k = 0; k < nstash; ++k) {
-            const float *st = vstash + (wave * (walk - 1) + k) * kVerifyStashFloats;
-            const int64_t row0 = ((int64_t)(q0 + g) * p.hq + kvh * kGroup) * S + j + k;
+            const float *st = vstash + (wave * (walk - 1) + k) * STASH;
+            float mk[4], lk[4];
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
-                const int64_t idx = row0 + (int64_t)h * S;
-                float *dst = p.part_acc + idx * D + n;
-#pragma unroll
-                for (int blk = 0; blk < 8; ++blk) dst[16 * blk] = st[(blk * 4 + h) * 64 + lane];
-                if (n == 0) {
-                    const float mk = st[32 * 64 + 4 * g + h];
-                    p.part_max[idx] = mk == kNegInf ? kNegInf : mk * kLn2;
-                    p.part_sum[idx] = st[32 * 64 + 16 + 4 * g + h];
-                }
+                mk[h] = st[RB * 32 * 64 + 16 * rb + 4 * g + h];
+                lk[h] = st[RB * 32 * 64 + 16 * RB + 16 * rb + 4 * g + h];
             }
+            put_state(row, j + k,
+                      [&](int h, int blk) { return st[((rb * 8 + blk) * 4 + h) * 64 + lane]; }, mk,
+                      lk);
         }
     }
 }
 
-template <int KV>
+template <int KV, int RB>
 hipError_t launch_verify_kv(const DecodeParams &p_in, hipStream_t stream) {
+    constexpr int STASH = verify_stash_floats<RB>();
     DecodeParams p = p_in;
     p.split_walk = split_walk_for(p, KV != 0, kVerifyWaves);
     if (p.split_walk > 1) {
         // the stash must fit beside the kernel's static LDS
         static const size_t static_lds = [] {
             hipFuncAttributes a{};
-            return hipFuncGetAttributes(&a, reinterpret_cast<const void *>(&verify_kernel<KV>)) ==
+            return hipFuncGetAttributes(&a, reinterpret_cast<const void *>(&verify_kernel<KV, RB>)) ==
                            hipSuccess
                        ? a.sharedSizeBytes
                        : (size_t)65536;
         }();
         const size_t max_lds = max_lds_per_block();
-        while (p.split_walk > 1 && static_lds + (size_t)kVerifyWaves * (p.split_walk - 1) *
-                                                     kVerifyStashFloats * sizeof(float) > max_lds)
+        while (p.split_walk > 1 &&
+               static_lds + (size_t)kVerifyWaves * (p.split_walk - 1) * STASH * sizeof(float) > max_lds)
             p.split_walk /= 2;
     }
-    const unsigned grid =
-        (unsigned)(p.batch * (p.hkv / kVerifyWaves) * (p.splits / p.split_walk));
-    const size_t stash_bytes =
-        (size_t)kVerifyWaves * (p.split_walk - 1) * kVerifyStashFloats * sizeof(float);
-    hipLaunchKernelGGL((verify_kernel<KV>), dim3(grid), dim3(kVerifyWaves * 64),
+    const unsigned grid = (unsigned)((int64_t)p.batch * (p.hkv / kVerifyWaves) *
+                                     (p.splits / p.split_walk) * p.q_chunks);
+    const size_t stash_bytes = (size_t)kVerifyWaves * (p.split_walk - 1) * STASH * sizeof(float);
+    hipLaunchKernelGGL((verify_kernel<KV, RB>), dim3(grid), dim3(kVerifyWaves * 64),
                        (unsigned)stash_bytes, stream, p, p.page_table, p.seq_lens, p.cu_seqlens_q);
     return hipGetLastError();
 }
 
+template <int RB>
+hipError_t launch_verify_rb(const DecodeParams &p, int kv_type, hipStream_t stream) {
+    if (kv_type == kKvInt8) return launch_verify_kv<1, RB>(p, stream);
+    if (kv_type == kKvFp8) return launch_verify_kv<2, RB>(p, stream);
+    return launch_verify_kv<0, RB>(p, stream);
+}
+
 }  // namespace
 
-hipError_t launch_verify(const DecodeParams &p, int kv_type, hipStream_t stream) {
-    hipError_t err;
-    if (kv_type == kKvInt8)
-        err = launch_verify_kv<1>(p, stream);
-    else if (kv_type == kKvFp8)
-        err = launch_verify_kv<2>(p, stream);
-    else
-        err = launch_verify_kv<0>(p, stream);
+// Query tokens one workgroup takes: 4 (one row block) up to max_q_len 4,
+// else 8 (two blocks sharing the K and V operands); more tokens per request
+// are cut into chunks of that size.
+int verify_tokens_per_workgroup(int max_q_len) { return max_q_len <= 4 ? 4 : 8; }
+
+hipError_t launch_verify(const DecodeParams &p_in, int kv_type, int max_q_len,
+                         hipStream_t stream) {
+    DecodeParams p = p_in;
+    const int qt = verify_tokens_per_workgroup(max_q_len);
+    p.max_q_len = max_q_len;
+    p.q_chunks = (max_q_len + qt - 1) / qt;
+    const hipError_t err = qt == 4 ? launch_verify_rb<1>(p, kv_type, stream)
+                                   : launch_verify_rb<2>(p, kv_type, stream);
     if (err != hipSuccess) return err;
     return launch_split_merge(p.part_acc, p.part_max, p.part_sum, p.total_q * p.hq, kHeadDim,
                               p.splits, p.out, p.lse, stream);

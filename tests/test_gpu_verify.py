@@ -57,6 +57,77 @@ def test_verify_parity(kv, lens, qlens, S):
     compare_attention(out, lse, o_ref, l_ref, label=f"verify {kv} {lens}")
 
 
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8"])
+@pytest.mark.parametrize("lens,qlens,S", [
+    ([70, 6, 1290, 4000], [6, 6, 5, 6], 4),        # 6 rows: a step with 5 draft tokens
+    ([64, 65, 2000, 8], [8, 7, 8, 8], 16),         # two row blocks across page / split edges
+    ([4096, 3, 129, 700], [5, 3, 8, 0], 64),       # many empty splits; a request with no rows
+])
+def test_verify_parity_up_to_eight_rows(kv, lens, qlens, S):
+    """5 to 8 query rows per request: one workgroup takes 8 query tokens (two
+    row blocks sharing every K and V operand)."""
+    c = small_case(lens, kv=kv, S=S, seed=57)
+    q_rows, cu = W.verify_queries(c, qlens)
+    print(f"[case] verify {kv} lens={lens} qlens={qlens} S={S} max_q_len 8", flush=True)
+    out, lse = run_verify(c, q_rows, cu, max_q_len=8)
+    o_ref, l_ref = oracle_verify(c, q_rows, cu)
+    compare_attention(out, lse, o_ref, l_ref, label=f"verify8 {kv} {lens}")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8"])
+def test_verify_more_rows_than_one_workgroup_takes(kv):
+    """Up to 20 query rows per request: chunks of 8 tokens, each chunk a grid
+    slice of its own reading the request's K and V."""
+    c = small_case([300, 40, 2000, 20], kv=kv, S=8, seed=58)
+    qlens = [20, 9, 13, 17]
+    q_rows, cu = W.verify_queries(c, qlens)
+    print(f"[case] verify {kv} qlens={qlens} max_q_len 20 (chunks)", flush=True)
+    out, lse = run_verify(c, q_rows, cu, max_q_len=20)
+    o_ref, l_ref = oracle_verify(c, q_rows, cu)
+    compare_attention(out, lse, o_ref, l_ref, label=f"verify chunks {kv}")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("max_q_len,qlens", [(4, [6, 2, 4]), (8, [10, 8, 3]), (3, [5, 3, 1])])
+def test_verify_rows_past_max_q_len(kv, max_q_len, qlens):
+    """A request with more query rows in the device data than the declared
+    max_q_len: its first max_q_len rows are computed with the causal limits
+    of all its rows (they match the oracle's), the rest get out = 0 and
+    lse = -inf."""
+    c = small_case([500, 90, 1400], kv=kv, S=4, seed=59)
+    q_rows, cu = W.verify_queries(c, qlens)
+    print(f"[case] verify {kv} qlens={qlens} past max_q_len {max_q_len}", flush=True)
+    d = DevCase(c)
+    T = q_rows.shape[0]
+    ws = torch.empty(spa.verify_workspace_bytes(T, 32, 8, 128, 4), dtype=torch.uint8,
+                     device="cuda")
+    ws.view(torch.float32).fill_(float("nan"))     # stale state must not be what is read
+    out, lse = spa.paged_verify_attention(
+        bf16_dev(q_rows), d.k, d.v, d.page_list, d.seq_lens, torch.from_numpy(cu).cuda(), 4,
+        float(c.scale), max_q_len=max_q_len, kv_dtype=c.kv_dtype, k_scales=d.ks, v_scales=d.vs,
+        workspace=ws)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle_verify(c, q_rows, cu)
+    inside = np.concatenate([np.arange(n) < max_q_len for n in qlens])
+    compare_attention(out[torch.from_numpy(inside).cuda()], lse[torch.from_numpy(inside).cuda()],
+                      o_ref[inside], l_ref[inside], label=f"verify rows <= max_q_len {kv}")
+    past = torch.from_numpy(~inside).cuda()
+    assert torch.isneginf(lse[past]).all() and (out[past].float() == 0).all()
+
+
+def test_verify_headline_shape_six_query_tokens():
+    """Batch 32, context 8K, 6 query tokens per request (a speculative step
+    with 5 draft tokens): every output against the oracle."""
+    c = config_case(4)
+    q_rows, cu = W.verify_queries(c, [6] * c.batch)
+    print("[case] verify batch 32 / 8K / 6 tokens", flush=True)
+    d = DevCase(c)
+    pt, _, _ = d.page_table()
+    out, lse = run_verify(c, q_rows, cu, page_table=pt, max_q_len=6)
+    o_ref, l_ref = oracle_verify(c, q_rows, cu)
+    compare_attention(out, lse, o_ref, l_ref, label="verify b32 8K q6")
+
+
 def test_verify_headline_shape_four_draft_tokens():
     """Batch 32, context 8K, 4 query tokens per request (draft rows at the end
     of each context): every output against the oracle."""

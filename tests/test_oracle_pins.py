@@ -497,9 +497,11 @@ def _verify(c, q_rows, cu):
 
 @pytest.mark.parametrize("kv", ["bf16", "int8", "fp8"])
 @pytest.mark.parametrize("lens,qlens", [([20, 9, 33], [4, 1, 3]), ([5, 64, 2], [2, 4, 2]),
-                                        ([17, 40], [0, 4])])
+                                        ([17, 40], [0, 4]),
+                                        # 6 rows: a speculative step with 5 draft tokens
+                                        ([70, 6, 129], [6, 6, 5]), ([11, 66], [8, 7])])
 def test_verify_matches_dense_causal_brute_force(kv, lens, qlens):
-    c = _small(lens, kv_dtype=kv)
+    c = _small(lens, kv_dtype=kv, num_pages=40, max_seq_pages=24)
     q_rows, cu = W.verify_queries(c, qlens)
     out, lse = _verify(c, q_rows, cu)
     bo, bl = dense_verify(c, q_rows, cu)
@@ -510,8 +512,8 @@ def test_verify_matches_dense_causal_brute_force(kv, lens, qlens):
 def test_verify_query_i_is_decode_over_its_prefix():
     """Query token i of a request with n queries is exactly the one-token
     decode of the same query over the first L - n + i + 1 tokens."""
-    c = _small([30, 23, 11], kv_dtype="bf16")
-    qlens = [4, 3, 2]
+    c = _small([30, 23, 11, 70], kv_dtype="bf16", num_pages=24)
+    qlens = [4, 3, 2, 6]
     q_rows, cu = W.verify_queries(c, qlens)
     out, lse = _verify(c, q_rows, cu)
     for b in range(c.batch):
