@@ -924,6 +924,17 @@ void decode_kernel(DecodeParams p,
         // thread counts this split in with a memory-side atomic.  The split
         // that arrives last (count S-1) reads all S partial states from memory,
         // merges them in split order and resets the counter for the next call.
+        // Ordering (the AMDGPU memory model's system-scope release/acquire
+        // sequences for gfx94x/gfx950, with the cache maintenance they carry
+        // made unnecessary): a store with sc0 sc1 writes through to memory and
+        // leaves no dirty L2 line, so the release's L2 writeback has nothing
+        // to do; vmcnt counts a store as done only once memory has acknowledged
+        // it, so after s_waitcnt vmcnt(0) in every wave and the barrier, all
+        // of the workgroup's state is in memory before the atomic is issued,
+        // and no XCD can see the count without the state.  The merger's loads
+        // bypass the caches (sc0 sc1) and are issued after the atomic has
+        // returned, so the acquire's cache invalidation has nothing stale to
+        // drop.
         __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (threadIdx.x == 0) {
