@@ -241,6 +241,31 @@ spa_status spa_paged_decode_attention(const void *q, const void *k_pages, const 
                                       void *out, float *lse, hipStream_t stream);
 
 /*
+ * spa_paged_decode_attention without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Same arguments, checks, launches
+ * and results (bit for bit) as spa_paged_decode_attention with a workspace
+ * of spa_decode_workspace_bytes(...) bytes; it calls no allocating routine.
+ *
+ * Its workspace is a 32 MiB (33554432-byte) array of device memory inside
+ * the library, one per GPU, held until the process ends; the first call on
+ * a device looks up that device's copy and clears its counter region with a
+ * fill kernel on `stream` (fused merges leave it zeroed again).  A call whose
+ * spa_decode_workspace_bytes(...) exceeds 32 MiB returns
+ * SPA_ERR_WORKSPACE_TOO_SMALL and launches nothing (batch 32 with 16 splits
+ * at 32 query heads needs about 8.5 MB).  Every call on one GPU uses the
+ * same array: calls that may overlap in time on one GPU (different streams
+ * without ordering between them, or different host threads) race on it and
+ * must be serialised by the caller.
+ */
+spa_status spa_paged_decode_attention_noalloc(
+    const void *q, const void *k_pages, const void *v_pages, const float *k_scales,
+    const float *v_scales, const int32_t *page_table, int64_t page_table_stride,
+    const int32_t *seq_lens, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t page_size, int32_t num_pages, int32_t num_splits, float scale,
+    spa_kv_dtype kv_dtype, uint32_t flags, void *out, float *lse, hipStream_t stream);
+
+/*
  * The launch plan spa_paged_decode_attention takes with flags == 0 for these
  * sizes: one producer flag (SPA_DECODE_HEAD_GROUPED or SPA_DECODE_PAGE_SPLIT)
  * or'ed with one merge flag (SPA_DECODE_FUSED_MERGE or

@@ -18,6 +18,7 @@ import torch
 __all__ = [
     "SpaError", "lib", "status_string", "build_page_table", "decode_workspace_bytes",
     "workspace_reset", "new_workspace", "paged_decode_attention", "split_merge",
+    "paged_decode_attention_noalloc",
     "SPA_OK", "SPA_ERR_INVALID_ARGUMENT", "SPA_ERR_UNSUPPORTED",
     "SPA_ERR_WORKSPACE_TOO_SMALL", "SPA_ERR_HIP", "SPA_KV_BF16", "SPA_KV_INT8", "SPA_KV_FP8",
     "SPA_DECODE_SEPARATE_MERGE", "SPA_DECODE_FUSED_MERGE", "SPA_DECODE_HEAD_GROUPED",
@@ -90,6 +91,10 @@ def lib():
                                              _I32, _I32, _I32, _I32, _F32, _ST, _U32, _P, _SZ,
                                              _P, _P, _P]
     L.spa_paged_decode_attention.restype = _ST
+    L.spa_paged_decode_attention_noalloc.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _P, _I32,
+                                                     _I32, _I32, _I32, _I32, _I32, _I32, _F32,
+                                                     _ST, _U32, _P, _P, _P]
+    L.spa_paged_decode_attention_noalloc.restype = _ST
     L.spa_decode_default_flags.argtypes = [_I32, _I32, _I32, _ST, _I64]
     L.spa_decode_default_flags.restype = _U32
     L.spa_paged_decode_partials.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _P, _I32, _I32, _I32,
@@ -353,6 +358,37 @@ def paged_decode_attention(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torc
         float(scale), kvd, flags, _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse),
         _stream(stream))
     _check(st, "spa_paged_decode_attention")
+    return out, lse
+
+
+def paged_decode_attention_noalloc(q: torch.Tensor, k_pages: torch.Tensor,
+                                   v_pages: torch.Tensor, page_table: torch.Tensor,
+                                   seq_lens: torch.Tensor, num_splits: int, scale: float, *,
+                                   kv_dtype: str = "bf16", k_scales: Optional[torch.Tensor] = None,
+                                   v_scales: Optional[torch.Tensor] = None,
+                                   out: Optional[torch.Tensor] = None,
+                                   lse: Optional[torch.Tensor] = None,
+                                   merge: Optional[str] = None, producer: Optional[str] = None,
+                                   stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """spa_paged_decode_attention_noalloc: paged_decode_attention on the
+    library's own per-GPU workspace (no workspace argument; the library
+    allocates nothing).  Pass ``out`` and ``lse`` to keep the call free of
+    allocations on the Python side too."""
+    B, Hq, D, num_pages, P, Hkv, kvd, k_scales, v_scales = _decode_inputs(
+        q, k_pages, v_pages, page_table, seq_lens, kv_dtype, k_scales, v_scales)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.bfloat16)
+    _need(lse, "lse", torch.float32)
+    flags = {None: 0, "fused": SPA_DECODE_FUSED_MERGE, "separate": SPA_DECODE_SEPARATE_MERGE}[merge]
+    flags |= _PRODUCER_FLAGS[producer]
+    st = lib().spa_paged_decode_attention_noalloc(
+        _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(k_scales), _ptr(v_scales), _ptr(page_table),
+        page_table.stride(0), _ptr(seq_lens), B, Hq, Hkv, D, P, num_pages, int(num_splits),
+        float(scale), kvd, flags, _ptr(out), _ptr(lse), _stream(stream))
+    _check(st, "spa_paged_decode_attention_noalloc")
     return out, lse
 
 

@@ -3,6 +3,8 @@
 // rejected call launches nothing and writes nothing.
 #include <math.h>
 
+#include <mutex>
+
 #include "../../include/spa.h"
 #include "internal.h"
 
@@ -39,6 +41,40 @@ bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 int kv_type_of(spa_kv_dtype d) {
     return d == SPA_KV_INT8 ? spa::kKvInt8 : d == SPA_KV_FP8 ? spa::kKvFp8 : spa::kKvBf16;
+}
+
+// Device memory of spa_paged_decode_attention_noalloc: one decode
+// workspace (counter region, then partial state) per GPU, held until the
+// process ends.  In host code `scratch` is a stand-in for the symbol, not a
+// device address: kernels and fills get the address hipGetSymbolAddress
+// returns for the current device.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's address on the current device.  The first call on a
+// device looks it up and clears its counter region with the fill kernel on
+// `stream` (the fused merge needs zeroed counters and leaves them zeroed).
+spa_status scratch_of_current_device(void **ptr, hipStream_t stream) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (dev < 0 || dev >= kMaxDevices) return SPA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e);
+        if (p == nullptr) return SPA_ERR_HIP;
+        e = spa::launch_fill_zero(p, spa::kCounterRegionBytes / sizeof(uint32_t), stream);
+        if (e != hipSuccess) return hip_status(e);
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return SPA_OK;
 }
 
 // Launch plan of a decode call: KV type, producer shape, merge placement.
@@ -130,6 +166,19 @@ spa_status decode_setup(const void *q, const void *k_pages, const void *v_pages,
     p->num_pages = num_pages;
     p->qk_scale_log2 = scale * 1.4426950408889634f;
     return SPA_OK;
+}
+
+// The decode launches of a checked call on a workspace of layout w.
+spa_status run_decode(spa::DecodeParams &p, const DecodePlan &plan, const spa::WorkspaceLayout &w,
+                      void *workspace, void *out, float *lse, hipStream_t stream) {
+    char *ws = static_cast<char *>(workspace);
+    p.part_acc = reinterpret_cast<float *>(ws + w.acc_off);
+    p.part_max = reinterpret_cast<float *>(ws + w.max_off);
+    p.part_sum = reinterpret_cast<float *>(ws + w.sum_off);
+    p.counters = reinterpret_cast<int32_t *>(ws + w.cnt_off);
+    p.out = static_cast<uint16_t *>(out);
+    p.lse = lse;
+    return hip_status(spa::launch_decode(p, plan.kv_type, plan.mode, plan.fused, stream));
 }
 
 }  // namespace
@@ -270,15 +319,31 @@ spa_status spa_paged_decode_attention(const void *q, const void *k_pages, const 
     const spa::WorkspaceLayout w =
         spa::workspace_layout(batch, num_q_heads, num_kv_heads, head_dim, num_splits);
     if (workspace_bytes < w.total) return SPA_ERR_WORKSPACE_TOO_SMALL;
+    return run_decode(p, plan, w, workspace, out, lse, stream);
+}
 
-    char *ws = static_cast<char *>(workspace);
-    p.part_acc = reinterpret_cast<float *>(ws + w.acc_off);
-    p.part_max = reinterpret_cast<float *>(ws + w.max_off);
-    p.part_sum = reinterpret_cast<float *>(ws + w.sum_off);
-    p.counters = reinterpret_cast<int32_t *>(ws + w.cnt_off);
-    p.out = static_cast<uint16_t *>(out);
-    p.lse = lse;
-    return hip_status(spa::launch_decode(p, plan.kv_type, plan.mode, plan.fused, stream));
+spa_status spa_paged_decode_attention_noalloc(
+    const void *q, const void *k_pages, const void *v_pages, const float *k_scales,
+    const float *v_scales, const int32_t *page_table, int64_t page_table_stride,
+    const int32_t *seq_lens, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t page_size, int32_t num_pages, int32_t num_splits, float scale,
+    spa_kv_dtype kv_dtype, uint32_t flags, void *out, float *lse, hipStream_t stream) {
+    spa::DecodeParams p{};
+    DecodePlan plan{};
+    spa_status st = decode_setup(q, k_pages, v_pages, k_scales, v_scales, page_table,
+                                 page_table_stride, seq_lens, batch, num_q_heads, num_kv_heads,
+                                 head_dim, page_size, num_pages, num_splits, scale, kv_dtype,
+                                 flags, /*producer_only=*/false, &p, &plan);
+    if (st != SPA_OK || batch == 0) return st;
+    if (!out) return SPA_ERR_INVALID_ARGUMENT;
+    if (!aligned(out, 2) || (lse && !aligned(lse, 4))) return SPA_ERR_INVALID_ARGUMENT;
+    const spa::WorkspaceLayout w =
+        spa::workspace_layout(batch, num_q_heads, num_kv_heads, head_dim, num_splits);
+    if (w.total > kScratchBytes) return SPA_ERR_WORKSPACE_TOO_SMALL;
+    void *ws = nullptr;
+    st = scratch_of_current_device(&ws, stream);
+    if (st != SPA_OK) return st;
+    return run_decode(p, plan, w, ws, out, lse, stream);
 }
 
 uint32_t spa_decode_default_flags(int32_t batch, int32_t num_kv_heads, int32_t num_splits,

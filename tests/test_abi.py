@@ -106,6 +106,27 @@ def test_workspace_bytes():
     assert _attn(wsb=n - 1, B=32, S=16) == spa.SPA_ERR_WORKSPACE_TOO_SMALL
 
 
+def _noalloc(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ks=None, vs=None, pt=FAKE, pts=128, sl=FAKE, B=1, Hq=32,
+             Hkv=8, D=128, P=64, npg=16, S=4, scale=0.088, kvd=0, flags=0, out=FAKE, lse=FAKE)
+    a.update(kw)
+    return spa.lib().spa_paged_decode_attention_noalloc(
+        a["q"], a["k"], a["v"], a["ks"], a["vs"], a["pt"], a["pts"], a["sl"], a["B"], a["Hq"],
+        a["Hkv"], a["D"], a["P"], a["npg"], a["S"], a["scale"], a["kvd"], a["flags"], a["out"],
+        a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=64, S=64), spa.SPA_ERR_WORKSPACE_TOO_SMALL),   # needs 68 MB > the 32 MiB scratch
+    (dict(D=64), spa.SPA_ERR_UNSUPPORTED),
+    (dict(out=None), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(flags=3), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(B=0), spa.SPA_OK),                                 # no launch
+])
+def test_noalloc_argument_checks(kw, code):
+    assert _noalloc(**kw) == code
+
+
 def test_workspace_reset_checks():
     L = spa.lib()
     assert L.spa_workspace_reset(None, 0, None) == spa.SPA_OK
