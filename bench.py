@@ -10,17 +10,20 @@ Default workload: batch 32, context 8192, 32 query / 8 KV heads, head_dim 128,
 bf16 K/V in 64-token pages scattered over a 4096-page pool, 16 splits --
 lmdeploy's headline H200 shape.
 
-Timing: W untimed warm-up steps, then exactly K steps between two device
-synchronisations (events on the launch stream bracket the run; `value` and
-ms_per_step come from them).  Then K more of the same steps with HIP events
-around every attention call (both launches and the gap between them fall
-inside) and, for a two-launch plan, around the producer launch alone: the
-roofline figure is the algorithmic bytes over the producer's average
-duration.  These events are kept out of the timed steps because an event
-between two launches idles the GPU for about 4 us.  Two copies of the KV pool alternate so that
-consecutive steps do not read the same addresses.  A HIP-graph replay of the
-step is timed as well (the pages quote CUDA-graph latency).  The fp64 CPU
-oracle is timed on the host beside it.
+Timing: W untimed warm-up steps, then untimed steps until --settle-ms have
+passed (the GPU's clocks settle after about 10 ms of sustained work), then
+exactly K steps between two device synchronisations (events on the launch
+stream bracket the run; `value` and ms_per_step come from them).  Then K
+more of the same steps with HIP events around every attention call (both
+launches and the gap between them fall inside) and, for a two-launch plan,
+around the producer launch alone: the roofline figure is the algorithmic
+bytes over the producer's average duration.  These events are kept out of
+the timed steps because an event between two launches idles the GPU for
+about 4 us.  The KV pool holds R >= 2 copies of the batch's pages, R * (bytes
+of one copy) >= 1 GiB, and step i reads copy i % R, so no step finds its
+pages in the 256 MB Infinity Cache.  HIP graphs of R steps and of R calls
+are timed as well (the pages quote CUDA-graph latency), p10 / p50 / p90 per
+call over the replays.  The fp64 CPU oracle is timed on the host beside it.
 
 Prints ONE JSON line.  --summarize-pmc turns two rocprofv3 counter runs
 (FETCH_SIZE, WRITE_SIZE) into the HBM-traffic record the bench reports.
@@ -227,8 +230,32 @@ class HipEvents:
         self.events = []
 
 
+# Timing loops rotate over copies of the batch's pages so that consecutive
+# calls read different addresses: with at least this many bytes of distinct
+# K/V between two reads of the same page, the 256 MB Infinity Cache (MALL)
+# cannot serve them.
+ROTATION_BYTES = 1 << 30
+
+
+def rotation_copies(case, min_bytes: int = ROTATION_BYTES) -> int:
+    """Copies of the batch's used pages (at least 2) whose K/V (+ scales)
+    bytes together reach min_bytes."""
+    import numpy as np
+    P = case.page_size
+    used = int(sum(-(-int(L) // P) for L in case.seq_lens))
+    per = used * P * case.kv_bytes_per_token()
+    return max(2, -(-min_bytes // max(per, 1))), per
+
+
 class Rig:
-    """Device copies of one workload and the calls of one step on them."""
+    """Device copies of one workload and the calls of one step on them.
+
+    The KV pool holds R copies of the pages the batch uses (R from
+    rotation_copies), each in its own random placement; call i reads copy
+    i % R, through a req_to_token map whose rows c*B .. c*B+B-1 are the
+    batch's requests in copy c.  Step i builds copy i % R's page table with
+    the metadata kernel and decodes from it; attention-only calls use the
+    page tables built once at set-up."""
 
     def __init__(self, case, qlen: int = 0):
         import numpy as np
@@ -244,6 +271,9 @@ class Rig:
             return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(
                 torch.bfloat16)
 
+        self.R, self.copy_bytes = rotation_copies(case)
+        src, r2t, rpi = W.rotation_layout(case, self.R)
+        src = torch.from_numpy(src).to(dev)
         self.q = bf16(case.q)
         if case.kv_dtype == "bf16":
             k0, v0 = bf16(case.k_pages), bf16(case.v_pages)
@@ -253,15 +283,17 @@ class Rig:
             v0 = torch.from_numpy(case.v_pages).to(dev)
             ks0 = torch.from_numpy(case.k_scales).to(dev)
             vs0 = torch.from_numpy(case.v_scales).to(dev)
-        # two copies of the pool alternate so consecutive calls read new addresses
-        self.copies = [(k0, v0, ks0, vs0),
-                       (k0.clone(), v0.clone(), None if ks0 is None else ks0.clone(),
-                        None if vs0 is None else vs0.clone())]
-        self.r2t = torch.from_numpy(case.req_to_token).to(dev)
-        self.rpi = torch.from_numpy(case.req_pool_indices).to(dev)
+        # the rotated pool: page n holds the case's page src[n]
+        self.k = k0.index_select(0, src)
+        self.v = v0.index_select(0, src)
+        self.ks = None if ks0 is None else ks0.index_select(0, src)
+        self.vs = None if vs0 is None else vs0.index_select(0, src)
+        del k0, v0, ks0, vs0
+        self.r2t = torch.from_numpy(r2t).to(dev)
+        self.rpi = torch.from_numpy(rpi).to(dev)          # [R, B]
         self.sl = torch.from_numpy(case.seq_lens).to(dev)
         B, Hq, D, S = case.batch, case.num_q_heads, case.head_dim, case.num_splits
-        self.pt = torch.empty((B, case.max_seq_pages), dtype=torch.int32, device=dev)
+        self.pt = torch.empty((self.R, B, case.max_seq_pages), dtype=torch.int32, device=dev)
         self.cache = torch.empty((B,), dtype=torch.int32, device=dev)
         self.cu = torch.empty((B + 1,), dtype=torch.int32, device=dev)
         self.out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
@@ -291,85 +323,96 @@ class Rig:
             self.p_acc = torch.empty((B, Hq, S, D), dtype=torch.float32, device=dev)
             self.p_max = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
             self.p_sum = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
-        self.k1()                     # attention reads the page table this builds
+        for c in range(self.R):
+            self.k1(c)                # every copy's page table, for attention-only calls
         torch.cuda.synchronize()
 
-    def k1(self):
+    def k1(self, i):
+        """The metadata build of call i (copy i % R's page table)."""
         c = self.case
+        r = i % self.R
         if self.qlen:
-            self.spa.build_metadata(self.r2t, self.rpi, self.sl, c.page_size, c.max_seq_pages,
-                                    page_table=self.pt, cache_seqlens=self.cache,
+            self.spa.build_metadata(self.r2t, self.rpi[r], self.sl, c.page_size, c.max_seq_pages,
+                                    page_table=self.pt[r], cache_seqlens=self.cache,
                                     cu_seqlens_k=self.cu, q_mode=self.spa.Q_MODE_STRIDED,
                                     q_stride=self.qlen, cu_seqlens_q=self.cu_q)
             return
-        self.spa.build_page_table(self.r2t, self.rpi, self.sl, c.page_size, c.max_seq_pages,
-                                  page_table=self.pt, cache_seqlens=self.cache,
+        self.spa.build_page_table(self.r2t, self.rpi[r], self.sl, c.page_size, c.max_seq_pages,
+                                  page_table=self.pt[r], cache_seqlens=self.cache,
                                   cu_seqlens_k=self.cu)
 
     def attn(self, i):
         c = self.case
-        k, v, ks, vs = self.copies[i % 2]
+        pt = self.pt[i % self.R]
         if self.qlen:
-            self.spa.paged_verify_attention(self.q_rows, k, v, self.pt, self.sl, self.cu_q,
+            self.spa.paged_verify_attention(self.q_rows, self.k, self.v, pt, self.sl, self.cu_q,
                                             c.num_splits, float(c.scale), max_q_len=self.qlen,
-                                            kv_dtype=c.kv_dtype, k_scales=ks, v_scales=vs,
-                                            workspace=self.ws, out=self.out, lse=self.lse)
+                                            kv_dtype=c.kv_dtype, k_scales=self.ks,
+                                            v_scales=self.vs, workspace=self.ws, out=self.out,
+                                            lse=self.lse)
             return
-        self.spa.paged_decode_attention(self.q, k, v, self.pt, self.sl, c.num_splits,
-                                        float(c.scale), kv_dtype=c.kv_dtype, k_scales=ks,
-                                        v_scales=vs, workspace=self.ws, out=self.out,
+        self.spa.paged_decode_attention(self.q, self.k, self.v, pt, self.sl, c.num_splits,
+                                        float(c.scale), kv_dtype=c.kv_dtype, k_scales=self.ks,
+                                        v_scales=self.vs, workspace=self.ws, out=self.out,
                                         lse=self.lse, merge=self.merge,
                                         producer=self.producer)
-
 
     def producer_pass(self, i):
         """spa_paged_decode_partials: the producer launch of a two-launch call."""
         c = self.case
-        k, v, ks, vs = self.copies[i % 2]
-        self.spa.paged_decode_partials(self.q, k, v, self.pt, self.sl, c.num_splits,
-                                       float(c.scale), kv_dtype=c.kv_dtype, k_scales=ks,
-                                       v_scales=vs, partial_acc=self.p_acc,
-                                       partial_max=self.p_max, partial_sum=self.p_sum)
+        self.spa.paged_decode_partials(self.q, self.k, self.v, self.pt[i % self.R], self.sl,
+                                       c.num_splits, float(c.scale), kv_dtype=c.kv_dtype,
+                                       k_scales=self.ks, v_scales=self.vs,
+                                       partial_acc=self.p_acc, partial_max=self.p_max,
+                                       partial_sum=self.p_sum)
 
     def merge_pass(self):
         """spa_split_merge over the producer's split states."""
         self.spa.split_merge(self.p_acc, self.p_max, self.p_sum, out=self.out, lse=self.lse)
 
 
-def capture(fn):
-    """Two HIP graphs of fn(0) and fn(1), after a warm-up on a side stream."""
+def capture(fn, n):
+    """A HIP graph of fn(0), fn(1), ..., fn(n - 1), after a warm-up of the
+    same calls on a side stream."""
     import torch
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        for i in range(2):
+        for i in range(n):
             fn(i)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    gl = []
-    for i in range(2):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
             fn(i)
-        gl.append(g)
-    return gl
+    return g
 
 
-def time_graphs(gl, R, warm=200):
-    """Microseconds per replay over R back-to-back replays between two events,
-    after `warm` untimed replays (the clocks settle after about 10 ms of
-    sustained work)."""
+def time_graph(g, calls: int, replays: int, warm_ms: float = 50.0):
+    """Microseconds per call of a graph of `calls` calls: replays back to
+    back until warm_ms have passed (the clocks settle after about 10 ms of
+    sustained work), then `replays` replays, each between two events.
+    Returns (mean, p10, p50, p90) over the replays."""
+    import numpy as np
     import torch
-    for i in range(warm):
-        gl[i % 2].replay()
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(4):
+            g.replay()
+        torch.cuda.synchronize()
+        if (time.perf_counter() - t0) * 1e3 >= warm_ms:
+            break
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(replays)]
+    for a, b in ev:
+        a.record()
+        g.replay()
+        b.record()
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for i in range(R):
-        gl[i % 2].replay()
-    b.record()
-    torch.cuda.synchronize()
-    return a.elapsed_time(b) * 1e3 / R
+    us = np.array([a.elapsed_time(b) * 1e3 / calls for a, b in ev])
+    return (float(us.mean()), float(np.percentile(us, 10)), float(np.percentile(us, 50)),
+            float(np.percentile(us, 90)))
 
 
 def time_eager(fn, K, warmup=200):
@@ -404,16 +447,16 @@ def ablation(args) -> int:
             for merge in ("fused", "separate"):
                 rig.producer, rig.merge = producer, merge
                 e_mean, e_med = time_eager(rig.attn, args.steps)
-                g_us = time_graphs(capture(rig.attn), max(1, args.graph_replays))
-
-                def ten(i):
-                    for t in range(10):
-                        rig.attn(i + t)
-                rt = max(1, args.graph_replays // 10)
-                g10_us = time_graphs(capture(ten), rt, warm=min(20, 10 * rt)) / 10
+                # one call per graph (the graph launch paid per call), and a
+                # graph of R calls over the R page copies (paid once per R)
+                g1 = [capture(lambda i, c=c: rig.attn(c), 1) for c in range(2)]
+                g1_us = min(time_graph(g, 1, max(1, args.graph_replays // 2))[2] for g in g1)
+                gr = time_graph(capture(rig.attn, rig.R), rig.R, max(1, args.graph_replays // 4))
                 rows.append({"workload": case.name, "producer": producer, "merge": merge,
                              "eager_us_mean": round(e_mean, 3), "eager_us_median": round(e_med, 3),
-                             "graph_us": round(g_us, 3), "graph_x10_us": round(g10_us, 3),
+                             "graph_1_call_us": round(g1_us, 3), "graph_us_p50": round(gr[2], 3),
+                             "graph_us_p10": round(gr[1], 3), "graph_us_p90": round(gr[3], 3),
+                             "graph_calls": rig.R,
                              "h200_graph_us_pre_pdl": H200_GRAPH_US.get(case.name)})
                 print(f"[ablation] {rows[-1]}", file=sys.stderr, flush=True)
         del rig
@@ -468,10 +511,7 @@ def policy_sweep(args) -> int:
                                            k_scales=ks, v_scales=vs, workspace=ws, out=out,
                                            lse=lse, producer=prod, merge=merge)
 
-            def ten(i, call=call):
-                for j in range(10):
-                    call(j)
-            us.append(time_graphs(capture(ten), 10, warm=20) / 10)
+            us.append(time_graph(capture(call, 10), 10, 10, warm_ms=10.0)[0])
         best = min(range(4), key=lambda i: us[i])
         rows.append({"batch": B, "context": L, "splits": S, "waves": B * Hkv * S,
                      "page_split_fused_us": round(us[0], 2),
@@ -496,6 +536,9 @@ def main() -> int:
                          "then recover)")
     ap.add_argument("--config", type=int, default=4, help="workload 1..5 (4 = headline)")
     ap.add_argument("--graph-replays", type=int, default=200)
+    ap.add_argument("--settle-ms", type=float, default=30.0,
+                    help="untimed steps after the warm-up until this much time has passed, "
+                         "whatever --warmup is (reported as settle_ms / settle_steps)")
     ap.add_argument("--cpu-reps", type=int, default=40,
                     help="timed oracle calls for cpu_baseline (about 10 s of host work at the "
                          "headline shape)")
@@ -575,7 +618,7 @@ def main() -> int:
     hev = HipEvents()
 
     def step(i, ev=None):
-        k1()
+        k1(i)
         if ev is not None:
             hev.record(ev[0])
         if two:
@@ -591,6 +634,18 @@ def main() -> int:
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    # Settle: after an idle period the GPU's clocks take about 10 ms of
+    # sustained work to settle (durations rise ~12% and recover), so untimed
+    # steps continue until settle_ms have passed, however few warm-up steps
+    # were asked for.  The timed steps below are unaffected in number.
+    settle0 = time.perf_counter()
+    settle_steps = 0
+    while (time.perf_counter() - settle0) * 1e3 < args.settle_ms:
+        for _ in range(8):
+            step(args.warmup + settle_steps)
+            settle_steps += 1
+        torch.cuda.synchronize()
+    settle_ms = (time.perf_counter() - settle0) * 1e3
 
     # The K timed steps: events only around the whole run (an event between
     # two launches leaves the GPU idle for about 4 us, so per-launch events
@@ -612,10 +667,15 @@ def main() -> int:
     for i in range(K):
         step(K + i, evs[i])
     torch.cuda.synchronize()
-    attn_us_mean = float(np.mean([hev.ms(e[0], e[2]) * 1e3 for e in evs]))
-    kernel_us_mean = (float(np.mean([hev.ms(e[0], e[1]) * 1e3 for e in evs])) if two
-                      else attn_us_mean)
+    attn_us = np.array([hev.ms(e[0], e[2]) * 1e3 for e in evs])
+    kernel_us = np.array([hev.ms(e[0], e[1]) * 1e3 for e in evs]) if two else attn_us
+    attn_us_mean, kernel_us_mean = float(attn_us.mean()), float(kernel_us.mean())
     hev.close()
+
+    def pct(x):
+        return {"p10": round(float(np.percentile(x, 10)), 3),
+                "p50": round(float(np.percentile(x, 50)), 3),
+                "p90": round(float(np.percentile(x, 90)), 3)}
 
     if args.copy_ref_mib > 0:
         # device copies of a known size, for scaling the memory counters
@@ -626,25 +686,17 @@ def main() -> int:
         torch.cuda.synchronize()
         del src_buf, dst_buf
 
-    # HIP-graph replays: the whole step, and the attention call alone (the
-    # pages quote CUDA-graph latency of the attention), two graphs each over
-    # the two KV copies.  Timed back to back: R replays between two events.
+    # HIP-graph replays (the pages quote CUDA-graph latency): graphs of R
+    # steps and of R attention calls, call i on page copy i % R, so no call
+    # finds its pages in the Infinity Cache; per call, p10 / p50 / p90 over
+    # the replays (the graph launch, about 8 us, is paid once per R calls).
     def step_fn(i):
-        k1()
+        k1(i)
         attn(i)
 
-    R = max(1, args.graph_replays)
-    graph_step_us = time_graphs(capture(step_fn), R, warm=min(200, 10 * R))
-    graph_attn_us = time_graphs(capture(attn), R, warm=min(200, 10 * R))
-
-    # ten calls per graph (alternating KV copies): the graph launch, about
-    # 8 us between replays here, is paid once per ten calls
-    def ten_calls(i):
-        for t in range(10):
-            attn(i + t)
-
-    RT = max(1, R // 10)
-    graph_attn_x10_us = time_graphs(capture(ten_calls), RT, warm=min(20, 10 * RT)) / 10
+    reps = max(4, args.graph_replays)
+    gs = time_graph(capture(step_fn, rig.R), rig.R, max(4, reps // max(1, rig.R // 16)))
+    ga = time_graph(capture(attn, rig.R), rig.R, max(4, reps // max(1, rig.R // 16)))
 
     nbytes = W.verify_algorithmic_bytes(case, [Q] * B) if Q else W.algorithmic_bytes(case)
     achieved = nbytes / (kernel_us_mean * 1e-6) / 1e9
@@ -706,11 +758,22 @@ def main() -> int:
                             if not Q else "metadata build (page table, cu_seqlens_q) + "
                             "multi-token split-K decode attention")},
         "us_per_call": round(attn_us_mean, 3),
+        "us_per_call_pct": pct(attn_us),
         "producer_us": round(kernel_us_mean, 3) if two else None,
+        "producer_us_pct": pct(kernel_us) if two else None,
         "pct_of_peak": round(100.0 * achieved / PEAK_HBM_GBS, 2),
-        "graph_step_us": round(graph_step_us, 3),
-        "graph_attn_us": round(graph_attn_us, 3),
-        "graph_attn_x10_us": round(graph_attn_x10_us, 3),
+        "graph_step_us": round(gs[2], 3),
+        "graph_step_us_pct": {"p10": round(gs[1], 3), "p50": round(gs[2], 3),
+                              "p90": round(gs[3], 3)},
+        "graph_attn_us": round(ga[2], 3),
+        "graph_attn_us_pct": {"p10": round(ga[1], 3), "p50": round(ga[2], 3),
+                              "p90": round(ga[3], 3)},
+        "rotation": {"page_copies": rig.R, "bytes_per_copy": int(rig.copy_bytes),
+                     "bytes_rotated": int(rig.R * rig.copy_bytes),
+                     "note": "call i reads copy i % page_copies (distinct addresses), so "
+                             "the 256 MB Infinity Cache cannot hold the pages between reads"},
+        "settle_ms": round(settle_ms, 1),
+        "settle_steps": settle_steps,
         "context_h200_graph_attn_us": None if Q else H200_GRAPH_US.get(case.name),
         "algorithmic_bytes": int(nbytes),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,

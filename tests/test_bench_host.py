@@ -6,7 +6,10 @@ import csv
 import json
 import os
 
+import numpy as np
 import pytest
+
+import workloads as W
 
 import bench
 
@@ -116,3 +119,38 @@ def test_multi_gpu_request_is_refused(monkeypatch, capsys):
     monkeypatch.setattr("sys.argv", ["bench.py", "--gpus", "2"])
     assert bench.main() == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_rotation_layout_copies_map_back_to_the_case_pages():
+    """Each page copy's page table (the oracle's metadata definition over the
+    rotated req_to_token) names, page for page, copies of the case's own
+    pages; copies occupy disjoint page ranges; R copies reach 1 GiB."""
+    import bench
+    import oracle
+    c = W.make_case(seed=3, seq_lens=[100, 7, 300, 64], num_pages=40, num_splits=4,
+                    req_pool_rows=4, req_to_token_stride=1024, max_seq_pages=16,
+                    num_q_heads=8, num_kv_heads=2, head_dim=16)
+    R = 3
+    src, r2t, rpi = W.rotation_layout(c, R)
+    U = src.shape[0] // R
+    assert U == sum(-(-int(L) // c.page_size) for L in c.seq_lens)
+    seen = []
+    for cp in range(R):
+        pt, _, _ = oracle.build_page_table(r2t, rpi[cp], c.seq_lens, c.page_size,
+                                           c.max_seq_pages)
+        used = []
+        for b in range(c.batch):
+            n = -(-int(c.seq_lens[b]) // c.page_size)
+            assert np.array_equal(src[pt[b, :n]], c.page_list[b, :n]), (cp, b)
+            assert np.all((pt[b, :n] >= cp * U) & (pt[b, :n] < (cp + 1) * U))
+            used.extend(pt[b, :n].tolist())
+        assert len(set(used)) == U
+        seen.extend(used)
+    assert len(set(seen)) == R * U
+    case4 = W.make_config(4)
+    r, per = bench.rotation_copies(case4)
+    assert r == 2 and r * per >= (1 << 30)
+    case1_lens = W.config_seq_lens(1)
+    assert bench.rotation_copies(type("C", (), dict(page_size=64, seq_lens=case1_lens,
+                                                     kv_bytes_per_token=lambda s: 4096))())[0] \
+        == 256

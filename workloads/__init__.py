@@ -54,7 +54,7 @@ REQ_TO_TOKEN_STRIDE = 8192
 MAX_SEQ_PAGES = 128
 SCALE = np.float32(1.0 / np.sqrt(np.float64(HEAD_DIM)))
 
-_TAG_Q, _TAG_K, _TAG_V, _TAG_PERM, _TAG_LEN, _TAG_RPI, _TAG_FILL, _TAG_QROWS = range(1, 9)
+_TAG_Q, _TAG_K, _TAG_V, _TAG_PERM, _TAG_LEN, _TAG_RPI, _TAG_FILL, _TAG_QROWS, _TAG_ROT = range(1, 10)
 _CHUNK_ELEMS = 1 << 22
 
 
@@ -332,6 +332,43 @@ def verify_queries(case: DecodeCase, q_lens, seed: Optional[int] = None):
     q = normal_bf16((max(total, 1), case.num_q_heads, case.head_dim),
                     case.seed if seed is None else seed, _TAG_QROWS)[:total]
     return np.ascontiguousarray(q), cu
+
+
+def rotation_layout(case: DecodeCase, copies: int):
+    """Layout of ``copies`` disjoint copies of the pages a case's requests
+    use, for timing loops that must not find the previous call's data in a
+    cache: call i reads copy i % copies.
+
+    Copy c holds every used page once (U pages in all), each at a seeded
+    random position of its own range [c*U, (c+1)*U); request b of copy c is
+    row c*B + b of a req_to_token map over the copies (the request's slots
+    first, random valid slots of the copies after).  Every copy holds the
+    same data, so every copy gives the same result.
+
+    Returns (src [copies*U] int64: the case page each copied page holds,
+    req_to_token [copies*B, stride] int32, req_pool_indices [copies, B]
+    int32)."""
+    P, B = case.page_size, case.batch
+    stride = case.req_to_token.shape[1]
+    npg = [-(-int(L) // P) for L in case.seq_lens]
+    used = np.concatenate([case.page_list[b, :n] for b, n in enumerate(npg)]).astype(np.int64)
+    U = int(used.shape[0])
+    src = np.empty(copies * U, dtype=np.int64)
+    rng = _gen(case.seed, _TAG_ROT)
+    r2t = rng.integers(0, max(1, copies * U) * P, size=(copies * B, stride),
+                       dtype=np.int64).astype(np.int32)
+    starts = np.concatenate([[0], np.cumsum(npg)]).astype(np.int64)
+    for c in range(copies):
+        pos = c * U + rng.permutation(U).astype(np.int64)   # copy c's page for used page i
+        src[pos] = used
+        for b in range(B):
+            n = npg[b]
+            if n:
+                pg = pos[starts[b]:starts[b] + n]
+                slots = pg[:, None] * P + np.arange(P, dtype=np.int64)[None, :]
+                r2t[c * B + b, :n * P] = slots.reshape(-1).astype(np.int32)
+    rpi = np.arange(copies * B, dtype=np.int32).reshape(copies, B)
+    return src, r2t, rpi
 
 
 def algorithmic_bytes(case: DecodeCase) -> int:
