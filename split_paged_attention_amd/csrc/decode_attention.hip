@@ -243,7 +243,7 @@ void decode_kernel(DecodeParams p,
     // larger than the GPU's resident workgroups then run in one round, and
     // the later splits skip the workgroup start (request ranking, page-id
     // and first-page latency).  Each split's arithmetic is unchanged.
-    const int walk = (HG && !FUSED && p.split_walk > 1) ? p.split_walk : 1;
+    const int walk = (HG && !FUSED && !QUANT && p.split_walk > 1) ? p.split_walk : 1;
     const int SG = S / walk;                        // split groups per kv group
     const int kv_per_grp = HG ? NW : 1;             // kv heads per workgroup
     const int grp_per_b = p.hkv / kv_per_grp;
@@ -354,6 +354,13 @@ void decode_kernel(DecodeParams p,
     for (int h = 0; h < 4; ++h) qscale[h] = p.qk_scale_log2 * qinv[h];
 
     float m[4], lpart[4], acc[4][8], psum[4];
+    // Matrix-core P.V state (head-grouped int8 codes): oacc[T] is the
+    // 16 x 16 output tile of dims 16T .. 16T + 15, rows 4g + h = head h (the
+    // four row groups hold the same values), column j = dim 16T + j; for
+    // int8, pacc has the sums of P' (value codes carry a bias of 1152).
+    f32x4_t oacc[8], pacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 8; ++t) oacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
         m[h] = kNegInf;
@@ -363,9 +370,11 @@ void decode_kernel(DecodeParams p,
         for (int d = 0; d < 8; ++d) acc[h][d] = 0.f;
     }
 
-    __shared__ uint32_t pbuf[NW][8][4][4];          // [wave][pair u][phase r][head]
+    // Head-grouped int8 codes run P.V on the matrix cores (see below).
+    constexpr bool MXPV = I8 && HG;
+    __shared__ uint32_t pbuf[MXPV ? 1 : NW][8][4][4];   // [wave][pair u][phase r][head]
     __shared__ float sm_m[NW][4], sm_l[NW][4];
-    __shared__ float sm_acc[HG ? 1 : NW][4][D];     // page split: waves' states
+    __shared__ float sm_acc[HG ? 1 : NW][4][HG ? 1 : D];   // page split: waves' states
     // Head-grouped: the page's K rows, staged per wave: loaded as whole rows
     // (bf16: 4 rows of 256 bytes per load instruction, which memory serves
     // about 6% faster than 16 rows x 64 bytes; 1-byte codes: 8 rows of 128
@@ -381,6 +390,14 @@ void decode_kernel(DecodeParams p,
     constexpr bool KDMA = QUANT && KSTAGE;
     constexpr int KROWB = KDMA ? D : D * (QUANT ? 1 : 2) + 16;   // bytes per staged row
     __shared__ __attribute__((aligned(16))) uint8_t ktile[KSTAGE ? NW : 1][KSTAGE ? P : 1][KROWB];
+    // Matrix-core P.V, per wave: the page's probabilities P' (f16, value
+    // scale folded in) token-major, 4 heads per 8-byte row; and half a page
+    // of value codes (32 token rows of 128 bytes, padded by 16 so that the 8
+    // rows of a transposed read fall in distinct banks).  Transposed reads
+    // turn both into operands whose contraction runs over tokens.
+    constexpr int VROWB = D + 16;
+    __shared__ __attribute__((aligned(16))) uint16_t ptile[MXPV ? NW : 1][MXPV ? P : 1][4];
+    __shared__ __attribute__((aligned(16))) uint8_t vtile[MXPV ? NW : 1][MXPV ? P / 2 : 1][MXPV ? VROWB : 1];
     __shared__ int sm_last;
 
     const int32_t *pt_row = page_table + (int64_t)b * p.pt_stride;
@@ -539,6 +556,59 @@ void decode_kernel(DecodeParams p,
         }
     };
 
+    // Matrix-core P.V: this wave's split jw is complete; write its
+    // partial state from the matrix-core layout (lane (j, g) holds head g at
+    // dims 16T + j) and start the next split.
+    auto finish_split_mx = [&](int jw) {
+        if constexpr (I8) {
+            // remove the 1152 bias of the value codes
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+#pragma unroll
+                for (int h = 0; h < 4; ++h) oacc[t][h] = __builtin_fmaf(-kI8Bias, pacc[h], oacc[t][h]);
+        }
+        float lsum[4];   // the lanes' sums over their own tokens, over the wave
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            float x = row_sum16(lpart[h]);
+            x += __shfl_xor(x, 16);
+            x += __shfl_xor(x, 32);
+            lsum[h] = x;
+        }
+        const int64_t idx0 = ((int64_t)b * p.hq + kvh * kGroup) * S + jw;
+        const int jl = lane & 15;
+        const int off = (g * S * D + jl) * 4;   // bytes: head g's row, dim jl
+        float o[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+            o[t] = pick4(oacc[t][0], oacc[t][1], oacc[t][2], oacc[t][3], g);
+        if constexpr (FUSED) {
+            const auto r = __builtin_amdgcn_make_buffer_rsrc(p.part_acc + idx0 * D, (short)0,
+                                                             (3 * S + 1) * D * 4, kBufferWord3);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) buf_st4<kSysCoherent>(__float_as_uint(o[t]), r, off + 64 * t);
+        } else {
+            float *base = reinterpret_cast<float *>(reinterpret_cast<char *>(p.part_acc + idx0 * D) + off);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) base[16 * t] = o[t];
+        }
+        if (lane == 0) {
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                put(p.part_max + idx0 + (int64_t)h * S, m[h] == kNegInf ? kNegInf : m[h] * kLn2);
+                put(p.part_sum + idx0 + (int64_t)h * S, lsum[h]);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) oacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        pacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            m[h] = kNegInf;
+            lpart[h] = 0.f;
+        }
+    };
+
     // Software pipeline over this wave's pages: the next page's K loads are
     // issued as soon as QK^T has consumed the K registers, each half of its V
     // loads as soon as P.V has consumed that half of the V registers, so
@@ -569,10 +639,134 @@ void decode_kernel(DecodeParams p,
             vsc_tok = vsc_next * (I8 ? 1.f : kF8ValueScale);
         }
     }
+    // The matrix-core P.V loop keeps its loads in flight across iterations;
+    // the first page's loads complete before it starts, so the compiler's
+    // wait insertion, which merges the state on entry with the loop's own,
+    // does not make every iteration wait for them.
+    if constexpr (MXPV) __builtin_amdgcn_s_waitcnt(kWaitVm0);
     for (; pg < pg1; pg += PSTEP) {
         int64_t page_next;
         const int valid_next = page_rows(pg + PSTEP, page_next);
         const int valid = min(P, L - pg * P);       // tokens of this page that count
+
+        if constexpr (MXPV) {
+            // ---- this page's K rows are in the tile: the loads issued after
+            // their direct-to-LDS loads are the two V halves (16 instructions).
+            // (The builtin, unlike an asm wait, is seen by the compiler's own
+            // wait insertion, which then knows the older loads are done.)
+            __builtin_amdgcn_s_waitcnt(kWaitVm16);
+            __builtin_amdgcn_sched_barrier(0);
+            load_v_scales(page_next, valid_next);
+            __builtin_amdgcn_sched_barrier(0);
+            // ---- S = Q K^T: lane (n, g) gets s[head h][token 16t + n] in sacc[t][h]
+            uint8_t(*kt)[KROWB] = ktile[wave];
+            f32x4_t sacc[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                sacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const uint2 h = *reinterpret_cast<const uint2 *>(
+                        &kt[16 * t + n][(((4 * (c >> 1) + g) ^ (n & 7)) << 4) + 8 * (c & 1)]);
+                    sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        qa16[c], i8x8_to_f16(h), sacc[t], 0, 0, 0);
+                }
+            }
+            // From here on lane (n, g) takes token 16g + n, its own lane
+            // index: the scores of tile g (every row group holds all 4 heads
+            // of every tile), and the key and value scales it loaded itself.
+            // Tokens past the context get -inf (the minimum with -inf).
+            float sc[4];
+            {
+                const float lim = lane < valid ? kPosInf : kNegInf;
+                const float kts = ksc_tok;
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    const float x = pick4(sacc[0][h], sacc[1][h], sacc[2][h], sacc[3][h], g);
+                    sc[h] = fminf(x * (qscale[h] * kts), lim);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            load_k_scales(page_next, valid_next);   // after the scores' last read
+            // the next page's K rows go into the tile once this page's
+            // operand reads have returned
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+            load_k(page_next, valid_next, 0, 4);
+            __builtin_amdgcn_sched_barrier(0);
+
+            // ---- online softmax (base 2); maxima over the wave's 64 tokens
+            float alpha[4], pr[4];
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const float mx = wave_max(sc[h]);
+                const float mnew = mx > m[h] ? mx : m[h];   // (no NaN-quieting as with fmaxf)
+                alpha[h] = exp2_fast(m[h] - mnew);
+                m[h] = mnew;
+                pr[h] = exp2_fast(sc[h] - mnew);
+                lpart[h] = __builtin_fmaf(lpart[h], alpha[h], pr[h]);
+            }
+            {   // P' = p * value scale, f16 (11 significant bits), row = token
+                const float vs = vsc_tok;
+                *reinterpret_cast<uint2 *>(&ptile[wave][lane][0]) =
+                    make_uint2(pack_f16x2(pr[0] * vs, pr[1] * vs), pack_f16x2(pr[2] * vs, pr[3] * vs));
+            }
+            if (alpha[0] != 1.f || alpha[1] != 1.f || alpha[2] != 1.f || alpha[3] != 1.f) {
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) oacc[t][h] *= alpha[h];
+#pragma unroll
+                for (int h = 0; h < 4; ++h) pacc[h] *= alpha[h];
+            }
+            __asm__ volatile("" ::: "memory");
+
+            // ---- O += P' V on the matrix cores, one half page (32 tokens,
+            // one k-step) at a time.  Contraction order: lane group G holds
+            // tokens 32 hf + 8G .. +7, element e = token 32 hf + 8G + e, in
+            // both operands.  A (P'): lane 16G + i gets head i & 3 through
+            // two 4-token transposed reads (lane 16G + q addresses token row
+            // 32 hf + 8G + 4r + q/4).  B (V): lane 16G + j gets dim 16T + j
+            // through one 8-token transposed byte read (lane 16G + q addresses
+            // token row 8G + q/2, bytes 16T + 8 (q & 1) ..).
+            const int q16 = lane & 15;
+            const int vt_rd = (wave * (P / 2) + 8 * g + (q16 >> 1)) * VROWB + 8 * (q16 & 1);
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                // this half's value codes into the tile (lane (r, c): token
+                // 4i + r, dims 8c .. 8c + 7), then its registers take the
+                // next page's half
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    *reinterpret_cast<uint2 *>(&vtile[wave][4 * i + vr][8 * vc]) = vr8[8 * hf + i];
+                __asm__ volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+                load_v_half(page_next, valid_next, hf);
+                __builtin_amdgcn_sched_barrier(0);
+                const uint16_t *prow = &ptile[wave][32 * hf + 8 * g + (q16 >> 2)][0];
+                const f16x8_t pa = join_f16x8(lds_tr16_b64(prow), lds_tr16_b64(prow + 16));
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    // one flat offset from the tile's base: the compiler then
+                    // still knows which LDS object each read touches, and does
+                    // not hold it back for the key rows' direct-to-LDS loads
+                    const uint2 w = lds_tr8_b64(&vtile[0][0][0] + vt_rd + 16 * t);
+                    oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        pa, i8x8_to_f16_biased(w),
+                        oacc[t], 0, 0, 0);
+                }
+                const f16x8_t ones = {1, 1, 1, 1, 1, 1, 1, 1};
+                pacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, ones, pacc, 0, 0, 0);
+                __asm__ volatile("" ::: "memory");
+            }
+            vsc_tok = vsc_next;
+            if (pg + 1 == split_end) {
+                finish_split_mx(jcur);
+                ++jcur;
+                split_end = min(split_end + pps, pages);
+            }
+            continue;
+        }
+
 
         // ---- S = Q K^T: lane (n, g) gets s[head h][token 16t + n] in sacc[t][h]
         f32x4_t sacc[4];

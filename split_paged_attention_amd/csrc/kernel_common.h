@@ -17,6 +17,11 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));   // store operand
 // Cache-policy immediate of buffer accesses for system-scope coherence
 // (sc0 sc1): stores write through to memory, loads bypass the caches.
 constexpr int kSysCoherent = 17;
+// s_waitcnt immediates (gfx9 layout: vmcnt bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8; a field at its maximum does not wait).
+constexpr int kWaitVm0 = 0x0F70;     // vmcnt(0)
+constexpr int kWaitVm16 = 0x4F70;    // vmcnt(16)
+constexpr int kWaitLgkm0 = 0xC07F;   // lgkmcnt(0)
 // Cache-policy immediate for data read once (nt, streaming).
 constexpr int kStreaming = 2;
 
@@ -26,6 +31,10 @@ constexpr int kStreaming = 2;
 template <int AUX = 0>
 __device__ __forceinline__ void buf_st16(uint4 v, __amdgpu_buffer_rsrc_t r, int off) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, off, 0, AUX);
+}
+template <int AUX = 0>
+__device__ __forceinline__ void buf_st4(uint32_t v, __amdgpu_buffer_rsrc_t r, int off) {
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, AUX);
 }
 // AUX is the cache-policy immediate.
 template <int AUX = 0>
@@ -58,6 +67,7 @@ constexpr int kBufferWord3 = 0x00020000;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
+constexpr float kPosInf = __builtin_inff();
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -129,6 +139,16 @@ __device__ __forceinline__ f16x8_t i8x8_to_f16(uint2 w) {
 // Eight e4m3 key codes (dims in byte order) -> their exact f16 values; the
 // converter takes bytes 0-1 (word_sel false) or 2-3 of a word, low byte to
 // the low half.
+// Eight int8 value codes -> eight exact f16 values 1152 + code (the bias is
+// removed once per split through the sum of the probabilities).
+__device__ __forceinline__ f16x8_t i8x8_to_f16_biased(uint2 w) {
+    const uint32_t x = w.x ^ 0x80808080u, y = w.y ^ 0x80808080u;
+    constexpr uint32_t kExp = 0x64646464u;
+    return __builtin_bit_cast(f16x8_t, make_uint4(__builtin_amdgcn_perm(kExp, x, 0x04010400u),
+                                                  __builtin_amdgcn_perm(kExp, x, 0x04030402u),
+                                                  __builtin_amdgcn_perm(kExp, y, 0x04010400u),
+                                                  __builtin_amdgcn_perm(kExp, y, 0x04030402u)));
+}
 __device__ __forceinline__ f16x8_t e4m3x8_to_f16(uint2 w) {
     const f16x2_t h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.x, 1.f, false);
     const f16x2_t h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.x, 1.f, true);
@@ -163,6 +183,73 @@ template <int K>
 __device__ __forceinline__ uint32_t i8_pair_f16(uint32_t wb, uint32_t wa) {
     constexpr uint32_t sel = (uint32_t)K | (0x0Cu << 8) | ((uint32_t)(4 + K) << 16) | (0x0Cu << 24);
     return __builtin_amdgcn_perm(wb, wa, sel) ^ 0x64806480u;
+}
+
+// Maximum over the 64 lanes of a wave, returned as a wave-uniform value: the
+// row butterfly (xor 1, xor 2, half-row mirror, row mirror), then row 0 into
+// row 1 and row 2 into row 3 (broadcast of each row's lane 15), then rows 0-1
+// into rows 2-3 (lane 31), so lane 63 holds the maximum of all four rows.
+// One v_max_f32 with a DPP source per step; written out because the compiler
+// splits each step into a DPP move, a NaN-quieting max and the max.  The
+// inputs are never NaN.  s_nop 1 gives each DPP read the two wait states it
+// needs after the VALU write of its source.
+__device__ __forceinline__ float wave_max(float x) {
+    float y;
+    __asm__("s_nop 1\n\t"
+            "v_max_f32_dpp %0, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+            "s_nop 1\n\t"
+            "v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+            "s_nop 1\n\t"
+            "v_max_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+            "s_nop 1\n\t"
+            "v_max_f32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf\n\t"
+            "s_nop 1\n\t"
+            "v_max_f32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+            "s_nop 1\n\t"
+            "v_max_f32_dpp %0, %0, %0 row_bcast:31 row_mask:0xc bank_mask:0xf"
+            : "=&v"(y)
+            : "v"(x));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(y), 63));
+}
+
+// Transposed LDS reads (gfx950; lane mappings measured with an in-bounds
+// probe).  In each group of 16 lanes 16G .. 16G + 15, every lane supplies the
+// address of one 8-byte chunk, and
+//  * ds_read_b64_tr_b16: lane 16G + i receives as 16-bit element e (0..3)
+//    element i mod 4 of the chunk addressed by lane 16G + 4e + i/4;
+//  * ds_read_b64_tr_b8: lane 16G + i receives as byte e (0..7) byte i mod 8
+//    of the chunk addressed by lane 16G + 2e + i/8.
+// With chunks that are rows of a token-major tile, a lane thus gathers one
+// column (a head, a dimension) over 4 or 8 tokens: a matrix-core operand
+// whose contraction runs over tokens.
+__device__ __forceinline__ uint64_t lds_tr16_b64(const uint16_t *p) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16 *)(const_cast<uint16_t *>(p)));
+    return __builtin_bit_cast(uint64_t, v);
+}
+__device__ __forceinline__ uint2 lds_tr8_b64(const uint8_t *p) {
+    typedef int v2i32 __attribute__((ext_vector_type(2)));
+    typedef __attribute__((address_space(3))) v2i32 lds_v2i32;
+    const v2i32 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32 *)(const_cast<uint8_t *>(p)));
+    return make_uint2((uint32_t)v.x, (uint32_t)v.y);
+}
+__device__ __forceinline__ bf16x8_t join_bf16x8(uint64_t lo, uint64_t hi) {
+    return __builtin_bit_cast(bf16x8_t, make_uint4((uint32_t)lo, (uint32_t)(lo >> 32),
+                                                   (uint32_t)hi, (uint32_t)(hi >> 32)));
+}
+__device__ __forceinline__ f16x8_t join_f16x8(uint64_t lo, uint64_t hi) {
+    return __builtin_bit_cast(f16x8_t, make_uint4((uint32_t)lo, (uint32_t)(lo >> 32),
+                                                  (uint32_t)hi, (uint32_t)(hi >> 32)));
+}
+
+// v_g of four per-lane values, g = 0..3 (two levels of selects on the bits of
+// g, which compile to conditional moves rather than branches).
+__device__ __forceinline__ float pick4(float v0, float v1, float v2, float v3, int g) {
+    const float lo = (g & 1) ? v1 : v0;
+    const float hi = (g & 1) ? v3 : v2;
+    return (g & 2) ? hi : lo;
 }
 
 // Value of v in lane src (a cross-lane permute, no memory access).

@@ -40,23 +40,6 @@ constexpr int kVerifyWaves = 2;   // kv heads per workgroup, one per wave
 template <int RB>
 constexpr int verify_stash_floats() { return RB * (32 * 64 + 32); }
 
-// Transposed LDS read of 4 16-bit elements (see the addressing in the kernel).
-__device__ __forceinline__ uint64_t tr_read(const uint16_t *p) {
-    typedef short v4i16 __attribute__((ext_vector_type(4)));
-    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-    const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_v4i16 *)(const_cast<uint16_t *>(p)));
-    return __builtin_bit_cast(uint64_t, v);
-}
-__device__ __forceinline__ bf16x8_t join_bf16x8(uint64_t lo, uint64_t hi) {
-    return __builtin_bit_cast(bf16x8_t, make_uint4((uint32_t)lo, (uint32_t)(lo >> 32),
-                                                   (uint32_t)hi, (uint32_t)(hi >> 32)));
-}
-__device__ __forceinline__ f16x8_t join_f16x8(uint64_t lo, uint64_t hi) {
-    return __builtin_bit_cast(f16x8_t, make_uint4((uint32_t)lo, (uint32_t)(lo >> 32),
-                                                  (uint32_t)hi, (uint32_t)(hi >> 32)));
-}
-
 // KV: 0 = bf16 pages, 1 = int8 codes, 2 = e4m3 codes (with fp32 scales).
 // RB: row blocks of 4 query tokens x 4 heads; a workgroup takes 4 RB tokens.
 // Two blocks hold twice the accumulators, so they run one wave per SIMD.
@@ -474,13 +457,13 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
             uint64_t a_lo[RB], a_hi[RB];
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
-                a_lo[rb] = tr_read(&pt16[r0][16 * rb + tr_col]);
-                a_hi[rb] = tr_read(&pt16[r0 + 4][16 * rb + tr_col]);
+                a_lo[rb] = lds_tr16_b64(&pt16[r0][16 * rb + tr_col]);
+                a_hi[rb] = lds_tr16_b64(&pt16[r0 + 4][16 * rb + tr_col]);
             }
 #pragma unroll
             for (int blk = 0; blk < 8; ++blk) {
-                const uint64_t b_lo = tr_read(&vt[tr_row][16 * blk + tr_col]);
-                const uint64_t b_hi = tr_read(&vt[tr_row + 4][16 * blk + tr_col]);
+                const uint64_t b_lo = lds_tr16_b64(&vt[tr_row][16 * blk + tr_col]);
+                const uint64_t b_hi = lds_tr16_b64(&vt[tr_row + 4][16 * blk + tr_col]);
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb) {
                     if constexpr (!QUANT)
