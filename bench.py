@@ -526,6 +526,96 @@ def policy_sweep(args) -> int:
     return 0
 
 
+TIMELINE_NAMES = ["entry", "length known", "first page id", "first scores", "pages done",
+                  "states issued", "states in memory", "arrival counted", "merge done", "end"]
+
+
+def timeline(args) -> int:
+    """Per-wave timeline of one decode call from the diagnostics build
+    libspa_timeline.so (include/spa_timeline.h): warm-up calls on the rotated
+    pool, then --timeline-calls single calls, each on the next page copy,
+    stamped and read back.  Prints one JSON line: the last call's per-link
+    durations (between consecutive steps each wave reached) and, per page
+    count of a wave's workgroup, when its waves started and ended.  The
+    stamps themselves cost time: spans are longer than the library's."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import split_paged_attention_amd as spa
+    from split_paged_attention_amd import build as spa_build
+    import workloads as W
+
+    if not os.path.exists(spa_build.TIMELINE_LIB):
+        print(f"{spa_build.TIMELINE_LIB} is missing: build it first "
+              "(python split_paged_attention_amd/build.py --timeline)", file=sys.stderr)
+        return 2
+    spa.LIB_PATH = spa_build.TIMELINE_LIB
+    L = spa.lib()
+    L.spa_timeline_clear.argtypes = []
+    L.spa_timeline_clear.restype = ctypes.c_int
+    L.spa_timeline_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    L.spa_timeline_read.restype = ctypes.c_int
+    SLOTS, WAVES = 16, 65536
+    torch.cuda.set_device(0)
+    case = W.make_config(args.config)
+    rig = Rig(case)
+    i = 0
+    t_end = time.time() + max(args.settle_ms, 30.0) / 1e3
+    while i < args.warmup or time.time() < t_end:
+        rig.attn(i)
+        i += 1
+        if i % 64 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    spans, t = [], None
+    for _ in range(args.timeline_calls):
+        if L.spa_timeline_clear() != 0:
+            raise RuntimeError("spa_timeline_clear failed")
+        rig.attn(i)
+        i += 1
+        torch.cuda.synchronize()
+        buf = np.zeros(WAVES * SLOTS, dtype=np.uint64)
+        if L.spa_timeline_read(buf.ctypes.data, buf.nbytes) != 0:
+            raise RuntimeError("spa_timeline_read failed")
+        t = buf.reshape(WAVES, SLOTS)[:, :].astype(np.int64)
+        t = t[t[:, 0] != 0]
+        spans.append(float((t[:, 9].max() - t[:, 0].min()) / 100.0))
+    base = t[:, 0].min()
+    us = lambda x: (x - base) / 100.0     # 100 MHz clock -> us
+    links = {}
+    for k in range(1, 9):
+        ok = (t[:, k] != 0) & (t[:, k - 1] != 0)
+        if ok.any():
+            d = (t[ok, k] - t[ok, k - 1]) / 100.0
+            links[f"{TIMELINE_NAMES[k - 1]} -> {TIMELINE_NAMES[k]}"] = {
+                "waves": int(ok.sum()), "min_us": round(float(d.min()), 3),
+                "median_us": round(float(np.median(d)), 3),
+                "p90_us": round(float(np.percentile(d, 90)), 3), "max_us": round(float(d.max()), 3)}
+    at = {TIMELINE_NAMES[k]: round(float(np.median(us(t[t[:, k] != 0, k]))), 3)
+          for k in range(10) if (t[:, k] != 0).any()}
+    st, en, npg = us(t[:, 0]), us(t[:, 9]), t[:, 11]
+    by_pages = {}
+    for k in sorted(set(npg.tolist())):
+        m = npg == k
+        by_pages[str(k)] = {"waves": int(m.sum()), "start_median_us": round(float(np.median(st[m])), 2),
+                            "end_median_us": round(float(np.median(en[m])), 2),
+                            "end_max_us": round(float(en[m].max()), 2),
+                            "life_median_us": round(float(np.median(en[m] - st[m])), 2)}
+    flags = spa.decode_default_flags(case.batch, case.num_kv_heads, case.num_splits, case.kv_dtype,
+                                     case.max_seq_pages)
+    rec = {"timeline": case.name, "library": os.path.basename(spa.LIB_PATH),
+           "default_flags": int(flags), "waves": int(t.shape[0]), "calls": len(spans),
+           "span_us": [round(x, 2) for x in spans],
+           "wave_start_us_pct": [round(float(x), 2) for x in np.percentile(st, [0, 50, 90, 100])],
+           "wave_end_us_pct": [round(float(x), 2) for x in np.percentile(en, [0, 50, 90, 100])],
+           "step_median_us": at, "links": links, "by_workgroup_pages": by_pages,
+           "rotation": {"page_copies": rig.R}}
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -559,6 +649,10 @@ def main() -> int:
                     help="time both producers and merges over a grid of decode shapes")
     ap.add_argument("--verify-qlen", type=int, default=0,
                     help="multi-token decode with this many query tokens per request (1..64)")
+    ap.add_argument("--timeline", action="store_true",
+                    help="per-wave timeline of the one-token decode producer (diagnostics "
+                         "build libspa_timeline.so) instead of the bench line")
+    ap.add_argument("--timeline-calls", type=int, default=5)
     args = ap.parse_args()
 
     if args.summarize_trace:
@@ -589,6 +683,8 @@ def main() -> int:
     import split_paged_attention_amd as spa
     import workloads as W
 
+    if args.timeline:
+        return timeline(args)
     torch.cuda.set_device(0)
     spa.lib()  # fail loudly if the HIP library is missing
     if args.ablation:

@@ -12,6 +12,10 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libspa.so")
 OBJDIR = os.path.join(HERE, "_build")
+# The diagnostics build: the same sources with SPA_TIMELINE defined (per-wave
+# timeline of the decode producer, include/spa_timeline.h).
+TIMELINE_LIB = os.path.join(HERE, "libspa_timeline.so")
+TIMELINE_OBJDIR = os.path.join(HERE, "_build_timeline")
 SOURCES = ["metadata.hip", "decode_attention.hip", "verify_attention.hip", "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -22,9 +26,10 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC] + DEVICE_FLAGS
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + COMMON + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, verbose: bool, objdir: str = OBJDIR, defines=()) -> str:
+    obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC] + COMMON + [f"-D{d}" for d in defines] + ["-x", "hip", "-c",
+                                                            os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -37,19 +42,31 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(OBJDIR, exist_ok=True)
+def _build(lib: str, objdir: str, defines, verbose: bool) -> str:
+    os.makedirs(objdir, exist_ok=True)
     with ThreadPoolExecutor(len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, objdir, defines), SOURCES))
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = True) -> str:
+    """libspa.so, the library."""
+    return _build(LIB, OBJDIR, (), verbose)
+
+
+def build_timeline(verbose: bool = True) -> str:
+    """libspa_timeline.so, the diagnostics build (not used by the library)."""
+    return _build(TIMELINE_LIB, TIMELINE_OBJDIR, ("SPA_TIMELINE",), verbose)
 
 
 if __name__ == "__main__":
     build()
+    if "--timeline" in sys.argv[1:]:
+        build_timeline()
     sys.exit(0)

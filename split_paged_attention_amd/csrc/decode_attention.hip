@@ -45,6 +45,22 @@
 #include "kernel_common.h"
 
 namespace spa {
+
+#ifdef SPA_TIMELINE
+// Diagnostics build only: the per-wave timeline (include/spa_timeline.h).
+__device__ uint64_t timeline_buf[kTimelineWaves * kTimelineSlots];
+#define SPA_TL_VAL(k, v)                                                    \
+    do {                                                                    \
+        if (tl_on) timeline_buf[tl_row + (k)] = (uint64_t)(v);              \
+    } while (0)
+#define SPA_TL(k) SPA_TL_VAL(k, __builtin_amdgcn_s_memrealtime())
+#else
+#define SPA_TL_VAL(k, v) \
+    do {                 \
+    } while (0)
+#define SPA_TL(k) SPA_TL_VAL(k, 0)
+#endif
+
 namespace {
 
 // ---------------------------------------------------------------------------
@@ -223,6 +239,12 @@ void decode_kernel(DecodeParams p,
     // wave index is uniform per wave; say so, so that page ids, buffer
     // descriptors and loop bounds live in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#ifdef SPA_TIMELINE
+    const size_t tl_wave = (size_t)blockIdx.x * NW + wave;
+    const bool tl_on = lane == 0 && tl_wave < kTimelineWaves;
+    const size_t tl_row = tl_wave * kTimelineSlots;
+#endif
+    SPA_TL(kTlEntry);
     const int n = lane & 15, g = lane >> 4;     // QK layout: token n of a 16-block, k-chunk g
     const int vr = lane >> 4, vc = lane & 15;   // PV layout: token phase r, dims 8c..8c+7
 
@@ -297,6 +319,7 @@ void decode_kernel(DecodeParams p,
     // A length the page-table row cannot cover is cut to the row, so the
     // page-id loads stay inside it.
     L = (int)min((int64_t)max(L, 0), p.pt_stride * P);
+    SPA_TL(kTlLength);
     const int kvh = kvblock * kv_per_grp + (HG ? wave : 0);
     const int pages = (L + P - 1) / P;
     const int pps = (pages + S - 1) / S;
@@ -630,6 +653,7 @@ void decode_kernel(DecodeParams p,
     if (pg < pg1) {
         int64_t page;
         const int rows = page_rows(pg, page);
+        SPA_TL(kTlFirstPageId);
         load_k(page, rows);
         if constexpr (QUANT && KSTAGE) load_k_scales(page, rows);
         load_v_half(page, rows, 0);
@@ -644,6 +668,9 @@ void decode_kernel(DecodeParams p,
     // wait insertion, which merges the state on entry with the loop's own,
     // does not make every iteration wait for them.
     if constexpr (MXPV) __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    SPA_TL_VAL(kTlWhat, (uint64_t)b | ((uint64_t)kvh << 16) | ((uint64_t)j << 32));
+    SPA_TL_VAL(kTlPages, pg1 - pg0);
+    [[maybe_unused]] const int pg_first = pg;
     for (; pg < pg1; pg += PSTEP) {
         int64_t page_next;
         const int valid_next = page_rows(pg + PSTEP, page_next);
@@ -686,6 +713,7 @@ void decode_kernel(DecodeParams p,
                     sc[h] = fminf(x * (qscale[h] * kts), lim);
                 }
             }
+            if (pg == pg_first) SPA_TL(kTlFirstScores);
             __builtin_amdgcn_sched_barrier(0);
             load_k_scales(page_next, valid_next);   // after the scores' last read
             // the next page's K rows go into the tile once this page's
@@ -843,6 +871,7 @@ void decode_kernel(DecodeParams p,
                 s[t][h] = ok ? sacc[t][h] * f : kNegInf;
             }
         }
+        if (pg == pg_first) SPA_TL(kTlFirstScores);
         if constexpr (!KSTAGE) {
             // keep the prefetch after the last read of the K registers it reuses
             __builtin_amdgcn_sched_barrier(0);
@@ -1052,6 +1081,7 @@ void decode_kernel(DecodeParams p,
             }
         }
     }
+    SPA_TL(kTlPagesDone);
     if constexpr (HG) {
         // splits of this workgroup with no pages (past the context): empty
         // states (the others were written at their last page)
@@ -1112,6 +1142,7 @@ void decode_kernel(DecodeParams p,
         }
     }
 
+    SPA_TL(kTlStatesIssued);
     if constexpr (FUSED) {
         // Last-split-done: the partial state above went to memory with
         // write-through stores; once every wave's stores have completed, one
@@ -1131,12 +1162,14 @@ void decode_kernel(DecodeParams p,
         // drop.
         __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+        SPA_TL(kTlStatesInMemory);
         if (threadIdx.x == 0) {
             const int old = __hip_atomic_fetch_add(p.counters + grp, 1, __ATOMIC_RELAXED,
                                                    __HIP_MEMORY_SCOPE_SYSTEM);
             sm_last = (old == S - 1);
         }
         __syncthreads();
+        SPA_TL(kTlArrived);
         if (sm_last) {
             // all query heads of this workgroup's kv heads: HEADS rows of
             // D outputs, VEC consecutive outputs per thread
@@ -1158,8 +1191,10 @@ void decode_kernel(DecodeParams p,
                                p.lse != nullptr && d0 == 0);
             if (threadIdx.x == 0)
                 __hip_atomic_store(p.counters + grp, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            SPA_TL(kTlMergeDone);
         }
     }
+    SPA_TL(kTlEnd);
 }
 
 // Separate merge: one workgroup per (b, h) row.
@@ -1339,3 +1374,23 @@ hipError_t launch_fill_zero(void *ptr, size_t words, hipStream_t stream) {
 }
 
 }  // namespace spa
+
+#ifdef SPA_TIMELINE
+#include "spa.h"
+#include "spa_timeline.h"
+static_assert(SPA_TIMELINE_SLOTS == spa::kTimelineSlots && SPA_TIMELINE_WAVES == spa::kTimelineWaves,
+              "timeline shape");
+extern "C" int spa_timeline_clear(void) {
+    void *ptr = nullptr;
+    hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(spa::timeline_buf));
+    if (e == hipSuccess) e = hipMemset(ptr, 0, sizeof(spa::timeline_buf));
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    return e == hipSuccess ? SPA_OK : SPA_ERR_HIP;
+}
+extern "C" int spa_timeline_read(uint64_t *dst, size_t bytes) {
+    if (dst == nullptr || bytes > sizeof(spa::timeline_buf)) return SPA_ERR_INVALID_ARGUMENT;
+    const hipError_t e = hipMemcpyFromSymbol(dst, HIP_SYMBOL(spa::timeline_buf), bytes, 0,
+                                             hipMemcpyDeviceToHost);
+    return e == hipSuccess ? SPA_OK : SPA_ERR_HIP;
+}
+#endif

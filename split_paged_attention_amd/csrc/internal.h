@@ -12,6 +12,15 @@ namespace spa {
 constexpr int kHeadDim = 128;
 constexpr int kPageSize = 64;
 constexpr int kGroup = 4;       // query heads per kv head
+// Per-wave timeline of the decode producer (diagnostics build, SPA_TIMELINE):
+// slot numbers of include/spa_timeline.h.
+enum TimelineSlot : int {
+    kTlEntry = 0, kTlLength = 1, kTlFirstPageId = 2, kTlFirstScores = 3, kTlPagesDone = 4,
+    kTlStatesIssued = 5, kTlStatesInMemory = 6, kTlArrived = 7, kTlMergeDone = 8, kTlEnd = 9,
+    kTlWhat = 10, kTlPages = 11
+};
+constexpr int kTimelineSlots = 16;
+constexpr size_t kTimelineWaves = 65536;
 // Multi-token decode: query tokens per request the host may declare
 // (max_q_len); one workgroup takes up to 8 of them, more are cut into chunks.
 constexpr int kMaxVerifyQueryLen = 64;

@@ -18,8 +18,11 @@ FAKE = ctypes.c_void_p(0x100000)       # aligned, never dereferenced
 FAKE_ODD = ctypes.c_void_p(0x100002)   # misaligned
 
 
-def declared_functions():
-    text = open(HEADER).read()
+TIMELINE_HEADER = os.path.join(ROOT, "include", "spa_timeline.h")
+
+
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(spa_[a-z0-9_]+)\s*\(", text)))
 
@@ -41,6 +44,25 @@ def test_library_exports_every_declared_symbol():
         assert n in exported, n
         assert hasattr(L, n)
     assert L.spa_abi_version() == 3
+
+
+def _exports(path):
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                         check=True).stdout
+    return set(l.split()[-1] for l in out.splitlines() if l.strip())
+
+
+def test_timeline_build_exports_the_library_and_its_own_calls():
+    """libspa_timeline.so (the diagnostics build) exports every function of
+    spa.h and of spa_timeline.h; libspa.so exports none of the latter."""
+    from split_paged_attention_amd import build as spa_build
+    tl = _exports(spa_build.TIMELINE_LIB)
+    own = declared_functions(TIMELINE_HEADER)
+    assert own == ["spa_timeline_clear", "spa_timeline_read"]
+    for n in declared_functions() + own:
+        assert n in tl, n
+    lib_exports = _exports(spa.LIB_PATH)
+    assert not any(n in lib_exports for n in own)
 
 
 def test_status_strings():
