@@ -259,13 +259,14 @@ void decode_kernel(DecodeParams p,
     // XCDs in serpentine order (ragged int8 batch: 71.5 -> 64.7 us against
     // round robin).  Otherwise the S splits of a group share an XCD.
     const int S = p.splits;
-    // A head-grouped workgroup with the separate merge walks `walk`
-    // consecutive splits (S a multiple of it), one page pipeline across the
-    // split boundaries, writing each split's state as it completes: grids
+    // A head-grouped bf16 workgroup walks `walk` consecutive splits (S a
+    // multiple of it), one page pipeline across the split boundaries, the
+    // states of all but its last split kept in LDS until the walk ends: grids
     // larger than the GPU's resident workgroups then run in one round, and
     // the later splits skip the workgroup start (request ranking, page-id
-    // and first-page latency).  Each split's arithmetic is unchanged.
-    const int walk = (HG && !FUSED && !QUANT && p.split_walk > 1) ? p.split_walk : 1;
+    // and first-page latency).  Each split's arithmetic is unchanged.  With
+    // the fused merge a group's S splits arrive as its S / walk workgroups.
+    const int walk = (HG && !QUANT && p.split_walk > 1) ? p.split_walk : 1;
     const int SG = S / walk;                        // split groups per kv group
     const int kv_per_grp = HG ? NW : 1;             // kv heads per workgroup
     const int grp_per_b = p.hkv / kv_per_grp;
@@ -1022,7 +1023,7 @@ void decode_kernel(DecodeParams p,
                 // the loop: stores between the page loads measured 5 us per
                 // split boundary), start the next one
                 reduce_state();
-                if (!FUSED && pg + 1 < pg1) {
+                if (pg + 1 < pg1) {
                     float *st = stash + (wave * (walk - 1) + nstash) * kStashFloats;
                     float v8[8];
 #pragma unroll
@@ -1086,18 +1087,27 @@ void decode_kernel(DecodeParams p,
         // splits of this workgroup with no pages (past the context): empty
         // states (the others were written at their last page)
         for (int jw = jcur; jw < j + walk; ++jw) store_empty(jw);
-        // the stashed splits j .. j + nstash - 1 (separate merge only)
-        for (int k = 0; k < (FUSED ? 0 : nstash); ++k) {
+        // the stashed splits j .. j + nstash - 1
+        for (int k = 0; k < nstash; ++k) {
             const float *st = stash + (wave * (walk - 1) + k) * kStashFloats;
             const int64_t idx0 = ((int64_t)b * p.hq + kvh * kGroup) * S + j + k;
-            char *base = reinterpret_cast<char *>(p.part_acc + idx0 * D) + (vr * S * D + 8 * vc) * 4;
-            *reinterpret_cast<float4 *>(base) = *reinterpret_cast<const float4 *>(st + vr * D + 8 * vc);
-            *reinterpret_cast<float4 *>(base + 16) =
-                *reinterpret_cast<const float4 *>(st + vr * D + 8 * vc + 4);
+            const int off = (vr * S * D + 8 * vc) * 4;   // bytes from this wave's first row
+            const uint4 lo = *reinterpret_cast<const uint4 *>(st + vr * D + 8 * vc);
+            const uint4 hi = *reinterpret_cast<const uint4 *>(st + vr * D + 8 * vc + 4);
+            if constexpr (FUSED) {
+                const auto r = __builtin_amdgcn_make_buffer_rsrc(p.part_acc + idx0 * D, (short)0,
+                                                                 (3 * S + 1) * D * 4, kBufferWord3);
+                buf_st16<kSysCoherent>(lo, r, off);
+                buf_st16<kSysCoherent>(hi, r, off + 16);
+            } else {
+                char *base = reinterpret_cast<char *>(p.part_acc + idx0 * D) + off;
+                *reinterpret_cast<uint4 *>(base) = lo;
+                *reinterpret_cast<uint4 *>(base + 16) = hi;
+            }
             if (lane < 4) {
                 const float mk = st[4 * D + lane];
-                p.part_max[idx0 + (int64_t)lane * S] = mk == kNegInf ? kNegInf : mk * kLn2;
-                p.part_sum[idx0 + (int64_t)lane * S] = st[4 * D + 4 + lane];
+                put(p.part_max + idx0 + (int64_t)lane * S, mk == kNegInf ? kNegInf : mk * kLn2);
+                put(p.part_sum + idx0 + (int64_t)lane * S, st[4 * D + 4 + lane]);
             }
         }
     } else {
@@ -1166,7 +1176,8 @@ void decode_kernel(DecodeParams p,
         if (threadIdx.x == 0) {
             const int old = __hip_atomic_fetch_add(p.counters + grp, 1, __ATOMIC_RELAXED,
                                                    __HIP_MEMORY_SCOPE_SYSTEM);
-            sm_last = (old == S - 1);
+            // (a group's splits arrive as S / walk workgroups)
+            sm_last = (old == S / walk - 1);
         }
         __syncthreads();
         SPA_TL(kTlArrived);
@@ -1218,16 +1229,18 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t *__restrict__ p
 template <int KV, int NW, bool HG>
 hipError_t launch_nw(const DecodeParams &p_in, bool fused, hipStream_t stream) {
     DecodeParams p = p_in;
-    p.split_walk = (HG && !fused) ? split_walk_for(p, KV != 0, NW) : 1;
+    p.split_walk = HG ? split_walk_for(p, KV != 0, NW) : 1;
     if (p.split_walk > 1) {
         // the stash must fit beside the kernel's static LDS
-        static const size_t static_lds = [] {
+        auto lds_of = [](const void *f) {
             hipFuncAttributes a{};
-            return hipFuncGetAttributes(&a, reinterpret_cast<const void *>(
-                                                &decode_kernel<KV, NW, false, HG>)) == hipSuccess
-                       ? a.sharedSizeBytes
-                       : (size_t)65536;
-        }();
+            return hipFuncGetAttributes(&a, f) == hipSuccess ? a.sharedSizeBytes : (size_t)65536;
+        };
+        static const size_t static_lds_sep =
+            lds_of(reinterpret_cast<const void *>(&decode_kernel<KV, NW, false, HG>));
+        static const size_t static_lds_fused =
+            lds_of(reinterpret_cast<const void *>(&decode_kernel<KV, NW, true, HG>));
+        const size_t static_lds = fused ? static_lds_fused : static_lds_sep;
         const size_t max_lds = max_lds_per_block();
         while (p.split_walk > 1 &&
                static_lds + (size_t)NW * (p.split_walk - 1) * kStashFloats * sizeof(float) > max_lds)
@@ -1238,8 +1251,8 @@ hipError_t launch_nw(const DecodeParams &p_in, bool fused, hipStream_t stream) {
     // LDS stash for the states of all but the last split of a walk
     const size_t stash_bytes = (size_t)NW * (p.split_walk - 1) * kStashFloats * sizeof(float);
     if (fused)
-        hipLaunchKernelGGL((decode_kernel<KV, NW, true, HG>), dim3(grid), dim3(NW * 64), 0, stream,
-                           p, p.page_table, p.seq_lens);
+        hipLaunchKernelGGL((decode_kernel<KV, NW, true, HG>), dim3(grid), dim3(NW * 64),
+                           (unsigned)stash_bytes, stream, p, p.page_table, p.seq_lens);
     else
         hipLaunchKernelGGL((decode_kernel<KV, NW, false, HG>), dim3(grid), dim3(NW * 64),
                            (unsigned)stash_bytes, stream, p, p.page_table, p.seq_lens);
@@ -1267,7 +1280,7 @@ size_t max_lds_per_block() {
     return (size_t)device_attr<hipDeviceAttributeMaxSharedMemoryPerBlock>(65536);
 }
 
-// Splits one bf16 head-grouped workgroup walks (separate merge), from a
+// Splits one bf16 head-grouped workgroup walks, from a
 // sweep over batch 8-32 x context 1K-8K x 4/8/16 splits: fewer, longer page
 // streams read faster.  Walks first cut the grid to one round of resident
 // workgroups (4 per CU); splits of at least 4 pages then walk on down to one

@@ -414,8 +414,10 @@ def test_split_walk_ragged(S):
     consecutive splits (states of all but the last kept in LDS until the
     workgroup ends): ragged lengths with empty requests, exact page
     multiples and splits past the context inside a walk.  Checked against
-    the oracle, and bit-exactly against the fused launch, whose workgroups
-    take one split each."""
+    the oracle; the fused launch (which walks too, a group's splits arriving
+    as its walks) bit-exactly against the separate one; and four of the
+    requests alone (a grid too small to walk) bit-exactly against their rows
+    of the walked call, since a walk changes no split's arithmetic."""
     rng = W._gen(64, 7)
     lens = rng.integers(1, 4097, size=64)
     lens[:8] = [0, 1, 63, 64, 65, 4096, 4095, 129]
@@ -428,6 +430,16 @@ def test_split_walk_ragged(S):
     o2, l2 = d.attention(producer="head_grouped", merge="fused")
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+    # lengths 65, 4096, 4095, 129: 4 x 4 kv-head blocks x S workgroups (at
+    # most 256) is one per CU at most, a grid no walk shortens
+    rows = slice(4, 8)
+    o3, l3 = spa.paged_decode_attention(d.q[rows].contiguous(), d.k, d.v,
+                                        d.page_list[rows].contiguous(), d.seq_lens[rows].contiguous(),
+                                        S, float(c.scale), kv_dtype="bf16",
+                                        producer="head_grouped", merge="separate")
+    torch.cuda.synchronize()
+    assert torch.equal(o3.view(torch.int16), o1[rows].view(torch.int16))
+    assert torch.equal(l3, l1[rows])
 
 
 @pytest.mark.parametrize("Hkv", [1, 2, 6, 16])
