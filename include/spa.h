@@ -55,7 +55,8 @@ typedef enum spa_kv_dtype {
  * the in-workgroup combination, the merge placement changes nothing. */
 #define SPA_DECODE_SEPARATE_MERGE 0x1u  /* merge as a second launch */
 #define SPA_DECODE_FUSED_MERGE 0x2u     /* merge in the last split workgroup (one launch) */
-#define SPA_DECODE_HEAD_GROUPED 0x4u    /* producer: 2 kv heads per workgroup, waves walk all pages */
+#define SPA_DECODE_HEAD_GROUPED 0x4u    /* producer: 2 kv heads per workgroup (1-byte codes: 4 when
+                                           num_kv_heads is a multiple of 4), waves walk all pages */
 #define SPA_DECODE_PAGE_SPLIT 0x8u      /* producer: 1 kv head per workgroup, 4 waves share pages */
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -214,9 +215,9 @@ spa_status spa_workspace_reset(void *workspace, size_t bytes, hipStream_t stream
  * shape from batch, num_kv_heads, num_splits, kv_dtype and
  * page_table_stride (the same sizes always give the same choice, so results
  * are reproducible) and the merge placement that is faster for it; a bf16
- * head-grouped workgroup with the separate merge may also take several
- * consecutive splits, sized from the device's compute units (the per-split
- * arithmetic, and so the result, is unchanged).  L == 0 gives out = 0 and
+ * head-grouped workgroup may also take several consecutive splits, sized
+ * from the device's compute units (the per-split arithmetic, and so the
+ * result, is unchanged).  L == 0 gives out = 0 and
  * lse = -inf.  Contradictory flags (both merges, both producers) are
  * SPA_ERR_INVALID_ARGUMENT.
  *
@@ -270,10 +271,13 @@ spa_status spa_paged_decode_attention_noalloc(
  * sizes: one producer flag (SPA_DECODE_HEAD_GROUPED or SPA_DECODE_PAGE_SPLIT)
  * or'ed with one merge flag (SPA_DECODE_FUSED_MERGE or
  * SPA_DECODE_SEPARATE_MERGE).  Passing the result back as flags gives the
- * same launches.  The choice depends on these arguments only (and, for the
- * splits a bf16 head-grouped workgroup walks, on the current device's
- * compute units).  0 for sizes spa_paged_decode_attention would reject as
- * invalid or unsupported.
+ * same launches.  The flags depend on batch, num_kv_heads and num_splits
+ * (head grouped from 512 request x kv head x split triples and an even
+ * num_kv_heads; merge fused for up to 8 page-split or 4 head-grouped
+ * splits); kv_dtype and page_table_stride are checked.  Within the plan,
+ * the splits a bf16 head-grouped workgroup walks also depend on
+ * page_table_stride and the current device's compute units.  0 for sizes
+ * spa_paged_decode_attention would reject as invalid or unsupported.
  */
 uint32_t spa_decode_default_flags(int32_t batch, int32_t num_kv_heads, int32_t num_splits,
                                   spa_kv_dtype kv_dtype, int64_t page_table_stride);

@@ -1308,27 +1308,33 @@ int split_walk_for(const DecodeParams &p, bool quant, int nw) {
 }
 
 
-// Producer shapes.  Head-grouped: 2 kv heads per workgroup, each wave walks
-// all pages of its split (long per-wave streams, row-aligned reads).
-// Page-split: one kv head per workgroup, 4 waves sharing its pages (4x the
-// waves, for grids too small to fill the GPU otherwise).
-constexpr int kNwHeadGrouped = 2;
+// Producer shapes.  Head-grouped: a block of kv heads per workgroup, one
+// wave each, each wave walking all pages of its split (long per-wave
+// streams, row-aligned reads; the block's waves read adjacent pieces of the
+// same token rows).  bf16: 2 kv heads (4 measured 1% slower per call at
+// batch 32 / 8K).  1-byte codes: 4 kv heads when the kv heads divide into
+// blocks of 4, else 2 (4 against 2, alternating runs: ragged int8 batch
+// producer 53.4-53.8 -> 51.4-51.7 us, fp8 batch 32 / 8K 97.8-98.0 -> 96.6
+// us).  Page-split: one kv head per workgroup, 4 waves sharing its pages
+// (4x the waves, for grids too small to fill the GPU otherwise).
+constexpr int kNwHeadGrouped = 2;        // also the kv-head multiple head grouping needs
+constexpr int kNwHeadGroupedCodes = 4;
 constexpr int kNwPageSplit = 4;
 // Producer choice, from a sweep over batch 1-32 x context 1K-8K x 4/8/16
-// splits (32 query / 8 kv heads).  bf16: head grouped from 512 (request,
-// kv head, split) triples up, page split below.  1-byte codes: a head-grouped
-// wave reads half the bytes per token, so it needs more of them in flight --
-// head grouped from 2048 triples, or from 1024 when a split spans at most 16
-// pages; page split otherwise.
+// splits (32 query / 8 kv heads) for each KV type: head grouped from 512
+// (request, kv head, split) triples up, page split below.  (1-byte codes
+// needed 1024-2048 triples with 2 kv heads per workgroup; with 4 they
+// follow bf16.)
 constexpr int64_t kHeadGroupedMinWaves = 512;
-constexpr int64_t kHeadGroupedMinWavesQuant = 2048;
-constexpr int64_t kHeadGroupedMinWavesQuantShort = 1024;
-constexpr int64_t kShortSplitPages = 16;
 
 template <int KV>
 hipError_t launch_kv(const DecodeParams &p, DecodeMode mode, bool fused, hipStream_t stream) {
-    if (mode == DecodeMode::kHeadGrouped)
+    if (mode == DecodeMode::kHeadGrouped) {
+        if constexpr (KV != 0)
+            if (p.hkv % kNwHeadGroupedCodes == 0)
+                return launch_nw<KV, kNwHeadGroupedCodes, true>(p, fused, stream);
         return launch_nw<KV, kNwHeadGrouped, true>(p, fused, stream);
+    }
     return launch_nw<KV, kNwPageSplit, false>(p, fused, stream);
 }
 
@@ -1354,19 +1360,10 @@ hipError_t launch_decode(const DecodeParams &p, int kv_type, DecodeMode mode, bo
                               p.splits, p.out, p.lse, stream);
 }
 
-DecodeMode default_mode(int batch, int hkv, int splits, int kv_type, int64_t pt_width) {
+DecodeMode default_mode(int batch, int hkv, int splits) {
     if (hkv % kNwHeadGrouped != 0) return DecodeMode::kPageSplit;
     const int64_t waves = (int64_t)batch * hkv * splits;
-    bool grouped;
-    if (kv_type == kKvBf16) {
-        grouped = waves >= kHeadGroupedMinWaves;
-    } else {
-        // the page table's width bounds the pages of any request
-        const int64_t split_pages = (pt_width + splits - 1) / splits;
-        grouped = waves >= kHeadGroupedMinWavesQuant ||
-                  (waves >= kHeadGroupedMinWavesQuantShort && split_pages <= kShortSplitPages);
-    }
-    return grouped ? DecodeMode::kHeadGrouped : DecodeMode::kPageSplit;
+    return waves >= kHeadGroupedMinWaves ? DecodeMode::kHeadGrouped : DecodeMode::kPageSplit;
 }
 
 bool mode_supported(DecodeMode mode, int hkv) {

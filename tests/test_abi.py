@@ -197,10 +197,14 @@ def test_default_flags():
     assert f(1, 8, 4, "bf16", 16) == PS | FUS           # batch 1 / 1K, 4 splits
     assert f(1, 8, 16, "bf16", 128) == PS | SEP         # more than 8 splits: second launch
     assert f(8, 8, 4, "bf16", 16) == PS | FUS           # 256 triples
-    assert f(16, 8, 4, "bf16", 16) == HG | SEP          # 512 triples
+    assert f(16, 8, 4, "bf16", 16) == HG | FUS          # 512 triples, 4 splits
+    assert f(16, 8, 8, "bf16", 16) == HG | SEP          # 1024 triples, 8 splits
     assert f(32, 8, 16, "int8", 128) == HG | SEP        # 4096 triples
     assert f(8, 8, 16, "fp8", 128) == HG | SEP          # 1024 triples, 8-page splits
+    assert f(4, 8, 16, "int8", 16) == HG | SEP          # 512 triples
+    assert f(32, 8, 4, "fp8", 128) == HG | FUS          # 1024 triples, 4 splits
     assert f(8, 8, 4, "fp8", 128) == PS | FUS           # 256 triples
+    assert f(2, 8, 16, "int8", 16) == PS | SEP          # 256 triples, 16 splits
     assert f(32, 3, 16, "bf16", 128) == PS | SEP        # odd kv heads: page split only
     # every result is exactly one producer and one merge flag
     for args in [(1, 8, 1, "bf16", 1), (64, 8, 8, "int8", 32), (4, 2, 1024, "fp8", 128)]:
