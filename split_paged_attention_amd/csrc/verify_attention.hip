@@ -34,7 +34,13 @@
 namespace spa {
 namespace {
 
-constexpr int kVerifyWaves = 2;   // kv heads per workgroup, one per wave
+// kv heads per workgroup, one per wave: 4 when the kv heads divide into
+// fours, else 2 (4 against 2 at batch 32 / 8K, graph replay p50: bf16 4
+// tokens 207.0 -> 203.2 us, fp8 4 tokens 124.8 -> 122.2, bf16 6 tokens
+// 226.7 -> 219.2; the workgroup's waves read adjacent pieces of the same
+// token rows)
+constexpr int kVerifyWaves = 2;        // also the kv-head multiple the kernel needs
+constexpr int kVerifyWavesWide = 4;
 // One stashed split state of a wave: 32 accumulators per lane (64 lanes) and
 // row block, then the maxima and sums of the RB blocks' 16 rows.
 template <int RB>
@@ -43,11 +49,12 @@ constexpr int verify_stash_floats() { return RB * (32 * 64 + 32); }
 // KV: 0 = bf16 pages, 1 = int8 codes, 2 = e4m3 codes (with fp32 scales).
 // RB: row blocks of 4 query tokens x 4 heads; a workgroup takes 4 RB tokens.
 // Two blocks hold twice the accumulators, so they run one wave per SIMD.
-template <int KV, int RB>
-__global__ __launch_bounds__(kVerifyWaves * 64) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 2 : 1)))
+// NW: kv heads per workgroup.
+template <int KV, int RB, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 2 : 1)))
 void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
                    const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ cu_q) {
-    constexpr int D = kHeadDim, P = kPageSize, NW = kVerifyWaves;
+    constexpr int D = kHeadDim, P = kPageSize;
     constexpr int QT = 4 * RB;                   // query tokens per workgroup
     constexpr int PW = 16 * RB;                  // P tile width: the blocks' MFMA rows
     constexpr int STASH = verify_stash_floats<RB>();
@@ -533,38 +540,44 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
     }
 }
 
-template <int KV, int RB>
+template <int KV, int RB, int NW>
 hipError_t launch_verify_kv(const DecodeParams &p_in, hipStream_t stream) {
     constexpr int STASH = verify_stash_floats<RB>();
     DecodeParams p = p_in;
-    p.split_walk = split_walk_for(p, KV != 0, kVerifyWaves);
+    p.split_walk = split_walk_for(p, KV != 0, NW);
     if (p.split_walk > 1) {
         // the stash must fit beside the kernel's static LDS
         static const size_t static_lds = [] {
             hipFuncAttributes a{};
-            return hipFuncGetAttributes(&a, reinterpret_cast<const void *>(&verify_kernel<KV, RB>)) ==
+            return hipFuncGetAttributes(&a, reinterpret_cast<const void *>(&verify_kernel<KV, RB, NW>)) ==
                            hipSuccess
                        ? a.sharedSizeBytes
                        : (size_t)65536;
         }();
         const size_t max_lds = max_lds_per_block();
         while (p.split_walk > 1 &&
-               static_lds + (size_t)kVerifyWaves * (p.split_walk - 1) * STASH * sizeof(float) > max_lds)
+               static_lds + (size_t)NW * (p.split_walk - 1) * STASH * sizeof(float) > max_lds)
             p.split_walk /= 2;
     }
-    const unsigned grid = (unsigned)((int64_t)p.batch * (p.hkv / kVerifyWaves) *
+    const unsigned grid = (unsigned)((int64_t)p.batch * (p.hkv / NW) *
                                      (p.splits / p.split_walk) * p.q_chunks);
-    const size_t stash_bytes = (size_t)kVerifyWaves * (p.split_walk - 1) * STASH * sizeof(float);
-    hipLaunchKernelGGL((verify_kernel<KV, RB>), dim3(grid), dim3(kVerifyWaves * 64),
+    const size_t stash_bytes = (size_t)NW * (p.split_walk - 1) * STASH * sizeof(float);
+    hipLaunchKernelGGL((verify_kernel<KV, RB, NW>), dim3(grid), dim3(NW * 64),
                        (unsigned)stash_bytes, stream, p, p.page_table, p.seq_lens, p.cu_seqlens_q);
     return hipGetLastError();
 }
 
+template <int RB, int NW>
+hipError_t launch_verify_nw(const DecodeParams &p, int kv_type, hipStream_t stream) {
+    if (kv_type == kKvInt8) return launch_verify_kv<1, RB, NW>(p, stream);
+    if (kv_type == kKvFp8) return launch_verify_kv<2, RB, NW>(p, stream);
+    return launch_verify_kv<0, RB, NW>(p, stream);
+}
+
 template <int RB>
 hipError_t launch_verify_rb(const DecodeParams &p, int kv_type, hipStream_t stream) {
-    if (kv_type == kKvInt8) return launch_verify_kv<1, RB>(p, stream);
-    if (kv_type == kKvFp8) return launch_verify_kv<2, RB>(p, stream);
-    return launch_verify_kv<0, RB>(p, stream);
+    if (p.hkv % kVerifyWavesWide == 0) return launch_verify_nw<RB, kVerifyWavesWide>(p, kv_type, stream);
+    return launch_verify_nw<RB, kVerifyWaves>(p, kv_type, stream);
 }
 
 }  // namespace

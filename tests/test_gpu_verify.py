@@ -13,12 +13,12 @@ from tests.gpu_util import DevCase, bf16_dev, compare_attention, config_case
 pytestmark = pytest.mark.gpu
 
 
-def small_case(lens, kv="bf16", S=4, seed=31):
+def small_case(lens, kv="bf16", S=4, seed=31, Hkv=8):
     P = 64
     need = sum(-(-L // P) for L in lens)
     msp = max(1, max(-(-L // P) for L in lens))
     return W.make_case(seed=seed, seq_lens=lens, num_pages=need + 3, num_splits=S, kv_dtype=kv,
-                       num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=P,
+                       num_q_heads=4 * Hkv, num_kv_heads=Hkv, head_dim=128, page_size=P,
                        req_pool_rows=max(4, len(lens)), req_to_token_stride=msp * P,
                        max_seq_pages=msp, name=f"verify{lens}_{kv}_S{S}")
 
@@ -72,6 +72,20 @@ def test_verify_parity_up_to_eight_rows(kv, lens, qlens, S):
     out, lse = run_verify(c, q_rows, cu, max_q_len=8)
     o_ref, l_ref = oracle_verify(c, q_rows, cu)
     compare_attention(out, lse, o_ref, l_ref, label=f"verify8 {kv} {lens}")
+
+
+@pytest.mark.parametrize("Hkv", [2, 6, 4])
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_verify_kv_head_counts(kv, Hkv):
+    """Workgroups of 2 kv heads (2 or 6 kv heads) and of 4 (4 kv heads),
+    with 4 and with 6 query rows per request."""
+    c = small_case([700, 64, 1500, 9], kv=kv, S=4, seed=61, Hkv=Hkv)
+    for qlens, mq in (([4, 2, 3, 1], 4), ([6, 5, 2, 6], 8)):
+        q_rows, cu = W.verify_queries(c, qlens)
+        print(f"[case] verify Hkv={Hkv} {kv} qlens={qlens}", flush=True)
+        out, lse = run_verify(c, q_rows, cu, max_q_len=mq)
+        o_ref, l_ref = oracle_verify(c, q_rows, cu)
+        compare_attention(out, lse, o_ref, l_ref, label=f"verify Hkv={Hkv} {kv} {qlens}")
 
 
 @pytest.mark.parametrize("kv", ["bf16", "int8", "fp8"])
