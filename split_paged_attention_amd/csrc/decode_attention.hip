@@ -361,8 +361,7 @@ void decode_kernel(DecodeParams p,
         for (int c = 0; c < 4; ++c)
 #pragma unroll
             for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)qa[c][e]));
-        amax = fmaxf(amax, __shfl_xor(amax, 16));
-        amax = fmaxf(amax, __shfl_xor(amax, 32));   // lane n: head n & 3, all 128 dims
+        amax = max_xor32(max_xor16(amax));   // lane n: head n & 3, all 128 dims
         const int sh = amax > 0.f ? 15 - __builtin_amdgcn_frexp_expf(amax) : 0;
         const float up = __builtin_ldexpf(1.f, sh);
 #pragma unroll
@@ -541,8 +540,7 @@ void decode_kernel(DecodeParams p,
 #pragma unroll
             for (int d = 0; d < 8; ++d) {
                 float x = acc[h][d];
-                x += __shfl_xor(x, 16);
-                x += __shfl_xor(x, 32);
+                x = add_xor32(add_xor16(x));
                 acc[h][d] = x;
             }
         }
@@ -595,8 +593,7 @@ void decode_kernel(DecodeParams p,
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
             float x = row_sum16(lpart[h]);
-            x += __shfl_xor(x, 16);
-            x += __shfl_xor(x, 32);
+            x = add_xor32(add_xor16(x));
             lsum[h] = x;
         }
         const int64_t idx0 = ((int64_t)b * p.hq + kvh * kGroup) * S + jw;

@@ -92,6 +92,36 @@ __device__ __forceinline__ float row_sum16(float x) {
     return x;
 }
 
+// Lane l combined with lane l ^ 16 (xor16) or l ^ 32 (xor32), by the gfx950
+// cross-lane swaps (vector ALU, no LDS round trip as a shuffle takes).  A
+// value swapped with a copy of itself: v_permlane16_swap exchanges the odd
+// 16-lane rows of the first operand with the even rows of the second,
+// leaving rows (0, 0, 2, 2) and (1, 1, 3, 3); v_permlane32_swap exchanges
+// the upper 32 lanes of the first with the lower 32 of the second, leaving
+// (lo, lo) and (hi, hi).  Every lane then combines the same two values as
+// with a shuffle (the operands of a commutative operation in the other
+// order for half of the lanes: same result).  Whole wave active.
+__device__ __forceinline__ float add_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float add_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     bf16x2_t v;
     v[0] = (__bf16)lo;   // round to nearest even

@@ -198,8 +198,7 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
             for (int c = 0; c < 4; ++c)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)qa[rb][c][e]));
-            amax = fmaxf(amax, __shfl_xor(amax, 16));
-            amax = fmaxf(amax, __shfl_xor(amax, 32));   // lane n: row n, all 128 dims
+            amax = max_xor32(max_xor16(amax));   // lane n: row n, all 128 dims
             const int sh = amax > 0.f ? 15 - __builtin_amdgcn_frexp_expf(amax) : 0;
             const float up = __builtin_ldexpf(1.f, sh);
 #pragma unroll
