@@ -372,9 +372,25 @@ def test_full_step_config5_metadata_then_attention():
     compare_attention(out, lse, o_ref, l_ref, label="config 5 step")
 
 
-def test_hip_graph_replay_matches_eager():
-    c = config_case(3)
-    print("[case] HIP graph capture of the decode step", flush=True)
+def _walk_case():
+    lens = W._gen(64, 13).integers(1, 4097, size=64).tolist()
+    lens[:2] = [0, 4096]
+    return small_case(lens, kv="bf16", S=16, seed=64)
+
+
+def _int8_hg_case():
+    lens = W._gen(32, 17).integers(1, 3000, size=32).tolist()
+    return small_case(lens, kv="int8", S=4, seed=32)
+
+
+@pytest.mark.parametrize("make,kw", [
+    (lambda: config_case(3), {}),                     # default: page split, fused merge
+    (_walk_case, dict(producer="head_grouped", merge="fused")),   # fused with split walks
+    (_int8_hg_case, {}),                              # default: 4-head 1-byte, fused merge
+], ids=["b8_ctx1k_default", "bf16_walks_fused", "int8_hg_fused_default"])
+def test_hip_graph_replay_matches_eager(make, kw):
+    c = make()
+    print(f"[case] HIP graph capture of the decode step {c.name} {kw}", flush=True)
     d = DevCase(c)
     B, Hq, D, S = c.batch, c.num_q_heads, c.head_dim, c.num_splits
     ws = spa.new_workspace(B, Hq, c.num_kv_heads, D, S)
@@ -387,7 +403,7 @@ def test_hip_graph_replay_matches_eager():
     def step():
         spa.build_page_table(d.r2t, d.rpi, d.seq_lens, c.page_size, c.max_seq_pages,
                              page_table=pt, cache_seqlens=cache, cu_seqlens_k=cu)
-        d.attention(page_table=pt, workspace=ws, out=out, lse=lse)
+        d.attention(page_table=pt, workspace=ws, out=out, lse=lse, **kw)
 
     step()
     torch.cuda.synchronize()
