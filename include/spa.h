@@ -271,10 +271,11 @@ spa_status spa_paged_decode_attention_noalloc(
  * sizes: one producer flag (SPA_DECODE_HEAD_GROUPED or SPA_DECODE_PAGE_SPLIT)
  * or'ed with one merge flag (SPA_DECODE_FUSED_MERGE or
  * SPA_DECODE_SEPARATE_MERGE).  Passing the result back as flags gives the
- * same launches.  The flags depend on batch, num_kv_heads and num_splits
- * (head grouped from 512 request x kv head x split triples and an even
- * num_kv_heads; merge fused for up to 8 page-split or 4 head-grouped
- * splits); kv_dtype and page_table_stride are checked.  Within the plan,
+ * same launches.  The flags depend on batch, num_kv_heads, num_splits and
+ * kv_dtype (head grouped from 512 request x kv head x split triples for
+ * bf16 and 1024 for 1-byte codes, with an even num_kv_heads; merge fused
+ * for up to 8 page-split or 4 head-grouped splits); page_table_stride is
+ * checked.  Within the plan,
  * the splits a bf16 head-grouped workgroup walks also depend on
  * page_table_stride and the current device's compute units.  0 for sizes
  * spa_paged_decode_attention would reject as invalid or unsupported.

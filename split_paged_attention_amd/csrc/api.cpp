@@ -92,7 +92,7 @@ struct DecodePlan {
 DecodePlan default_plan(int32_t batch, int32_t hkv, int32_t splits, int kv_type) {
     DecodePlan plan{};
     plan.kv_type = kv_type;
-    plan.mode = spa::default_mode(batch, hkv, splits);
+    plan.mode = spa::default_mode(batch, hkv, splits, kv_type);
     const int fused_max_splits = plan.mode == spa::DecodeMode::kPageSplit ? 8 : 4;
     plan.fused = splits <= fused_max_splits && (int64_t)batch * hkv <= spa::kMaxCounterGroups;
     return plan;

@@ -489,11 +489,18 @@ void decode_kernel(DecodeParams p,
             } else if constexpr (!QUANT) {
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
-                    kr[t][c] = buf_ld16<KV_POLICY>(r, k_lane + 64 * c, 16 * t * row_bytes);
+                    // (default policy: each 128-byte line of a row comes
+                    // from two 64-byte loads; streamed, the page-split
+                    // producer measured 12% slower over the bf16 policy
+                    // sweep, batch 1 / 8K / 16 splits 16%)
+                    kr[t][c] = buf_ld16<0>(r, k_lane + 64 * c, 16 * t * row_bytes);
             } else {
 #pragma unroll
                 for (int c2 = 0; c2 < 2; ++c2)
-                    kr8[t][c2] = buf_ld16<KV_POLICY>(r, k_lane + 64 * c2, 16 * t * row_bytes);
+                    // (default policy, as for bf16 above: a row's two
+                    // 64-byte halves come from two loads; streamed, 10%
+                    // slower over the 1-byte policy sweeps)
+                    kr8[t][c2] = buf_ld16<0>(r, k_lane + 64 * c2, 16 * t * row_bytes);
             }
         }
         if constexpr (QUANT && !KSTAGE) load_k_scales(page, valid_rows);
@@ -1319,10 +1326,12 @@ constexpr int kNwHeadGroupedCodes = 4;
 constexpr int kNwPageSplit = 4;
 // Producer choice, from a sweep over batch 1-32 x context 1K-8K x 4/8/16
 // splits (32 query / 8 kv heads) for each KV type: head grouped from 512
-// (request, kv head, split) triples up, page split below.  (1-byte codes
-// needed 1024-2048 triples with 2 kv heads per workgroup; with 4 they
-// follow bf16.)
+// (request, kv head, split) triples up for bf16 and from 1024 for 1-byte
+// codes, page split below (the page-split producer's keys in 64-byte
+// pieces read faster with the default cache policy, which moved the
+// 1-byte threshold back up from 512).
 constexpr int64_t kHeadGroupedMinWaves = 512;
+constexpr int64_t kHeadGroupedMinWavesQuant = 1024;
 
 template <int KV>
 hipError_t launch_kv(const DecodeParams &p, DecodeMode mode, bool fused, hipStream_t stream) {
@@ -1357,10 +1366,11 @@ hipError_t launch_decode(const DecodeParams &p, int kv_type, DecodeMode mode, bo
                               p.splits, p.out, p.lse, stream);
 }
 
-DecodeMode default_mode(int batch, int hkv, int splits) {
+DecodeMode default_mode(int batch, int hkv, int splits, int kv_type) {
     if (hkv % kNwHeadGrouped != 0) return DecodeMode::kPageSplit;
     const int64_t waves = (int64_t)batch * hkv * splits;
-    return waves >= kHeadGroupedMinWaves ? DecodeMode::kHeadGrouped : DecodeMode::kPageSplit;
+    const int64_t min_waves = kv_type == kKvBf16 ? kHeadGroupedMinWaves : kHeadGroupedMinWavesQuant;
+    return waves >= min_waves ? DecodeMode::kHeadGrouped : DecodeMode::kPageSplit;
 }
 
 bool mode_supported(DecodeMode mode, int hkv) {

@@ -60,12 +60,17 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
     constexpr int STASH = verify_stash_floats<RB>();
     constexpr bool QUANT = KV != 0;
     constexpr bool I8 = KV == 1;
-    // K/V cache policy: bf16 pages stream past the caches (non-temporal
-    // loads, as in the one-token decode: batch 32 / 8K, 4 query tokens
-    // 200.2 -> 173.3 us per call, 6 tokens 215.4 -> 196.6 us); 1-byte codes
-    // keep the default policy (non-temporal measured 1% slower for fp8 and
-    // 6% for the ragged int8 batch).
-    constexpr int KV_POLICY = QUANT ? 0 : kStreaming;
+    // K/V cache policy: values stream past the caches (non-temporal loads,
+    // as in the one-token decode; bf16 at batch 32 / 8K, 4 query tokens
+    // 200.2 -> 173.3 us per call, 6 tokens 215.4 -> 196.6 us with keys
+    // and values streamed).  Keys, whose rows go out in 64-byte pieces,
+    // keep the default policy except for bf16 with one row block (1-byte
+    // codes, values streamed, keys default: fp8 4 tokens 118.9 -> 110.1 us,
+    // ragged int8 82.2 -> 81.6 us, keys streamed too: 117.6 and 88.0 us;
+    // bf16 keys default: 4 tokens 174.2 -> 183.5 us, 6 tokens 197.2 ->
+    // 194.4 us).
+    constexpr int K_POLICY = (QUANT || RB == 2) ? 0 : kStreaming;
+    constexpr int V_POLICY = kStreaming;
     constexpr int ES = QUANT ? 1 : 2;            // bytes per element
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -271,11 +276,11 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
             if constexpr (!QUANT) {
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
-                    kr[t][c] = buf_ld16<KV_POLICY>(r, k_lane + 64 * c, 16 * t * row_bytes);
+                    kr[t][c] = buf_ld16<K_POLICY>(r, k_lane + 64 * c, 16 * t * row_bytes);
             } else {
 #pragma unroll
                 for (int c2 = 0; c2 < 2; ++c2)
-                    kr8[t][c2] = buf_ld16<KV_POLICY>(r, k_lane + 64 * c2, 16 * t * row_bytes);
+                    kr8[t][c2] = buf_ld16<K_POLICY>(r, k_lane + 64 * c2, 16 * t * row_bytes);
             }
         }
         if constexpr (QUANT) {
@@ -290,9 +295,9 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
 #pragma unroll
         for (int i = 8 * half; i < 8 * half + 8; ++i) {
             if constexpr (!QUANT)
-                vr16[i] = buf_ld16<KV_POLICY>(r, v_lane, 4 * i * row_bytes);
+                vr16[i] = buf_ld16<V_POLICY>(r, v_lane, 4 * i * row_bytes);
             else
-                vr8[i] = buf_ld8<KV_POLICY>(r, v_lane, 4 * i * row_bytes);
+                vr8[i] = buf_ld8<V_POLICY>(r, v_lane, 4 * i * row_bytes);
         }
         if (QUANT && half == 0) {
             const auto rs = rsrc(p.v_scales, page, (int64_t)P * p.hkv, kvh, 4,

@@ -201,7 +201,8 @@ def test_default_flags():
     assert f(16, 8, 8, "bf16", 16) == HG | SEP          # 1024 triples, 8 splits
     assert f(32, 8, 16, "int8", 128) == HG | SEP        # 4096 triples
     assert f(8, 8, 16, "fp8", 128) == HG | SEP          # 1024 triples, 8-page splits
-    assert f(4, 8, 16, "int8", 16) == HG | SEP          # 512 triples
+    assert f(4, 8, 16, "int8", 16) == PS | SEP          # 512 triples: 1-byte page split
+    assert f(4, 8, 16, "bf16", 16) == HG | SEP          # 512 triples: bf16 head grouped
     assert f(32, 8, 4, "fp8", 128) == HG | FUS          # 1024 triples, 4 splits
     assert f(8, 8, 4, "fp8", 128) == PS | FUS           # 256 triples
     assert f(2, 8, 16, "int8", 16) == PS | SEP          # 256 triples, 16 splits

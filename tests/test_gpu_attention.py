@@ -172,15 +172,15 @@ def test_fused_equals_two_launch_bit_exact(kv, producer):
 @pytest.mark.parametrize("kv", ["bf16", "int8", "fp8"])
 def test_default_head_grouped_fused_merge(kv):
     """A head-grouped grid of 4 splits, where the default plan fuses the
-    merge into the producer launch (16 ragged requests x 8 kv heads x 4
-    splits = 512 triples): against the oracle, and bit-exactly against the
+    merge into the producer launch (32 ragged requests x 8 kv heads x 4
+    splits = 1024 triples): against the oracle, and bit-exactly against the
     two-launch merge."""
-    lens = W._gen(16, 5).integers(1, 3000, size=16).tolist()
+    lens = W._gen(32, 5).integers(1, 3000, size=32).tolist()
     lens[:3] = [1, 64, 2999]
     c = small_case(lens, kv=kv, S=4, seed=16)
-    assert spa.decode_default_flags(16, 8, 4, kv, c.max_seq_pages) == (
+    assert spa.decode_default_flags(32, 8, 4, kv, c.max_seq_pages) == (
         spa.SPA_DECODE_HEAD_GROUPED | spa.SPA_DECODE_FUSED_MERGE)
-    print(f"[case] default head-grouped fused {kv} batch 16 S=4", flush=True)
+    print(f"[case] default head-grouped fused {kv} batch 32 S=4", flush=True)
     d = DevCase(c)
     o1, l1 = d.attention()
     o_ref, l_ref = oracle.case_attention(c)
