@@ -469,8 +469,11 @@ def policy_sweep(args) -> int:
     """Producer x merge choice across decode shapes (batch 1-32, context
     1K-8K, 4/8/16 splits; 32 query / 8 KV heads, head_dim 128, 64-token pages
     drawn at random from a 4096-page pool): microseconds per call from HIP
-    graphs of 10 calls each, for both producers with both merges and for the
-    library's default.  One JSON line; a progress line per shape on stderr."""
+    graphs of R calls, for both producers with both merges and for the
+    library's default.  The R calls of a graph read disjoint page sets that
+    together cover the pool (R = pool pages // pages per call), so every
+    call reads pages the Infinity Cache has not held since the pool's last
+    pass.  One JSON line; a progress line per shape on stderr."""
     import itertools
 
     import torch
@@ -497,9 +500,10 @@ def policy_sweep(args) -> int:
     rows = []
     for B, L, S in itertools.product([1, 2, 4, 8, 16, 32], [1024, 2048, 4096, 8192], [4, 8, 16]):
         npg = B * (L // P)
+        R = max(1, pool // npg)
         q = torch.randn(B, Hq, D, device=dev, generator=g).to(torch.bfloat16)
-        pt = torch.randperm(pool, device=dev, generator=g)[:npg].to(torch.int32)
-        pt = pt.view(B, L // P).contiguous()
+        pts = torch.randperm(pool, device=dev, generator=g)[:R * npg].to(torch.int32)
+        pts = pts.view(R, B, L // P).contiguous()
         sl = torch.full((B,), L, dtype=torch.int32, device=dev)
         ws = spa.new_workspace(B, Hq, Hkv, D, S, device=dev)
         out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
@@ -507,13 +511,13 @@ def policy_sweep(args) -> int:
         us = []
         for prod, merge in variants:
             def call(i, prod=prod, merge=merge):
-                spa.paged_decode_attention(q, k, v, pt, sl, S, 0.0884, kv_dtype=kv,
+                spa.paged_decode_attention(q, k, v, pts[i % R], sl, S, 0.0884, kv_dtype=kv,
                                            k_scales=ks, v_scales=vs, workspace=ws, out=out,
                                            lse=lse, producer=prod, merge=merge)
 
-            us.append(time_graph(capture(call, 10), 10, 10, warm_ms=10.0)[0])
+            us.append(time_graph(capture(call, R), R, max(2, 40 // R), warm_ms=10.0)[0])
         best = min(range(4), key=lambda i: us[i])
-        rows.append({"batch": B, "context": L, "splits": S, "waves": B * Hkv * S,
+        rows.append({"batch": B, "context": L, "splits": S, "waves": B * Hkv * S, "calls": R,
                      "page_split_fused_us": round(us[0], 2),
                      "page_split_separate_us": round(us[1], 2),
                      "head_grouped_fused_us": round(us[2], 2),

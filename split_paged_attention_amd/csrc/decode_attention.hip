@@ -490,16 +490,19 @@ void decode_kernel(DecodeParams p,
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
                     // (default policy: each 128-byte line of a row comes
-                    // from two 64-byte loads; streamed, the page-split
-                    // producer measured 12% slower over the bf16 policy
-                    // sweep, batch 1 / 8K / 16 splits 16%)
+                    // from two 64-byte loads.  Over the bf16 policy sweep,
+                    // page sets rotated over a 1 GiB pool, streaming them
+                    // measured 2.6% slower in geometric mean: 4-9% slower
+                    // where a wave reads 2 or more pages of a split, 4-5%
+                    // faster below one page)
                     kr[t][c] = buf_ld16<0>(r, k_lane + 64 * c, 16 * t * row_bytes);
             } else {
 #pragma unroll
                 for (int c2 = 0; c2 < 2; ++c2)
                     // (default policy, as for bf16 above: a row's two
-                    // 64-byte halves come from two loads; streamed, 10%
-                    // slower over the 1-byte policy sweeps)
+                    // 64-byte halves come from two loads; streamed, 6.5%
+                    // slower in geometric mean over the int8 and fp8
+                    // policy sweeps)
                     kr8[t][c2] = buf_ld16<0>(r, k_lane + 64 * c2, 16 * t * row_bytes);
             }
         }

@@ -48,7 +48,7 @@ struct DecodeParams {
     int64_t pt_stride;
     const int32_t *seq_lens;   // [B]
     int32_t batch, hq, hkv, splits;
-    int32_t split_walk;        // head-grouped, separate merge: splits per workgroup (divides splits)
+    int32_t split_walk;        // head-grouped bf16: splits per workgroup (divides splits)
     int32_t num_pages;         // pool size: page ids outside [0, num_pages) load nothing
     float qk_scale_log2;       // scale * log2(e)
     float *part_acc;           // [B, Hq, S, D]
