@@ -304,14 +304,19 @@ void decode_kernel(DecodeParams p,
         b = 0;
         L = seq_lens[0];
     } else if (p.batch <= 64) {
+        // (equal lengths skip the ranking: rank r is request r; batch 32 /
+        // 8K producer 162.2 -> 161.0 us bf16, 95.9 -> 94.7 us fp8)
         const int Li = lane < p.batch ? seq_lens[lane] : INT32_MIN;
-        int rank = 0;
-        for (int k = 0; k < p.batch; ++k) {
-            const int Lk = __builtin_amdgcn_readlane(Li, k);
-            rank += (Lk > Li) || (Lk == Li && k < lane);
+        b = r;
+        if (__ballot(lane < p.batch && Li != __builtin_amdgcn_readfirstlane(Li)) != 0) {
+            int rank = 0;
+            for (int k = 0; k < p.batch; ++k) {
+                const int Lk = __builtin_amdgcn_readlane(Li, k);
+                rank += (Lk > Li) || (Lk == Li && k < lane);
+            }
+            const unsigned long long hit = __ballot(lane < p.batch && rank == r);
+            b = __builtin_amdgcn_readfirstlane(__ffsll((long long)hit) - 1);
         }
-        const unsigned long long hit = __ballot(lane < p.batch && rank == r);
-        b = __builtin_amdgcn_readfirstlane(__ffsll((long long)hit) - 1);
         L = __builtin_amdgcn_readlane(Li, b);
     } else {
         b = r;
