@@ -585,6 +585,10 @@ def timeline(args) -> int:
             raise RuntimeError("spa_timeline_read failed")
         t = buf.reshape(WAVES, SLOTS)[:, :].astype(np.int64)
         t = t[t[:, 0] != 0]
+        # waves of workgroups past a walked grid stamp only their entry (they
+        # exit at once); they are counted, not charted
+        exited = int((t[:, 1] == 0).sum())
+        t = t[t[:, 1] != 0]
         spans.append(float((t[:, 9].max() - t[:, 0].min()) / 100.0))
     base = t[:, 0].min()
     us = lambda x: (x - base) / 100.0     # 100 MHz clock -> us
@@ -610,7 +614,8 @@ def timeline(args) -> int:
     flags = spa.decode_default_flags(case.batch, case.num_kv_heads, case.num_splits, case.kv_dtype,
                                      case.max_seq_pages)
     rec = {"timeline": case.name, "library": os.path.basename(spa.LIB_PATH),
-           "default_flags": int(flags), "waves": int(t.shape[0]), "calls": len(spans),
+           "default_flags": int(flags), "waves": int(t.shape[0]),
+           "waves_exited_at_once": exited, "calls": len(spans),
            "span_us": [round(x, 2) for x in spans],
            "wave_start_us_pct": [round(float(x), 2) for x in np.percentile(st, [0, 50, 90, 100])],
            "wave_end_us_pct": [round(float(x), 2) for x in np.percentile(en, [0, 50, 90, 100])],

@@ -277,7 +277,9 @@ spa_status spa_paged_decode_attention_noalloc(
  * for up to 8 page-split or 4 head-grouped splits); page_table_stride is
  * checked.  Within the plan,
  * the splits a bf16 head-grouped workgroup walks also depend on
- * page_table_stride and the current device's compute units.  0 for sizes
+ * page_table_stride, the current device's compute units and, per call, on
+ * seq_lens (a walk is taken only when the longest request has at most 6/5
+ * of the mean number of pages).  0 for sizes
  * spa_paged_decode_attention would reject as invalid or unsupported.
  */
 uint32_t spa_decode_default_flags(int32_t batch, int32_t num_kv_heads, int32_t num_splits,

@@ -259,18 +259,34 @@ void decode_kernel(DecodeParams p,
     // XCDs in serpentine order (ragged int8 batch: 71.5 -> 64.7 us against
     // round robin).  Otherwise the S splits of a group share an XCD.
     const int S = p.splits;
-    // A head-grouped bf16 workgroup walks `walk` consecutive splits (S a
+    // Lane i holds request i's length (the walk choice and, for batches of
+    // up to 64, the request ranking below read it).
+    const int Li = lane < p.batch ? seq_lens[lane] : INT32_MIN;
+    // A head-grouped bf16 workgroup may walk `walk` consecutive splits (S a
     // multiple of it), one page pipeline across the split boundaries, the
     // states of all but its last split kept in LDS until the walk ends: grids
     // larger than the GPU's resident workgroups then run in one round, and
     // the later splits skip the workgroup start (request ranking, page-id
     // and first-page latency).  Each split's arithmetic is unchanged.  With
     // the fused merge a group's S splits arrive as its S / walk workgroups.
-    const int walk = (HG && !QUANT && p.split_walk > 1) ? p.split_walk : 1;
+    // The walk is taken only for a batch whose requests have about the same
+    // number of pages (pages_balanced); in a ragged batch the longest
+    // requests' walks trail the rest (batch 32, 16 splits, graph replay,
+    // walking 8 against one split per workgroup: lengths U[1, 8K] 142.5 /
+    // 105.0 us, U[2K, 8K] 148.2 / 119.8, U[6K, 8K] 161.1 / 168.7, all 8K
+    // 175.7 / 186.0).  The grid has a workgroup per split; when the batch
+    // walks, those past the walked grid exit at once.
+    int walk = 1;
+    if constexpr (HG && !QUANT) {
+        if (p.split_walk > 1 &&
+            pages_balanced(seq_lens, p.batch, Li, p.pt_stride * P, P, lane))
+            walk = p.split_walk;
+    }
     const int SG = S / walk;                        // split groups per kv group
     const int kv_per_grp = HG ? NW : 1;             // kv heads per workgroup
     const int grp_per_b = p.hkv / kv_per_grp;
     const int ngroups = p.batch * grp_per_b;
+    if ((int64_t)blockIdx.x >= (int64_t)ngroups * SG) return;
     int grp, j;
     {
         const int bid = blockIdx.x;
@@ -306,7 +322,6 @@ void decode_kernel(DecodeParams p,
     } else if (p.batch <= 64) {
         // (equal lengths skip the ranking: rank r is request r; batch 32 /
         // 8K producer 162.2 -> 161.0 us bf16, 95.9 -> 94.7 us fp8)
-        const int Li = lane < p.batch ? seq_lens[lane] : INT32_MIN;
         b = r;
         if (__ballot(lane < p.batch && Li != __builtin_amdgcn_readfirstlane(Li)) != 0) {
             int rank = 0;
@@ -1263,7 +1278,9 @@ hipError_t launch_nw(const DecodeParams &p_in, bool fused, hipStream_t stream) {
             p.split_walk /= 2;
     }
     const int kv_per_grp = HG ? NW : 1;
-    const unsigned grid = (unsigned)(p.batch * (p.hkv / kv_per_grp) * (p.splits / p.split_walk));
+    // a workgroup per split: the kernel decides whether the batch walks
+    // (workgroups past the walked grid then exit at once)
+    const unsigned grid = (unsigned)(p.batch * (p.hkv / kv_per_grp) * p.splits);
     // LDS stash for the states of all but the last split of a walk
     const size_t stash_bytes = (size_t)NW * (p.split_walk - 1) * kStashFloats * sizeof(float);
     if (fused)
@@ -1296,7 +1313,8 @@ size_t max_lds_per_block() {
     return (size_t)device_attr<hipDeviceAttributeMaxSharedMemoryPerBlock>(65536);
 }
 
-// Splits one bf16 head-grouped workgroup walks, from a
+// Splits one bf16 head-grouped workgroup walks when the batch's requests
+// have about the same number of pages (the kernel checks that), from a
 // sweep over batch 8-32 x context 1K-8K x 4/8/16 splits: fewer, longer page
 // streams read faster.  Walks first cut the grid to one round of resident
 // workgroups (4 per CU); splits of at least 4 pages then walk on down to one
@@ -1304,7 +1322,8 @@ size_t max_lds_per_block() {
 // workgroup, 168 us walking 8); shorter splits stop at one round, their
 // boundaries costing more than the longer streams save.  1-byte codes walk
 // one split: their waves move half the bytes per page and lose with fewer
-// of them.
+// of them (a ragged fp8 batch 21% slower walking 4; equal lengths at most
+// 4% faster).
 constexpr int kMaxSplitWalk = 8;
 constexpr int kLongSplitPages = 4;
 int split_walk_for(const DecodeParams &p, bool quant, int nw) {

@@ -49,6 +49,7 @@ struct DecodeParams {
     const int32_t *seq_lens;   // [B]
     int32_t batch, hq, hkv, splits;
     int32_t split_walk;        // head-grouped bf16: splits per workgroup (divides splits)
+                               // when the batch's page counts are balanced, else 1
     int32_t num_pages;         // pool size: page ids outside [0, num_pages) load nothing
     float qk_scale_log2;       // scale * log2(e)
     float *part_acc;           // [B, Hq, S, D]

@@ -122,6 +122,30 @@ __device__ __forceinline__ float max_xor32(float x) {
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Whether the requests of a batch have about the same number of pages: the
+// longest at most 6/5 of the mean.  A split walk gives a workgroup the pages
+// of several splits of one request, so it pays only for such a batch; in a
+// ragged one the longest requests' walks trail the rest.  Li is request
+// `lane`'s length (ignored where lane >= batch); lanes load the requests past
+// the first 64.  Lengths are cut to [0, max_len]; page counts are summed as
+// floats (exact while the batch holds under 2^24 pages).  Whole wave active;
+// the result is the same in every lane.
+__device__ __forceinline__ bool pages_balanced(const int32_t *__restrict__ seq_lens, int batch,
+                                               int Li, int64_t max_len, int page, int lane) {
+    float tot = 0.f, mx = 0.f;
+    auto add = [&](int len) {
+        const int64_t l = min((int64_t)max(len, 0), max_len);
+        const float pg = (float)((l + page - 1) / page);
+        tot += pg;
+        mx = fmaxf(mx, pg);
+    };
+    if (lane < batch) add(Li);
+    for (int i = lane + 64; i < batch; i += 64) add(seq_lens[i]);
+    tot = add_xor32(add_xor16(row_sum16(tot)));
+    mx = max_xor32(max_xor16(row_max16(mx)));
+    return __builtin_amdgcn_readfirstlane(5.f * mx * (float)batch <= 6.f * tot) != 0;
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     bf16x2_t v;
     v[0] = (__bf16)lo;   // round to nearest even

@@ -88,18 +88,30 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
     // allows.  Both placements need a chunk size that is a multiple of 8, so
     // the XCD of a block id is that of its offset in the chunk.
     const int S = p.splits;
+    // Lane i holds request i's length (the walk choice and, for batches of
+    // up to 64, the request ranking below read it).
+    const int Li = lane < p.batch ? seq_lens[lane] : INT32_MIN;
     // bf16: a workgroup may walk `walk` consecutive splits (S a multiple of
     // it) with one page pipeline, as the one-token decode does: the states
     // of all but the last wait in dynamic LDS until the workgroup ends, each
-    // split's arithmetic unchanged.
-    const int walk = (!QUANT && p.split_walk > 1) ? p.split_walk : 1;
+    // split's arithmetic unchanged.  As there, only a batch whose requests
+    // have about the same number of pages walks; the grid has a workgroup
+    // per split and chunk, and when the batch walks, those past the walked
+    // part of each chunk exit at once.
+    int walk = 1;
+    if constexpr (!QUANT) {
+        if (p.split_walk > 1 &&
+            pages_balanced(seq_lens, p.batch, Li, p.pt_stride * P, P, lane))
+            walk = p.split_walk;
+    }
     const int SG = S / walk;
     const int grp_per_b = p.hkv / NW;
     const int ngroups = p.batch * grp_per_b;
-    const int chunk = blockIdx.x / (ngroups * SG);
+    const int chunk = blockIdx.x / (ngroups * S);
     int grp, j;
     {
-        const int bid = blockIdx.x - chunk * ngroups * SG;
+        const int bid = blockIdx.x - chunk * ngroups * S;
+        if (bid >= ngroups * SG) return;
         const int xcd = bid & 7, slot = bid >> 3;
         if (QUANT && (p.batch & 7) == 0) {
             j = slot % SG;
@@ -124,8 +136,8 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
     // requests' workgroups are dispatched first and the serpentine deal
     // above gives each XCD about the same number of pages.  Batches of more
     // than 64 requests keep their natural order.
-    // (Lane i loads request i's length and query-row bounds together, so the
-    // ranking adds no load to the chain, and equal lengths skip it: ragged
+    // (Lane i also loads request i's query-row bounds, so the ranking adds
+    // no load to the chain, and equal lengths skip it: ragged
     // int8 batch, 4 query tokens 81.1 -> 75.9 us per call; batch 32 / 8K
     // unchanged.)
     const int r = grp / grp_per_b;
@@ -133,7 +145,6 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
     int b = r, L, q0, q1;
     if (p.batch > 1 && p.batch <= 64) {
         const bool in = lane < p.batch;
-        const int Li = in ? seq_lens[lane] : INT32_MIN;
         const int Qa = in ? cu_q[lane] : 0, Qb = in ? cu_q[lane + 1] : 0;
         const int L0 = __builtin_amdgcn_readfirstlane(Li);
         if (__ballot(in && Li != L0) != 0) {
@@ -596,8 +607,9 @@ hipError_t launch_verify_kv(const DecodeParams &p_in, hipStream_t stream) {
                static_lds + (size_t)NW * (p.split_walk - 1) * STASH * sizeof(float) > max_lds)
             p.split_walk /= 2;
     }
-    const unsigned grid = (unsigned)((int64_t)p.batch * (p.hkv / NW) *
-                                     (p.splits / p.split_walk) * p.q_chunks);
+    // a workgroup per split and chunk: the kernel decides whether the batch
+    // walks (workgroups past the walked grid then exit at once)
+    const unsigned grid = (unsigned)((int64_t)p.batch * (p.hkv / NW) * p.splits * p.q_chunks);
     const size_t stash_bytes = (size_t)NW * (p.split_walk - 1) * STASH * sizeof(float);
     hipLaunchKernelGGL((verify_kernel<KV, RB, NW>), dim3(grid), dim3(NW * 64),
                        (unsigned)stash_bytes, stream, p, p.page_table, p.seq_lens, p.cu_seqlens_q);

@@ -65,6 +65,24 @@ class DevCase:
                                           k_scales=self.ks, v_scales=self.vs, **kw)
 
 
+def walks_balanced(lens, page_size=64) -> bool:
+    """The producers' rule for taking a split walk, as include/spa.h states
+    it: the longest request has at most 6/5 of the mean number of pages.
+    Tests use it to build batches on either side of the rule."""
+    pages = (np.maximum(np.asarray(lens, dtype=np.int64), 0) + page_size - 1) // page_size
+    return 5 * int(pages.max()) * len(pages) <= 6 * int(pages.sum())
+
+
+def balanced_walk_lens(n, seed, hi=4096):
+    """n lengths balanced enough for split walks, with the cases a walk must
+    get right among them: an empty and a one-token request, exact page
+    multiples and splits past the context inside a walk."""
+    lens = W._gen(n, seed).integers(hi - 300, hi + 1, size=n)
+    lens[:8] = [0, 1, 63, 64, 65, hi, hi - 1, 129]
+    assert walks_balanced(lens)
+    return lens
+
+
 def compare_attention(out_dev, lse_dev, o_ref, l_ref, rows=None, label=""):
     """Max-abs errors of the bf16 output and fp32 LSE against fp64 oracle
     values; asserts the stated tolerances.  ``rows`` restricts to a subset

@@ -9,8 +9,8 @@ import torch
 import oracle
 import split_paged_attention_amd as spa
 import workloads as W
-from tests.gpu_util import (DevCase, bf16_dev, bits_host, compare_attention, config_case,
-                            counters_view, COUNTER_REGION_BYTES)
+from tests.gpu_util import (DevCase, balanced_walk_lens, bf16_dev, bits_host, compare_attention,
+                            config_case, counters_view, walks_balanced, COUNTER_REGION_BYTES)
 
 pytestmark = pytest.mark.gpu
 
@@ -373,9 +373,7 @@ def test_full_step_config5_metadata_then_attention():
 
 
 def _walk_case():
-    lens = W._gen(64, 13).integers(1, 4097, size=64).tolist()
-    lens[:2] = [0, 4096]
-    return small_case(lens, kv="bf16", S=16, seed=64)
+    return small_case(balanced_walk_lens(64, 13).tolist(), kv="bf16", S=16, seed=64)
 
 
 def _int8_hg_case():
@@ -428,6 +426,59 @@ def test_hip_graph_replay_matches_eager(make, kw):
     assert int(counters_view(ws).abs().sum()) == 0
 
 
+@pytest.mark.parametrize("merge", ["fused", "separate"])
+def test_graph_replay_follows_walk_choice(merge):
+    """One captured bf16 head-grouped call, replayed while the lengths
+    alternate in place between a batch balanced enough to walk and a ragged
+    one: the kernel chooses per replay, and every replay equals an eager
+    call on the same lengths, bit for bit (the fused merge's arrival
+    counters, counted per walk or per split, end at zero)."""
+    bal = balanced_walk_lens(64, 21)
+    rag = bal.copy()
+    rag[8:40] = 1
+    assert not walks_balanced(rag)
+    c = small_case(bal.tolist(), kv="bf16", S=16, seed=121)
+    print(f"[case] graph replay, walk chosen per replay, {merge} merge", flush=True)
+    d = DevCase(c)
+    B, Hq, D, S = c.batch, c.num_q_heads, c.head_dim, c.num_splits
+    ws = spa.new_workspace(B, Hq, c.num_kv_heads, D, S)
+    out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    sl = d.seq_lens
+    cases = [("balanced", torch.tensor(bal, dtype=torch.int32)),
+             ("ragged", torch.tensor(rag, dtype=torch.int32))]
+
+    def call():
+        spa.paged_decode_attention(d.q, d.k, d.v, d.page_list, sl, S, float(c.scale),
+                                   kv_dtype="bf16", workspace=ws, out=out, lse=lse,
+                                   producer="head_grouped", merge=merge)
+
+    eager = {}
+    for name, host in cases:
+        sl.copy_(host)
+        call()
+        torch.cuda.synchronize()
+        eager[name] = (out.clone(), lse.clone())
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for i in range(6):
+        name, host = cases[i % 2]
+        sl.copy_(host)
+        out.zero_(); lse.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager[name][0].view(torch.int16)), (i, name)
+        assert torch.equal(lse, eager[name][1]), (i, name)
+    assert int(counters_view(ws).abs().sum()) == 0
+
+
 # ---------------------------------------------------------------- other batch and head shapes
 
 @pytest.mark.parametrize("kv", ["bf16", "int8", "fp8"])
@@ -446,20 +497,20 @@ def test_large_ragged_batches(batch, producer, kv):
 
 
 @pytest.mark.parametrize("S", [16, 8])
-def test_split_walk_ragged(S):
+def test_split_walk(S):
     """bf16 head-grouped grids large enough that a workgroup walks several
     consecutive splits (states of all but the last kept in LDS until the
-    workgroup ends): ragged lengths with empty requests, exact page
-    multiples and splits past the context inside a walk.  Checked against
-    the oracle; the fused launch (which walks too, a group's splits arriving
-    as its walks) bit-exactly against the separate one; and four of the
-    requests alone (a grid too small to walk) bit-exactly against their rows
-    of the walked call, since a walk changes no split's arithmetic."""
-    rng = W._gen(64, 7)
-    lens = rng.integers(1, 4097, size=64)
-    lens[:8] = [0, 1, 63, 64, 65, 4096, 4095, 129]
+    workgroup ends), on a batch balanced enough to walk: empty and one-token
+    requests, exact page multiples and splits past the context inside a
+    walk.  Checked against the oracle; the fused launch (which walks too, a
+    group's splits arriving as its walks) bit-exactly against the separate
+    one.  A walk changes no split's arithmetic, so these rows are bit-equal
+    to the same requests in calls that do not walk: a batch made ragged by
+    cutting other requests to one token, and four requests alone (a grid
+    too small to walk)."""
+    lens = balanced_walk_lens(64, 7)
     c = small_case(lens.tolist(), kv="bf16", S=S, seed=64 + S)
-    print(f"[case] split walk S={S} batch 64 ragged", flush=True)
+    print(f"[case] split walk S={S} batch 64 balanced", flush=True)
     d = DevCase(c)
     o_ref, l_ref = oracle.case_attention(c)
     o1, l1 = d.attention(producer="head_grouped", merge="separate")
@@ -467,6 +518,17 @@ def test_split_walk_ragged(S):
     o2, l2 = d.attention(producer="head_grouped", merge="fused")
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+    ragged = lens.copy()
+    ragged[8:40] = 1
+    assert not walks_balanced(ragged)
+    sl = torch.tensor(ragged, dtype=torch.int32, device="cuda")
+    keep = list(range(8)) + list(range(40, 64))
+    for merge in ("separate", "fused"):
+        o3, l3 = spa.paged_decode_attention(d.q, d.k, d.v, d.page_list, sl, S, float(c.scale),
+                                            kv_dtype="bf16", producer="head_grouped", merge=merge)
+        torch.cuda.synchronize()
+        assert torch.equal(o3[keep].view(torch.int16), o1[keep].view(torch.int16)), merge
+        assert torch.equal(l3[keep], l1[keep]), merge
     # lengths 65, 4096, 4095, 129: 4 x 4 kv-head blocks x S workgroups (at
     # most 256) is one per CU at most, a grid no walk shortens
     rows = slice(4, 8)
@@ -477,6 +539,24 @@ def test_split_walk_ragged(S):
     torch.cuda.synchronize()
     assert torch.equal(o3.view(torch.int16), o1[rows].view(torch.int16))
     assert torch.equal(l3, l1[rows])
+
+
+@pytest.mark.parametrize("S", [16, 8])
+def test_ragged_batch_does_not_walk(S):
+    """A ragged bf16 batch of the same grid size (the longest request far
+    above the mean) takes one split per workgroup: checked against the
+    oracle for both merges."""
+    rng = W._gen(64, 8)
+    lens = rng.integers(1, 4097, size=64)
+    lens[:4] = [0, 4096, 64, 65]
+    assert not walks_balanced(lens)
+    c = small_case(lens.tolist(), kv="bf16", S=S, seed=90 + S)
+    print(f"[case] ragged no-walk S={S} batch 64", flush=True)
+    d = DevCase(c)
+    o_ref, l_ref = oracle.case_attention(c)
+    for merge in ("separate", "fused"):
+        out, lse = d.attention(producer="head_grouped", merge=merge)
+        compare_attention(out, lse, o_ref, l_ref, label=f"ragged S={S} {merge}")
 
 
 @pytest.mark.parametrize("Hkv", [1, 2, 6, 16])

@@ -8,7 +8,7 @@ import torch
 import oracle
 import split_paged_attention_amd as spa
 import workloads as W
-from tests.gpu_util import LSE_ATOL, OUT_ATOL, DevCase, config_case
+from tests.gpu_util import LSE_ATOL, OUT_ATOL, DevCase, balanced_walk_lens, config_case
 
 pytestmark = pytest.mark.gpu
 
@@ -84,10 +84,8 @@ def test_partials_then_merge_equal_one_call(kv, producer):
 
 def test_partials_split_walk_bit_identical():
     """A bf16 head-grouped grid large enough for walks of several splits per
-    workgroup (64 ragged requests, 16 splits)."""
-    rng = W._gen(65, 7)
-    lens = rng.integers(1, 4097, size=64)
-    lens[:6] = [0, 1, 64, 65, 4096, 129]
+    workgroup (64 requests balanced enough to walk, 16 splits)."""
+    lens = balanced_walk_lens(64, 65)
     c = small_case(lens.tolist(), kv="bf16", S=16, seed=66)
     assert spa.decode_default_flags(64, 8, 16, "bf16", c.max_seq_pages) == (
         spa.SPA_DECODE_HEAD_GROUPED | spa.SPA_DECODE_SEPARATE_MERGE)

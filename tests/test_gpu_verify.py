@@ -8,7 +8,8 @@ import torch
 import oracle
 import split_paged_attention_amd as spa
 import workloads as W
-from tests.gpu_util import DevCase, bf16_dev, compare_attention, config_case
+from tests.gpu_util import (DevCase, balanced_walk_lens, bf16_dev, compare_attention, config_case,
+                            walks_balanced)
 
 pytestmark = pytest.mark.gpu
 
@@ -213,23 +214,39 @@ def test_verify_large_batches(batch, kv):
 
 
 @pytest.mark.parametrize("S", [16, 8])
-def test_verify_split_walk_ragged(S):
+def test_verify_split_walk(S):
     """bf16 grids large enough that a workgroup walks several consecutive
     splits (states of all but the last held in LDS until the workgroup
-    ends): 64 ragged requests with 0-4 query rows, an empty context, exact
-    page multiples and splits past the context inside a walk."""
+    ends), on 64 requests balanced enough to walk, with 0-4 query rows, an
+    empty context, exact page multiples and splits past the context inside
+    a walk; then the same queries over a ragged batch (other requests cut
+    short), which takes one split per workgroup: the rows of the requests
+    both calls share are bit-equal."""
     rng = W._gen(64, 11)
-    lens = rng.integers(4, 4097, size=64)
-    lens[:6] = [4, 64, 65, 4096, 4095, 129]
+    lens = balanced_walk_lens(64, 12)
+    lens[0] = 4            # (an empty context would leave no room for query rows)
     qlens = rng.integers(0, 5, size=64)
     qlens[:4] = [4, 0, 1, 4]
     qlens = np.minimum(qlens, lens).tolist()
     c = small_case(lens.tolist(), kv="bf16", S=S, seed=80 + S)
     q_rows, cu = W.verify_queries(c, qlens)
-    print(f"[case] verify split walk S={S} batch 64 ragged", flush=True)
+    print(f"[case] verify split walk S={S} batch 64 balanced", flush=True)
     out, lse = run_verify(c, q_rows, cu)
     o_ref, l_ref = oracle_verify(c, q_rows, cu)
     compare_attention(out, lse, o_ref, l_ref, label=f"verify walk S={S}")
+    ragged = lens.copy()
+    ragged[8:40] = np.maximum(np.asarray(qlens[8:40]), 1)
+    assert not walks_balanced(ragged)
+    d = DevCase(c)
+    out2, lse2 = spa.paged_verify_attention(
+        bf16_dev(q_rows), d.k, d.v, d.page_list, torch.tensor(ragged, dtype=torch.int32).cuda(),
+        torch.from_numpy(cu).cuda(), S, float(c.scale), max_q_len=4, kv_dtype="bf16")
+    torch.cuda.synchronize()
+    cu_h = np.asarray(cu)
+    keep = np.concatenate([np.arange(cu_h[b], cu_h[b + 1]) for b in list(range(8)) + list(range(40, 64))])
+    keep = torch.from_numpy(keep).cuda()
+    assert torch.equal(out2[keep].view(torch.int16), out[keep].view(torch.int16))
+    assert torch.equal(lse2[keep], lse[keep])
 
 
 def test_verify_graph_replay_matches_eager():
