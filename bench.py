@@ -467,7 +467,9 @@ def ablation(args) -> int:
 
 def policy_sweep(args) -> int:
     """Producer x merge choice across decode shapes (batch 1-32, context
-    1K-8K, 4/8/16 splits; 32 query / 8 KV heads, head_dim 128, 64-token pages
+    1K-8K, 4/8/16 splits, equal lengths; then ragged batches of 8-32
+    requests with lengths U[1, 2K or 8K] and 8/16 splits; 32 query / 8 KV
+    heads, head_dim 128, 64-token pages
     drawn at random from a 4096-page pool): microseconds per call from HIP
     graphs of R calls, for both producers with both merges and for the
     library's default.  The R calls of a graph read disjoint page sets that
@@ -476,6 +478,7 @@ def policy_sweep(args) -> int:
     pass.  One JSON line; a progress line per shape on stderr."""
     import itertools
 
+    import numpy as np
     import torch
 
     import split_paged_attention_amd as spa
@@ -498,13 +501,21 @@ def policy_sweep(args) -> int:
     variants = [("page_split", "fused"), ("page_split", "separate"),
                 ("head_grouped", "fused"), ("head_grouped", "separate"), (None, None)]
     rows = []
-    for B, L, S in itertools.product([1, 2, 4, 8, 16, 32], [1024, 2048, 4096, 8192], [4, 8, 16]):
+    # equal lengths, then ragged batches (lengths U[1, L], seeded per shape)
+    shapes = [(B, L, S, False) for B, L, S in
+              itertools.product([1, 2, 4, 8, 16, 32], [1024, 2048, 4096, 8192], [4, 8, 16])]
+    shapes += [(B, L, S, True) for B, L, S in itertools.product([8, 16, 32], [2048, 8192], [8, 16])]
+    for B, L, S, ragged in shapes:
         npg = B * (L // P)
         R = max(1, pool // npg)
         q = torch.randn(B, Hq, D, device=dev, generator=g).to(torch.bfloat16)
         pts = torch.randperm(pool, device=dev, generator=g)[:R * npg].to(torch.int32)
         pts = pts.view(R, B, L // P).contiguous()
-        sl = torch.full((B,), L, dtype=torch.int32, device=dev)
+        if ragged:
+            lens = np.random.default_rng(1000 * B + S).integers(1, L + 1, size=B)
+            sl = torch.tensor(lens, dtype=torch.int32, device=dev)
+        else:
+            sl = torch.full((B,), L, dtype=torch.int32, device=dev)
         ws = spa.new_workspace(B, Hq, Hkv, D, S, device=dev)
         out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
         lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
@@ -517,7 +528,8 @@ def policy_sweep(args) -> int:
 
             us.append(time_graph(capture(call, R), R, max(2, 40 // R), warm_ms=10.0)[0])
         best = min(range(4), key=lambda i: us[i])
-        rows.append({"batch": B, "context": L, "splits": S, "waves": B * Hkv * S, "calls": R,
+        rows.append({"batch": B, "context": L, "ragged": ragged, "splits": S,
+                     "waves": B * Hkv * S, "calls": R,
                      "page_split_fused_us": round(us[0], 2),
                      "page_split_separate_us": round(us[1], 2),
                      "head_grouped_fused_us": round(us[2], 2),
