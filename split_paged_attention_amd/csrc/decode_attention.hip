@@ -33,12 +33,18 @@
 //   * fp8 (e4m3) KV: the same f16 matrix cores and f16 dot products; the
 //     hardware converter turns codes into exact f16 values (keys at scale 1,
 //     values at scale 1/256, the 256 going into the value scale);
-//   * P.V on the vector ALUs with v_dot2_f32_bf16: lane (r, c) owns dims
-//     8c..8c+7 of tokens 4i + r (so one V load instruction reads 4 whole
-//     256-byte rows), pairs tokens t and t + 16 in one dot2, and gets the
-//     packed bf16 probabilities of its tokens from a 512-byte per-wave LDS
-//     buffer.  P.V with K = tokens would need V transposed for the MFMA B
-//     operand; the VALU form reads V in its stored order instead.
+//   * P.V, head-grouped bf16 and int8: on the matrix cores, the page's
+//     values staged token-major in LDS (bf16: in the key tile, which QK^T
+//     has consumed) and turned into B operands by transposed LDS reads, the
+//     probabilities token-major beside them as A operands.  bf16
+//     probabilities go in two bf16 terms, hi + lo: each term's products with
+//     bf16 values are exact in fp32, so P.V carries them to 2^-17.
+//   * P.V, page-split producer and head-grouped e4m3: on the vector ALUs,
+//     v_dot2 over pairs of tokens: lane (r, c) owns dims 8c..8c+7 of tokens
+//     4i + r (so one V load instruction reads 4 whole 256-byte rows), pairs
+//     tokens t and t + 16 in one dot2, and gets the packed probabilities of
+//     its tokens from a 512-byte per-wave LDS buffer (bf16: the hi and lo
+//     terms, two dot2 each).
 // The path is HBM-bound (about 4 flop per KV byte for bf16), so the design
 // goal is bytes in flight and a single pass over K and V.
 #include "internal.h"
@@ -269,17 +275,20 @@ void decode_kernel(DecodeParams p,
     // the later splits skip the workgroup start (request ranking, page-id
     // and first-page latency).  Each split's arithmetic is unchanged.  With
     // the fused merge a group's S splits arrive as its S / walk workgroups.
-    // The walk is taken only for a batch whose requests have about the same
-    // number of pages (pages_balanced); in a ragged batch the longest
-    // requests' walks trail the rest (batch 32, 16 splits, graph replay,
-    // walking 8 against one split per workgroup: lengths U[1, 8K] 142.5 /
-    // 105.0 us, U[2K, 8K] 148.2 / 119.8, U[6K, 8K] 161.1 / 168.7, all 8K
-    // 175.7 / 186.0).  The grid has a workgroup per split; when the batch
-    // walks, those past the walked grid exit at once.
+    // When the walked grid is about one round of resident workgroups, the
+    // walk is taken only for a batch whose requests have about the same
+    // number of pages (pages_balanced): in a ragged batch the longest
+    // requests' walks would trail the rest (batch 32, 16 splits, graph
+    // replay, walking 8 against one split per workgroup: lengths U[1, 8K]
+    // 142.5 / 105.0 us, U[2K, 8K] 148.2 / 119.8, U[6K, 8K] 161.1 / 168.7,
+    // all 8K 175.7 / 186.0).  The grid then has a workgroup per split, and
+    // when the batch walks, those past the walked grid exit at once.  A
+    // walked grid of several rounds always walks (walk_checked = 0, grid
+    // cut): the dispatcher evens out the workgroups' lengths.
     int walk = 1;
     if constexpr (HG && !QUANT) {
         if (p.split_walk > 1 &&
-            pages_balanced(seq_lens, p.batch, Li, p.pt_stride * P, P, lane))
+            (!p.walk_checked || pages_balanced(seq_lens, p.batch, Li, p.pt_stride * P, P, lane)))
             walk = p.split_walk;
     }
     const int SG = S / walk;                        // split groups per kv group
@@ -413,9 +422,13 @@ void decode_kernel(DecodeParams p,
         for (int d = 0; d < 8; ++d) acc[h][d] = 0.f;
     }
 
-    // Head-grouped int8 codes run P.V on the matrix cores (see below).
+    // Head-grouped int8 codes and bf16 run P.V on the matrix cores (see
+    // below); e4m3 codes and the page-split producer on the vector ALU.
     constexpr bool MXPV = I8 && HG;
-    __shared__ uint32_t pbuf[MXPV ? 1 : NW][8][4][4];   // [wave][pair u][phase r][head]
+    constexpr bool BFPV = !QUANT && HG;
+    constexpr bool VPV = !MXPV && !BFPV;                 // vector-ALU P.V
+    __shared__ uint32_t pbuf[VPV ? NW : 1][8][4][4];      // [wave][pair u][phase r][head]
+    __shared__ uint32_t pbuf_lo[VPV && !QUANT ? NW : 1][8][4][4];   // bf16: low terms
     __shared__ float sm_m[NW][4], sm_l[NW][4];
     __shared__ float sm_acc[HG ? 1 : NW][4][HG ? 1 : D];   // page split: waves' states
     // Head-grouped: the page's K rows, staged per wave: loaded as whole rows
@@ -433,13 +446,20 @@ void decode_kernel(DecodeParams p,
     constexpr bool KDMA = QUANT && KSTAGE;
     constexpr int KROWB = KDMA ? D : D * (QUANT ? 1 : 2) + 16;   // bytes per staged row
     __shared__ __attribute__((aligned(16))) uint8_t ktile[KSTAGE ? NW : 1][KSTAGE ? P : 1][KROWB];
-    // Matrix-core P.V, per wave: the page's probabilities P' (f16, value
-    // scale folded in) token-major, 4 heads per 8-byte row; and half a page
-    // of value codes (32 token rows of 128 bytes, padded by 16 so that the 8
-    // rows of a transposed read fall in distinct banks).  Transposed reads
-    // turn both into operands whose contraction runs over tokens.
+    // Matrix-core P.V, per wave: the page's probabilities token-major, 4
+    // heads per 8-byte row (int8: P' in f16, value scale folded in; bf16:
+    // hi and lo terms); and the values (int8: half a page of codes, 32 token
+    // rows of 128 bytes, padded by 16 so that the 8 rows of a transposed read
+    // fall in distinct banks; bf16: the whole page in the key tile).
+    // Transposed reads turn both into operands whose contraction runs over
+    // tokens.
     constexpr int VROWB = D + 16;
-    __shared__ __attribute__((aligned(16))) uint16_t ptile[MXPV ? NW : 1][MXPV ? P : 1][4];
+    __shared__ __attribute__((aligned(16))) uint16_t ptile[MXPV || BFPV ? NW : 1][MXPV || BFPV ? P : 1][4];
+    // bf16: the probabilities' low terms (p = hi + lo to 16 significant bits;
+    // both terms' products with bf16 values are exact in fp32, so P.V
+    // carries p to 2^-17 instead of the 2^-9 of one bf16 term, which can
+    // cost 0.007 on an output of a few tokens)
+    __shared__ __attribute__((aligned(16))) uint16_t ptile_lo[BFPV ? NW : 1][BFPV ? P : 1][4];
     __shared__ __attribute__((aligned(16))) uint8_t vtile[MXPV ? NW : 1][MXPV ? P / 2 : 1][MXPV ? VROWB : 1];
     __shared__ int sm_last;
 
@@ -610,8 +630,10 @@ void decode_kernel(DecodeParams p,
 
     // Matrix-core P.V: this wave's split jw is complete; write its
     // partial state from the matrix-core layout (lane (j, g) holds head g at
-    // dims 16T + j) and start the next split.
-    auto finish_split_mx = [&](int jw) {
+    // dims 16T + j) and start the next split.  A bf16 split before its
+    // walk's last goes to the LDS stash instead, in the [head][dim] layout
+    // the stash write-out reads.
+    auto finish_split_mx = [&](int jw, bool to_stash) {
         if constexpr (I8) {
             // remove the 1152 bias of the value codes
 #pragma unroll
@@ -619,11 +641,13 @@ void decode_kernel(DecodeParams p,
 #pragma unroll
                 for (int h = 0; h < 4; ++h) oacc[t][h] = __builtin_fmaf(-kI8Bias, pacc[h], oacc[t][h]);
         }
-        float lsum[4];   // the lanes' sums over their own tokens, over the wave
+        // the sums over the tokens (int8: lane l holds token l's; bf16: lane
+        // (n, g) tokens 16t + n, every row of 16 lanes the same)
+        float lsum[4];
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
             float x = row_sum16(lpart[h]);
-            x = add_xor32(add_xor16(x));
+            if constexpr (I8) x = add_xor32(add_xor16(x));
             lsum[h] = x;
         }
         const int64_t idx0 = ((int64_t)b * p.hq + kvh * kGroup) * S + jw;
@@ -633,7 +657,19 @@ void decode_kernel(DecodeParams p,
 #pragma unroll
         for (int t = 0; t < 8; ++t)
             o[t] = pick4(oacc[t][0], oacc[t][1], oacc[t][2], oacc[t][3], g);
-        if constexpr (FUSED) {
+        if (to_stash) {
+            float *st = stash + (wave * (walk - 1) + nstash) * kStashFloats;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) st[g * D + 16 * t + jl] = o[t];
+            if (lane == 0) {
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    st[4 * D + h] = m[h];
+                    st[4 * D + 4 + h] = lsum[h];
+                }
+            }
+            ++nstash;
+        } else if constexpr (FUSED) {
             const auto r = __builtin_amdgcn_make_buffer_rsrc(p.part_acc + idx0 * D, (short)0,
                                                              (3 * S + 1) * D * 4, kBufferWord3);
 #pragma unroll
@@ -643,7 +679,7 @@ void decode_kernel(DecodeParams p,
 #pragma unroll
             for (int t = 0; t < 8; ++t) base[16 * t] = o[t];
         }
-        if (lane == 0) {
+        if (!to_stash && lane == 0) {
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
                 put(p.part_max + idx0 + (int64_t)h * S, m[h] == kNegInf ? kNegInf : m[h] * kLn2);
@@ -813,7 +849,7 @@ void decode_kernel(DecodeParams p,
             }
             vsc_tok = vsc_next;
             if (pg + 1 == split_end) {
-                finish_split_mx(jcur);
+                finish_split_mx(jcur, false);
                 ++jcur;
                 split_end = min(split_end + pps, pages);
             }
@@ -949,10 +985,71 @@ void decode_kernel(DecodeParams p,
             lpart[h] = __builtin_fmaf(lpart[h], alpha[h], rs);
         }
 
+        if constexpr (BFPV) {
+            // ---- this page's probabilities into the P tile, token-major,
+            // hi and lo terms; lane (n, g) writes token 16g + n (every row of
+            // 16 lanes holds all 64 tokens)
+            {
+                float a[4];
+#pragma unroll
+                for (int h = 0; h < 4; ++h) a[h] = pick4(pv[0][h], pv[1][h], pv[2][h], pv[3][h], g);
+                const uint2 hi = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+                *reinterpret_cast<uint2 *>(&ptile[wave][lane][0]) = hi;
+                *reinterpret_cast<uint2 *>(&ptile_lo[wave][lane][0]) =
+                    make_uint2(bf16x2_residual(a[0], a[1], hi.x), bf16x2_residual(a[2], a[3], hi.y));
+            }
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+#pragma unroll
+                for (int h = 0; h < 4; ++h) oacc[t][h] *= alpha[h];
+            // ---- this page's values into the key tile, whose rows QK^T has
+            // read (a wave's LDS operations complete in order), token-major
+            // like the keys; the registers then take the next page's values
+            uint8_t(*kt)[KROWB] = ktile[wave];
+            __asm__ volatile("" ::: "memory");
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                *reinterpret_cast<uint4 *>(&kt[4 * i + vr][16 * vc]) = vr16[i];
+            __asm__ volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            load_v_half(page_next, valid_next, 0);
+            load_v_half(page_next, valid_next, 1);
+            __builtin_amdgcn_sched_barrier(0);
+            // ---- O += P V on the matrix cores, 32 tokens per step.  A = P:
+            // lane (i, G) takes head i % 4 at tokens 8G .. 8G + 7 (two
+            // transposed reads of 4 token rows); B = V: lane (j, G) takes dim
+            // 16T + j at tokens 8G .. 8G + 7.  The low terms go first.
+            const uint16_t(*kt16)[KROWB / 2] = reinterpret_cast<const uint16_t(*)[KROWB / 2]>(kt);
+            const int tr_row = 8 * g + (n >> 2), tr_col = 4 * (n & 3);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const uint16_t *prh = &ptile[wave][32 * kb + 8 * g + (n >> 2)][0];
+                const uint16_t *prl = &ptile_lo[wave][32 * kb + 8 * g + (n >> 2)][0];
+                const bf16x8_t pah = join_bf16x8(lds_tr16_b64(prh), lds_tr16_b64(prh + 16));
+                const bf16x8_t pal = join_bf16x8(lds_tr16_b64(prl), lds_tr16_b64(prl + 16));
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const bf16x8_t vb =
+                        join_bf16x8(lds_tr16_b64(&kt16[32 * kb + tr_row][16 * t + tr_col]),
+                                    lds_tr16_b64(&kt16[32 * kb + tr_row + 4][16 * t + tr_col]));
+                    oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pal, vb, oacc[t], 0, 0, 0);
+                    oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pah, vb, oacc[t], 0, 0, 0);
+                }
+            }
+            // the next page's keys overwrite the tile only after these reads
+            __asm__ volatile("" ::: "memory");
+            if (pg + 1 == split_end) {
+                finish_split_mx(jcur, pg + 1 < pg1);
+                ++jcur;
+                split_end = min(split_end + pps, pages);
+            }
+            continue;
+        }
+
         // ---- probabilities for P.V: pair (token 32q + n, token 32q + 16 + n),
         // stored by row 0 of the wave as pbuf[pair u][phase r][h]
-        // with u = 4q + n/4, r = n % 4 (bf16, or f16 with the value scale
-        // folded in for 1-byte codes).
+        // with u = 4q + n/4, r = n % 4 (bf16 hi and lo terms, or f16 with the
+        // value scale folded in for 1-byte codes).
         {   // every row g holds the same values, so all lanes may store
 #pragma unroll
             for (int qq = 0; qq < 2; ++qq) {
@@ -971,10 +1068,14 @@ void decode_kernel(DecodeParams p,
                     w.z = pack_f16x2(a2, b2);
                     w.w = pack_f16x2(a3, b3);
                 } else {
+                    // two bf16 terms per probability, as on the matrix cores
                     w.x = pack_bf16x2(a0, b0);
                     w.y = pack_bf16x2(a1, b1);
                     w.z = pack_bf16x2(a2, b2);
                     w.w = pack_bf16x2(a3, b3);
+                    const uint4 wl = make_uint4(bf16x2_residual(a0, b0, w.x), bf16x2_residual(a1, b1, w.y),
+                                                bf16x2_residual(a2, b2, w.z), bf16x2_residual(a3, b3, w.w));
+                    *reinterpret_cast<uint4 *>(&pbuf_lo[wave][4 * qq + (n >> 2)][n & 3][0]) = wl;
                 }
                 *reinterpret_cast<uint4 *>(&pbuf[wave][4 * qq + (n >> 2)][n & 3][0]) = w;
             }
@@ -1002,6 +1103,8 @@ void decode_kernel(DecodeParams p,
             const int ib = ia + 4;                  // token 4*ia + r + 16
             const uint32_t ph[4] = {pk.x, pk.y, pk.z, pk.w};
             if constexpr (!QUANT) {
+                const uint4 pkl = *reinterpret_cast<const uint4 *>(&pbuf_lo[wave][u][vr][0]);
+                const uint32_t pl[4] = {pkl.x, pkl.y, pkl.z, pkl.w};
                 const uint32_t wa[4] = {vr16[ia].x, vr16[ia].y, vr16[ia].z, vr16[ia].w};
                 const uint32_t wb[4] = {vr16[ib].x, vr16[ib].y, vr16[ib].z, vr16[ib].w};
 #pragma unroll
@@ -1010,8 +1113,8 @@ void decode_kernel(DecodeParams p,
                     const uint32_t hi = __builtin_amdgcn_perm(wb[e], wa[e], 0x07060302u);
 #pragma unroll
                     for (int h = 0; h < 4; ++h) {
-                        acc[h][2 * e] = dot2(ph[h], lo, acc[h][2 * e]);
-                        acc[h][2 * e + 1] = dot2(ph[h], hi, acc[h][2 * e + 1]);
+                        acc[h][2 * e] = dot2(ph[h], lo, dot2(pl[h], lo, acc[h][2 * e]));
+                        acc[h][2 * e + 1] = dot2(ph[h], hi, dot2(pl[h], hi, acc[h][2 * e + 1]));
                     }
                 }
             } else {
@@ -1048,31 +1151,11 @@ void decode_kernel(DecodeParams p,
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (QUANT) vsc_tok = vsc_next * (I8 ? 1.f : kF8ValueScale);
         if constexpr (HG) {
+            // (the vector-ALU head-grouped producer serves e4m3 codes, which
+            // walk one split, so its split ends where the workgroup's does)
             if (pg + 1 == split_end) {
-                // split jcur complete: write its state (a split before the
-                // workgroup's last goes to the LDS stash, written out after
-                // the loop: stores between the page loads measured 5 us per
-                // split boundary), start the next one
+                // split jcur complete: write its state, start the next one
                 reduce_state();
-                if (pg + 1 < pg1) {
-                    float *st = stash + (wave * (walk - 1) + nstash) * kStashFloats;
-                    float v8[8];
-#pragma unroll
-                    for (int d = 0; d < 8; ++d)
-                        v8[d] = vr == 0 ? acc[0][d] : vr == 1 ? acc[1][d] : vr == 2 ? acc[2][d] : acc[3][d];
-                    *reinterpret_cast<float4 *>(st + vr * D + 8 * vc) =
-                        make_float4(v8[0], v8[1], v8[2], v8[3]);
-                    *reinterpret_cast<float4 *>(st + vr * D + 8 * vc + 4) =
-                        make_float4(v8[4], v8[5], v8[6], v8[7]);
-                    if (lane == 0) {
-#pragma unroll
-                        for (int h = 0; h < 4; ++h) {
-                            st[4 * D + h] = m[h];
-                            st[4 * D + 4 + h] = lpart[h];
-                        }
-                    }
-                    ++nstash;
-                } else
                 {
                     const int jw = jcur;
                     // One wave = one kv head: write its split state straight from
@@ -1278,9 +1361,11 @@ hipError_t launch_nw(const DecodeParams &p_in, bool fused, hipStream_t stream) {
             p.split_walk /= 2;
     }
     const int kv_per_grp = HG ? NW : 1;
-    // a workgroup per split: the kernel decides whether the batch walks
-    // (workgroups past the walked grid then exit at once)
-    const unsigned grid = (unsigned)(p.batch * (p.hkv / kv_per_grp) * p.splits);
+    const int64_t per_split = (int64_t)p.batch * (p.hkv / kv_per_grp) * p.splits;
+    p.walk_checked = walk_checked_for(per_split, p.split_walk);
+    // checked walks: a workgroup per split, the kernel deciding (those past
+    // the walked grid then exit at once)
+    const unsigned grid = (unsigned)(p.walk_checked ? per_split : per_split / p.split_walk);
     // LDS stash for the states of all but the last split of a walk
     const size_t stash_bytes = (size_t)NW * (p.split_walk - 1) * kStashFloats * sizeof(float);
     if (fused)
@@ -1326,6 +1411,16 @@ size_t max_lds_per_block() {
 // 4% faster).
 constexpr int kMaxSplitWalk = 8;
 constexpr int kLongSplitPages = 4;
+// A walked grid of at least kWalkRounds rounds of kWalkRoundWgsPerCu
+// workgroups per CU walks whatever the lengths (the dispatcher evens out
+// ragged workgroups over the rounds: batch 512, lengths U[1, 1K], 8 splits,
+// walking 8 262 us, one split per workgroup 311 us); a smaller one walks
+// only a balanced batch.
+constexpr int kWalkRounds = 2;
+constexpr int kWalkRoundWgsPerCu = 4;
+int walk_checked_for(int64_t split_wgs, int walk) {
+    return walk > 1 && split_wgs / walk < (int64_t)kWalkRounds * kWalkRoundWgsPerCu * cu_count();
+}
 int split_walk_for(const DecodeParams &p, bool quant, int nw) {
     if (quant) return 1;
     const int64_t wgs = (int64_t)p.batch * (p.hkv / nw) * p.splits;

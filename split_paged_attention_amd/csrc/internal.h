@@ -49,7 +49,8 @@ struct DecodeParams {
     const int32_t *seq_lens;   // [B]
     int32_t batch, hq, hkv, splits;
     int32_t split_walk;        // head-grouped bf16: splits per workgroup (divides splits)
-                               // when the batch's page counts are balanced, else 1
+    int32_t walk_checked;      // 1: walk only if the batch's page counts are balanced (grid
+                               // of a workgroup per split); 0: always (grid cut to match)
     int32_t num_pages;         // pool size: page ids outside [0, num_pages) load nothing
     float qk_scale_log2;       // scale * log2(e)
     float *part_acc;           // [B, Hq, S, D]
@@ -108,6 +109,9 @@ DecodeMode default_mode(int batch, int hkv, int splits, int kv_type);
 // Splits one head-grouped workgroup walks (bf16 only; 1 for 1-byte codes),
 // and the device's LDS limit per workgroup.
 int split_walk_for(const DecodeParams &p, bool quant, int nw);
+// 1 if a walk of `walk` splits over a grid of split_wgs workgroups (one per
+// split) is taken only for a batch with balanced page counts, 0 if always.
+int walk_checked_for(int64_t split_wgs, int walk);
 size_t max_lds_per_block();
 bool mode_supported(DecodeMode mode, int hkv);
 

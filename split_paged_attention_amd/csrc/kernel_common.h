@@ -152,6 +152,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     v[1] = (__bf16)hi;
     return __builtin_bit_cast(uint32_t, v);
 }
+// The low bf16 terms of (lo, hi) given their high terms `hi_terms` (a
+// pack_bf16x2 of the same pair): x - bf16(x) is exact in fp32 and rounds to
+// the next 8 significant bits.
+__device__ __forceinline__ uint32_t bf16x2_residual(float lo, float hi, uint32_t hi_terms) {
+    return pack_bf16x2(lo - __uint_as_float(hi_terms << 16),
+                       hi - __uint_as_float(hi_terms & 0xffff0000u));
+}
 __device__ __forceinline__ uint16_t to_bf16_bits(float x) {
     return __builtin_bit_cast(uint16_t, (__bf16)x);
 }

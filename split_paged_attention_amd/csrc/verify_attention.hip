@@ -94,23 +94,25 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
     // bf16: a workgroup may walk `walk` consecutive splits (S a multiple of
     // it) with one page pipeline, as the one-token decode does: the states
     // of all but the last wait in dynamic LDS until the workgroup ends, each
-    // split's arithmetic unchanged.  As there, only a batch whose requests
-    // have about the same number of pages walks; the grid has a workgroup
-    // per split and chunk, and when the batch walks, those past the walked
-    // part of each chunk exit at once.
+    // split's arithmetic unchanged.  As there, a walked grid of about one
+    // round walks only a batch whose requests have about the same number of
+    // pages (walk_checked): the grid then has a workgroup per split and
+    // chunk, and when the batch walks, those past the walked part of each
+    // chunk exit at once.
     int walk = 1;
     if constexpr (!QUANT) {
         if (p.split_walk > 1 &&
-            pages_balanced(seq_lens, p.batch, Li, p.pt_stride * P, P, lane))
+            (!p.walk_checked || pages_balanced(seq_lens, p.batch, Li, p.pt_stride * P, P, lane)))
             walk = p.split_walk;
     }
     const int SG = S / walk;
     const int grp_per_b = p.hkv / NW;
     const int ngroups = p.batch * grp_per_b;
-    const int chunk = blockIdx.x / (ngroups * S);
+    const int per_chunk = ngroups * (p.walk_checked ? S : SG);   // launched per chunk
+    const int chunk = blockIdx.x / per_chunk;
     int grp, j;
     {
-        const int bid = blockIdx.x - chunk * ngroups * S;
+        const int bid = blockIdx.x - chunk * per_chunk;
         if (bid >= ngroups * SG) return;
         const int xcd = bid & 7, slot = bid >> 3;
         if (QUANT && (p.batch & 7) == 0) {
@@ -285,8 +287,14 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
     constexpr int VROW = D + 16;
     __shared__ __attribute__((aligned(16))) uint16_t vbuf[NW][P / 2][VROW];
     __shared__ __attribute__((aligned(16))) uint16_t pbuf[NW][P][PW];
+    // bf16: the probabilities' low terms (p = hi + lo to 16 significant
+    // bits; both terms' products with bf16 values are exact in fp32, so P.V
+    // carries p to 2^-17 instead of the 2^-9 of one bf16 term, which can
+    // cost 0.007 on an output of a few tokens)
+    __shared__ __attribute__((aligned(16))) uint16_t pbuf_lo[QUANT ? 1 : NW][QUANT ? 1 : P][PW];
     uint16_t(*vt)[VROW] = vbuf[wave];
     uint16_t(*pt16)[PW] = pbuf[wave];
+    uint16_t(*ptl16)[PW] = pbuf_lo[QUANT ? 0 : wave];
     // Transposed-read addressing: lane 16G + 4e + qd supplies row 8G + e
     // (+ 4 for the second read), columns 4qd .. 4qd+3; lane 16G + i then
     // receives column i of rows 8G .. 8G+3 (8G+4 .. 8G+7): the MFMA operand
@@ -477,10 +485,13 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
             for (int rb = 0; rb < RB; ++rb) {
                 const float *a = pv[rb][t];
                 uint2 w;
-                if constexpr (QUANT)
+                if constexpr (QUANT) {
                     w = make_uint2(pack_f16x2(a[0] * vs, a[1] * vs), pack_f16x2(a[2] * vs, a[3] * vs));
-                else
+                } else {
                     w = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+                    *reinterpret_cast<uint2 *>(&ptl16[16 * t + n][16 * rb + 4 * g]) =
+                        make_uint2(bf16x2_residual(a[0], a[1], w.x), bf16x2_residual(a[2], a[3], w.y));
+                }
                 *reinterpret_cast<uint2 *>(&pt16[16 * t + n][16 * rb + 4 * g]) = w;
             }
         }
@@ -509,11 +520,16 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
                 __builtin_amdgcn_sched_barrier(0);
             }
             const int r0 = 32 * kb + tr_row;
-            uint64_t a_lo[RB], a_hi[RB];
+            // (a_lo / a_hi: tokens r0.. and r0 + 4..; al_*: the low terms)
+            uint64_t a_lo[RB], a_hi[RB], al_lo[RB], al_hi[RB];
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
                 a_lo[rb] = lds_tr16_b64(&pt16[r0][16 * rb + tr_col]);
                 a_hi[rb] = lds_tr16_b64(&pt16[r0 + 4][16 * rb + tr_col]);
+                if constexpr (!QUANT) {
+                    al_lo[rb] = lds_tr16_b64(&ptl16[r0][16 * rb + tr_col]);
+                    al_hi[rb] = lds_tr16_b64(&ptl16[r0 + 4][16 * rb + tr_col]);
+                }
             }
 #pragma unroll
             for (int blk = 0; blk < 8; ++blk) {
@@ -521,11 +537,13 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
                 const uint64_t b_hi = lds_tr16_b64(&vt[tr_row + 4][16 * blk + tr_col]);
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb) {
-                    if constexpr (!QUANT)
+                    if constexpr (!QUANT) {
+                        const bf16x8_t vb = join_bf16x8(b_lo, b_hi);
                         acc[rb][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            join_bf16x8(a_lo[rb], a_hi[rb]), join_bf16x8(b_lo, b_hi), acc[rb][blk],
-                            0, 0, 0);
-                    else
+                            join_bf16x8(al_lo[rb], al_hi[rb]), vb, acc[rb][blk], 0, 0, 0);
+                        acc[rb][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            join_bf16x8(a_lo[rb], a_hi[rb]), vb, acc[rb][blk], 0, 0, 0);
+                    } else
                         acc[rb][blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                             join_f16x8(a_lo[rb], a_hi[rb]), join_f16x8(b_lo, b_hi), acc[rb][blk],
                             0, 0, 0);
@@ -607,9 +625,12 @@ hipError_t launch_verify_kv(const DecodeParams &p_in, hipStream_t stream) {
                static_lds + (size_t)NW * (p.split_walk - 1) * STASH * sizeof(float) > max_lds)
             p.split_walk /= 2;
     }
-    // a workgroup per split and chunk: the kernel decides whether the batch
-    // walks (workgroups past the walked grid then exit at once)
-    const unsigned grid = (unsigned)((int64_t)p.batch * (p.hkv / NW) * p.splits * p.q_chunks);
+    const int64_t per_split = (int64_t)p.batch * (p.hkv / NW) * p.splits;
+    p.walk_checked = walk_checked_for(per_split * p.q_chunks, p.split_walk);
+    // checked walks: a workgroup per split and chunk, the kernel deciding
+    // (those past the walked grid then exit at once)
+    const unsigned grid = (unsigned)((p.walk_checked ? per_split : per_split / p.split_walk) *
+                                     p.q_chunks);
     const size_t stash_bytes = (size_t)NW * (p.split_walk - 1) * STASH * sizeof(float);
     hipLaunchKernelGGL((verify_kernel<KV, RB, NW>), dim3(grid), dim3(NW * 64),
                        (unsigned)stash_bytes, stream, p, p.page_table, p.seq_lens, p.cu_seqlens_q);

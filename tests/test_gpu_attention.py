@@ -426,6 +426,30 @@ def test_hip_graph_replay_matches_eager(make, kw):
     assert int(counters_view(ws).abs().sum()) == 0
 
 
+def test_large_grid_walks_whatever_the_lengths():
+    """512 ragged requests, 8 splits: the walked grid spans several rounds of
+    resident workgroups, so the producer walks without looking at the
+    lengths (the dispatcher evens out the workgroups over the rounds).
+    Against the oracle, and bit-exactly against four of the requests alone
+    (a grid too small to walk)."""
+    lens = W._gen(512, 31).integers(1, 321, size=512)
+    lens[:4] = [0, 1, 64, 320]
+    c = small_case(lens.tolist(), kv="bf16", S=8, seed=512)
+    print("[case] walked grid of several rounds, batch 512 ragged", flush=True)
+    d = DevCase(c)
+    o_ref, l_ref = oracle.case_attention(c)
+    o1, l1 = d.attention(producer="head_grouped", merge="separate")
+    compare_attention(o1, l1, o_ref, l_ref, label="batch 512 walked")
+    rows = slice(0, 4)
+    o2, l2 = spa.paged_decode_attention(d.q[rows].contiguous(), d.k, d.v,
+                                        d.page_list[rows].contiguous(), d.seq_lens[rows].contiguous(),
+                                        8, float(c.scale), kv_dtype="bf16",
+                                        producer="head_grouped", merge="separate")
+    torch.cuda.synchronize()
+    assert torch.equal(o2.view(torch.int16), o1[rows].view(torch.int16))
+    assert torch.equal(l2, l1[rows])
+
+
 @pytest.mark.parametrize("merge", ["fused", "separate"])
 def test_graph_replay_follows_walk_choice(merge):
     """One captured bf16 head-grouped call, replayed while the lengths
