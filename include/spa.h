@@ -271,15 +271,16 @@ spa_status spa_paged_decode_attention_noalloc(
  * sizes: one producer flag (SPA_DECODE_HEAD_GROUPED or SPA_DECODE_PAGE_SPLIT)
  * or'ed with one merge flag (SPA_DECODE_FUSED_MERGE or
  * SPA_DECODE_SEPARATE_MERGE).  Passing the result back as flags gives the
- * same launches.  The flags depend on batch, num_kv_heads, num_splits and
- * kv_dtype (head grouped from 512 request x kv head x split triples for
- * bf16 and 1024 for 1-byte codes, with an even num_kv_heads; merge fused
- * for up to 8 page-split or 4 head-grouped splits); page_table_stride is
- * checked.  Within the plan,
- * the splits a bf16 head-grouped workgroup walks also depend on
- * page_table_stride, the current device's compute units and, per call, on
- * seq_lens (a walk is taken only when the longest request has at most 6/5
- * of the mean number of pages).  0 for sizes
+ * same launches.  The flags depend on batch, num_kv_heads, num_splits,
+ * kv_dtype and page_table_stride (head grouped, with an even num_kv_heads,
+ * from 1024 request x kv head x split triples; for bf16 also from 256 when a
+ * split holds at most 8 pages, ceil(page_table_stride / num_splits), and
+ * from 64 when it holds at most 4; merge fused for up to 8 page-split or 4
+ * head-grouped splits).  Within the plan, the splits a bf16 head-grouped
+ * workgroup walks also depend on page_table_stride, the current device's
+ * compute units and, when the walked grid is about one round of resident
+ * workgroups, per call on seq_lens (a walk is then taken only when the
+ * longest request has at most 6/5 of the mean number of pages).  0 for sizes
  * spa_paged_decode_attention would reject as invalid or unsupported.
  */
 uint32_t spa_decode_default_flags(int32_t batch, int32_t num_kv_heads, int32_t num_splits,

@@ -89,10 +89,11 @@ struct DecodePlan {
 // up to 8 splits and head-grouped grids of up to 4; a second launch for more
 // splits, where the last arrival's merge of all of them sits on the
 // critical path of grids whose splits finish together.
-DecodePlan default_plan(int32_t batch, int32_t hkv, int32_t splits, int kv_type) {
+DecodePlan default_plan(int32_t batch, int32_t hkv, int32_t splits, int kv_type,
+                        int64_t pt_stride) {
     DecodePlan plan{};
     plan.kv_type = kv_type;
-    plan.mode = spa::default_mode(batch, hkv, splits, kv_type);
+    plan.mode = spa::default_mode(batch, hkv, splits, kv_type, pt_stride);
     const int fused_max_splits = plan.mode == spa::DecodeMode::kPageSplit ? 8 : 4;
     plan.fused = splits <= fused_max_splits && (int64_t)batch * hkv <= spa::kMaxCounterGroups;
     return plan;
@@ -130,7 +131,7 @@ spa_status decode_setup(const void *q, const void *k_pages, const void *v_pages,
     // grid = batch * kv_heads * splits workgroups must fit a 32-bit grid
     if ((int64_t)batch * num_kv_heads * num_splits > (int64_t)INT32_MAX)
         return SPA_ERR_UNSUPPORTED;
-    *plan = default_plan(batch, num_kv_heads, num_splits, kv_type_of(kv_dtype));
+    *plan = default_plan(batch, num_kv_heads, num_splits, kv_type_of(kv_dtype), page_table_stride);
     if (flags & SPA_DECODE_HEAD_GROUPED) plan->mode = spa::DecodeMode::kHeadGrouped;
     if (flags & SPA_DECODE_PAGE_SPLIT) plan->mode = spa::DecodeMode::kPageSplit;
     if (flags & SPA_DECODE_SEPARATE_MERGE) plan->fused = false;
@@ -350,7 +351,8 @@ uint32_t spa_decode_default_flags(int32_t batch, int32_t num_kv_heads, int32_t n
         page_table_stride < 1 || (int64_t)batch * num_kv_heads * num_splits > (int64_t)INT32_MAX)
         return 0u;
     if (kv_dtype != SPA_KV_BF16 && kv_dtype != SPA_KV_INT8 && kv_dtype != SPA_KV_FP8) return 0u;
-    const DecodePlan plan = default_plan(batch, num_kv_heads, num_splits, kv_type_of(kv_dtype));
+    const DecodePlan plan = default_plan(batch, num_kv_heads, num_splits, kv_type_of(kv_dtype),
+                                         page_table_stride);
     return (plan.mode == spa::DecodeMode::kHeadGrouped ? SPA_DECODE_HEAD_GROUPED
                                                        : SPA_DECODE_PAGE_SPLIT) |
            (plan.fused ? SPA_DECODE_FUSED_MERGE : SPA_DECODE_SEPARATE_MERGE);

@@ -1447,12 +1447,22 @@ constexpr int kNwHeadGrouped = 2;        // also the kv-head multiple head group
 constexpr int kNwHeadGroupedCodes = 4;
 constexpr int kNwPageSplit = 4;
 // Producer choice, from a sweep over batch 1-32 x context 1K-8K x 4/8/16
-// splits (32 query / 8 kv heads) for each KV type: head grouped from 512
-// (request, kv head, split) triples up for bf16 and from 1024 for 1-byte
-// codes, page split below (the page-split producer's keys in 64-byte
+// splits (32 query / 8 kv heads) for each KV type, equal lengths and ragged
+// batches.  1-byte codes: head grouped from 1024 (request, kv head, split)
+// triples, page split below (the page-split producer's keys in 64-byte
 // pieces read faster with the default cache policy, which moved the
-// 1-byte threshold back up from 512).
-constexpr int64_t kHeadGroupedMinWaves = 512;
+// threshold back up from 512).  bf16 (its head-grouped P.V on the matrix
+// cores): head grouped from 1024 triples, from 256 when splits hold at most
+// 8 pages and from 64 when they hold at most 4 (the pages per split bounded
+// by the page table's width); page split for small grids of long splits,
+// where its four waves per split shorten the longest request's chain
+// (ragged batch of 8 requests up to 8K, 8 splits: 30.4 against 34.8 us).
+// Over the sweep the default is within 5% of the best choice in 69 of 72
+// equal-length shapes and all 12 ragged ones (with 512 triples as the only
+// bound: 60 and 11).
+constexpr int64_t kHeadGroupedMinWaves = 1024;
+constexpr int64_t kHeadGroupedMinWavesMid = 256;     // splits of <= 8 pages
+constexpr int64_t kHeadGroupedMinWavesShort = 64;    // splits of <= 4 pages
 constexpr int64_t kHeadGroupedMinWavesQuant = 1024;
 
 template <int KV>
@@ -1488,11 +1498,16 @@ hipError_t launch_decode(const DecodeParams &p, int kv_type, DecodeMode mode, bo
                               p.splits, p.out, p.lse, stream);
 }
 
-DecodeMode default_mode(int batch, int hkv, int splits, int kv_type) {
+DecodeMode default_mode(int batch, int hkv, int splits, int kv_type, int64_t pt_stride) {
     if (hkv % kNwHeadGrouped != 0) return DecodeMode::kPageSplit;
     const int64_t waves = (int64_t)batch * hkv * splits;
-    const int64_t min_waves = kv_type == kKvBf16 ? kHeadGroupedMinWaves : kHeadGroupedMinWavesQuant;
-    return waves >= min_waves ? DecodeMode::kHeadGrouped : DecodeMode::kPageSplit;
+    if (kv_type != kKvBf16)
+        return waves >= kHeadGroupedMinWavesQuant ? DecodeMode::kHeadGrouped : DecodeMode::kPageSplit;
+    const int64_t split_pages = (pt_stride + splits - 1) / splits;
+    const bool hg = waves >= kHeadGroupedMinWaves ||
+                    (waves >= kHeadGroupedMinWavesMid && split_pages <= 8) ||
+                    (waves >= kHeadGroupedMinWavesShort && split_pages <= 4);
+    return hg ? DecodeMode::kHeadGrouped : DecodeMode::kPageSplit;
 }
 
 bool mode_supported(DecodeMode mode, int hkv) {

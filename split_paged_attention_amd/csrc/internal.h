@@ -105,7 +105,7 @@ hipError_t launch_build_metadata(const MetadataParams &p, hipStream_t stream);
 // Producer workgroup shape (same arithmetic per split, different rounding of
 // the in-workgroup combination, so one shape always uses one mode).
 enum class DecodeMode { kPageSplit, kHeadGrouped };
-DecodeMode default_mode(int batch, int hkv, int splits, int kv_type);
+DecodeMode default_mode(int batch, int hkv, int splits, int kv_type, int64_t pt_stride);
 // Splits one head-grouped workgroup walks (bf16 only; 1 for 1-byte codes),
 // and the device's LDS limit per workgroup.
 int split_walk_for(const DecodeParams &p, bool quant, int nw);

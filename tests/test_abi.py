@@ -196,7 +196,10 @@ def test_default_flags():
     assert f(32, 8, 16, "bf16", 128) == HG | SEP        # batch 32 / 8K: 4096 triples
     assert f(1, 8, 4, "bf16", 16) == PS | FUS           # batch 1 / 1K, 4 splits
     assert f(1, 8, 16, "bf16", 128) == PS | SEP         # more than 8 splits: second launch
-    assert f(8, 8, 4, "bf16", 16) == PS | FUS           # 256 triples
+    assert f(8, 8, 4, "bf16", 16) == HG | FUS           # 256 triples, 4-page splits
+    assert f(8, 8, 4, "bf16", 128) == PS | FUS          # 256 triples, 32-page splits
+    assert f(8, 8, 8, "bf16", 128) == PS | FUS          # 512 triples, 16-page splits
+    assert f(1, 8, 16, "bf16", 16) == HG | SEP          # 128 triples, 1-page splits
     assert f(16, 8, 4, "bf16", 16) == HG | FUS          # 512 triples, 4 splits
     assert f(16, 8, 8, "bf16", 16) == HG | SEP          # 1024 triples, 8 splits
     assert f(32, 8, 16, "int8", 128) == HG | SEP        # 4096 triples

@@ -381,11 +381,17 @@ def _int8_hg_case():
     return small_case(lens, kv="int8", S=4, seed=32)
 
 
+def _bf16_hg_small_case():
+    lens = W._gen(8, 23).integers(600, 1025, size=8).tolist()
+    return small_case(lens, kv="bf16", S=4, seed=8)   # 16-page table: 4-page splits
+
+
 @pytest.mark.parametrize("make,kw", [
     (lambda: config_case(3), {}),                     # default: page split, fused merge
+    (_bf16_hg_small_case, {}),                        # default: head grouped, fused merge
     (_walk_case, dict(producer="head_grouped", merge="fused")),   # fused with split walks
     (_int8_hg_case, {}),                              # default: 4-head 1-byte, fused merge
-], ids=["b8_ctx1k_default", "bf16_walks_fused", "int8_hg_fused_default"])
+], ids=["b8_ctx1k_default", "bf16_hg_small_default", "bf16_walks_fused", "int8_hg_fused_default"])
 def test_hip_graph_replay_matches_eager(make, kw):
     c = make()
     print(f"[case] HIP graph capture of the decode step {c.name} {kw}", flush=True)
