@@ -425,10 +425,9 @@ void decode_kernel(DecodeParams p,
     // Head-grouped int8 codes and bf16 run P.V on the matrix cores (see
     // below); e4m3 codes and the page-split producer on the vector ALU.
     constexpr bool MXPV = I8 && HG;
-    constexpr bool BFPV = !QUANT && HG;
+    constexpr bool BFPV = !QUANT;                        // bf16, both producers
     constexpr bool VPV = !MXPV && !BFPV;                 // vector-ALU P.V
     __shared__ uint32_t pbuf[VPV ? NW : 1][8][4][4];      // [wave][pair u][phase r][head]
-    __shared__ uint32_t pbuf_lo[VPV && !QUANT ? NW : 1][8][4][4];   // bf16: low terms
     __shared__ float sm_m[NW][4], sm_l[NW][4];
     __shared__ float sm_acc[HG ? 1 : NW][4][HG ? 1 : D];   // page split: waves' states
     // Head-grouped: the page's K rows, staged per wave: loaded as whole rows
@@ -460,6 +459,10 @@ void decode_kernel(DecodeParams p,
     // carries p to 2^-17 instead of the 2^-9 of one bf16 term, which can
     // cost 0.007 on an output of a few tokens)
     __shared__ __attribute__((aligned(16))) uint16_t ptile_lo[BFPV ? NW : 1][BFPV ? P : 1][4];
+    // bf16 page split (no key tile): half a page of values at a time, rows
+    // as the key tile's
+    constexpr int VROWB16 = 2 * D + 16;
+    __shared__ __attribute__((aligned(16))) uint8_t vtile16[BFPV && !HG ? NW : 1][BFPV && !HG ? P / 2 : 1][VROWB16];
     __shared__ __attribute__((aligned(16))) uint8_t vtile[MXPV ? NW : 1][MXPV ? P / 2 : 1][MXPV ? VROWB : 1];
     __shared__ int sm_last;
 
@@ -1002,54 +1005,81 @@ void decode_kernel(DecodeParams p,
             for (int t = 0; t < 8; ++t)
 #pragma unroll
                 for (int h = 0; h < 4; ++h) oacc[t][h] *= alpha[h];
-            // ---- this page's values into the key tile, whose rows QK^T has
-            // read (a wave's LDS operations complete in order), token-major
-            // like the keys; the registers then take the next page's values
-            uint8_t(*kt)[KROWB] = ktile[wave];
-            __asm__ volatile("" ::: "memory");
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                *reinterpret_cast<uint4 *>(&kt[4 * i + vr][16 * vc]) = vr16[i];
-            __asm__ volatile("" ::: "memory");
-            __builtin_amdgcn_sched_barrier(0);
-            load_v_half(page_next, valid_next, 0);
-            load_v_half(page_next, valid_next, 1);
-            __builtin_amdgcn_sched_barrier(0);
             // ---- O += P V on the matrix cores, 32 tokens per step.  A = P:
             // lane (i, G) takes head i % 4 at tokens 8G .. 8G + 7 (two
             // transposed reads of 4 token rows); B = V: lane (j, G) takes dim
             // 16T + j at tokens 8G .. 8G + 7.  The low terms go first.
-            const uint16_t(*kt16)[KROWB / 2] = reinterpret_cast<const uint16_t(*)[KROWB / 2]>(kt);
             const int tr_row = 8 * g + (n >> 2), tr_col = 4 * (n & 3);
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+            auto pv_step = [&](int kb, const uint16_t *vbase, int vrow0) {
+                // vbase: a token-major tile of rows of VROWB16 bytes whose row
+                // vrow0 holds token 32 kb
+                constexpr int RE = VROWB16 / 2;   // elements per row
                 const uint16_t *prh = &ptile[wave][32 * kb + 8 * g + (n >> 2)][0];
                 const uint16_t *prl = &ptile_lo[wave][32 * kb + 8 * g + (n >> 2)][0];
                 const bf16x8_t pah = join_bf16x8(lds_tr16_b64(prh), lds_tr16_b64(prh + 16));
                 const bf16x8_t pal = join_bf16x8(lds_tr16_b64(prl), lds_tr16_b64(prl + 16));
 #pragma unroll
                 for (int t = 0; t < 8; ++t) {
-                    const bf16x8_t vb =
-                        join_bf16x8(lds_tr16_b64(&kt16[32 * kb + tr_row][16 * t + tr_col]),
-                                    lds_tr16_b64(&kt16[32 * kb + tr_row + 4][16 * t + tr_col]));
+                    const uint16_t *vr0 = vbase + (vrow0 + tr_row) * RE + 16 * t + tr_col;
+                    const bf16x8_t vb = join_bf16x8(lds_tr16_b64(vr0), lds_tr16_b64(vr0 + 4 * RE));
                     oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pal, vb, oacc[t], 0, 0, 0);
                     oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pah, vb, oacc[t], 0, 0, 0);
                 }
-            }
-            // the next page's keys overwrite the tile only after these reads
-            __asm__ volatile("" ::: "memory");
-            if (pg + 1 == split_end) {
-                finish_split_mx(jcur, pg + 1 < pg1);
-                ++jcur;
-                split_end = min(split_end + pps, pages);
+            };
+            if constexpr (HG) {
+                // ---- this page's values into the key tile, whose rows QK^T
+                // has read (a wave's LDS operations complete in order),
+                // token-major like the keys; the registers then take the next
+                // page's values
+                static_assert(KROWB == VROWB16, "values staged in the key tile's rows");
+                uint8_t(*kt)[KROWB] = ktile[wave];
+                __asm__ volatile("" ::: "memory");
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    *reinterpret_cast<uint4 *>(&kt[4 * i + vr][16 * vc]) = vr16[i];
+                __asm__ volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+                load_v_half(page_next, valid_next, 0);
+                load_v_half(page_next, valid_next, 1);
+                __builtin_amdgcn_sched_barrier(0);
+                const uint16_t *vbase = reinterpret_cast<const uint16_t *>(&kt[0][0]);
+                pv_step(0, vbase, 0);
+                pv_step(1, vbase, 32);
+                // the next page's keys overwrite the tile only after these reads
+                __asm__ volatile("" ::: "memory");
+                if (pg + 1 == split_end) {
+                    finish_split_mx(jcur, pg + 1 < pg1);
+                    ++jcur;
+                    split_end = min(split_end + pps, pages);
+                }
+            } else {
+                // ---- page split: each half page of values into the wave's
+                // half-page tile in turn, its registers then taking the next
+                // page's half
+                uint8_t(*vt)[VROWB16] = vtile16[wave];
+                const uint16_t *vbase = reinterpret_cast<const uint16_t *>(&vt[0][0]);
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    __asm__ volatile("" ::: "memory");
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        *reinterpret_cast<uint4 *>(&vt[4 * i + vr][16 * vc]) = vr16[8 * kb + i];
+                    __asm__ volatile("" ::: "memory");
+                    __builtin_amdgcn_sched_barrier(0);
+                    load_v_half(page_next, valid_next, kb);
+                    __builtin_amdgcn_sched_barrier(0);
+                    pv_step(kb, vbase, 0);
+                    // the second half overwrites the tile only after these reads
+                    __asm__ volatile("" ::: "memory");
+                }
             }
             continue;
         }
 
-        // ---- probabilities for P.V: pair (token 32q + n, token 32q + 16 + n),
-        // stored by row 0 of the wave as pbuf[pair u][phase r][h]
-        // with u = 4q + n/4, r = n % 4 (bf16 hi and lo terms, or f16 with the
-        // value scale folded in for 1-byte codes).
+        // ---- vector-ALU P.V (1-byte codes: e4m3 head grouped, both codes
+        // page split).  Probabilities: pair (token 32q + n, token 32q + 16 +
+        // n), stored by row 0 of the wave as pbuf[pair u][phase r][h] with
+        // u = 4q + n/4, r = n % 4, in f16 with the value scale folded in.
         {   // every row g holds the same values, so all lanes may store
 #pragma unroll
             for (int qq = 0; qq < 2; ++qq) {
@@ -1057,26 +1087,15 @@ void decode_kernel(DecodeParams p,
                 float a0 = pv[2 * qq][0], a1 = pv[2 * qq][1], a2 = pv[2 * qq][2], a3 = pv[2 * qq][3];
                 float b0 = pv[2 * qq + 1][0], b1 = pv[2 * qq + 1][1], b2 = pv[2 * qq + 1][2],
                       b3 = pv[2 * qq + 1][3];
-                if constexpr (QUANT) {
-                    const float va = lane_value(vsc_tok, 32 * qq + n);
-                    const float vb = lane_value(vsc_tok, 32 * qq + 16 + n);
-                    a0 *= va; a1 *= va; a2 *= va; a3 *= va;
-                    b0 *= vb; b1 *= vb; b2 *= vb; b3 *= vb;
-                    // f16 keeps 11 significant bits
-                    w.x = pack_f16x2(a0, b0);
-                    w.y = pack_f16x2(a1, b1);
-                    w.z = pack_f16x2(a2, b2);
-                    w.w = pack_f16x2(a3, b3);
-                } else {
-                    // two bf16 terms per probability, as on the matrix cores
-                    w.x = pack_bf16x2(a0, b0);
-                    w.y = pack_bf16x2(a1, b1);
-                    w.z = pack_bf16x2(a2, b2);
-                    w.w = pack_bf16x2(a3, b3);
-                    const uint4 wl = make_uint4(bf16x2_residual(a0, b0, w.x), bf16x2_residual(a1, b1, w.y),
-                                                bf16x2_residual(a2, b2, w.z), bf16x2_residual(a3, b3, w.w));
-                    *reinterpret_cast<uint4 *>(&pbuf_lo[wave][4 * qq + (n >> 2)][n & 3][0]) = wl;
-                }
+                const float va = lane_value(vsc_tok, 32 * qq + n);
+                const float vb = lane_value(vsc_tok, 32 * qq + 16 + n);
+                a0 *= va; a1 *= va; a2 *= va; a3 *= va;
+                b0 *= vb; b1 *= vb; b2 *= vb; b3 *= vb;
+                // f16 keeps 11 significant bits
+                w.x = pack_f16x2(a0, b0);
+                w.y = pack_f16x2(a1, b1);
+                w.z = pack_f16x2(a2, b2);
+                w.w = pack_f16x2(a3, b3);
                 *reinterpret_cast<uint4 *>(&pbuf[wave][4 * qq + (n >> 2)][n & 3][0]) = w;
             }
         }
@@ -1102,22 +1121,7 @@ void decode_kernel(DecodeParams p,
             const int ia = u < 4 ? u : u + 4;       // token 4*ia + r
             const int ib = ia + 4;                  // token 4*ia + r + 16
             const uint32_t ph[4] = {pk.x, pk.y, pk.z, pk.w};
-            if constexpr (!QUANT) {
-                const uint4 pkl = *reinterpret_cast<const uint4 *>(&pbuf_lo[wave][u][vr][0]);
-                const uint32_t pl[4] = {pkl.x, pkl.y, pkl.z, pkl.w};
-                const uint32_t wa[4] = {vr16[ia].x, vr16[ia].y, vr16[ia].z, vr16[ia].w};
-                const uint32_t wb[4] = {vr16[ib].x, vr16[ib].y, vr16[ib].z, vr16[ib].w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t lo = __builtin_amdgcn_perm(wb[e], wa[e], 0x05040100u);
-                    const uint32_t hi = __builtin_amdgcn_perm(wb[e], wa[e], 0x07060302u);
-#pragma unroll
-                    for (int h = 0; h < 4; ++h) {
-                        acc[h][2 * e] = dot2(ph[h], lo, dot2(pl[h], lo, acc[h][2 * e]));
-                        acc[h][2 * e + 1] = dot2(ph[h], hi, dot2(pl[h], hi, acc[h][2 * e + 1]));
-                    }
-                }
-            } else {
+            {
                 // codes are finite (rows past the context read as 0) and
                 // masked tokens have probability 0, so no masking is needed;
                 // for int8, psum tracks sum(p') for the 1152 bias.
@@ -1225,19 +1229,31 @@ void decode_kernel(DecodeParams p,
             }
         }
     } else {
-        reduce_state();
+        if constexpr (BFPV) {
+            // matrix-core layout: lane (j, g) holds head g at dims 16T + j;
+            // the softmax sums are per lane over tokens 16t + n, the same in
+            // every row of 16 lanes
+#pragma unroll
+            for (int h = 0; h < 4; ++h) lpart[h] = row_sum16(lpart[h]);
+            const int jl = lane & 15;
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                sm_acc[wave][g][16 * t + jl] = pick4(oacc[t][0], oacc[t][1], oacc[t][2], oacc[t][3], g);
+        } else {
+            reduce_state();
+            if (lane < 16) {
+#pragma unroll
+                for (int h = 0; h < 4; ++h)
+#pragma unroll
+                    for (int d = 0; d < 8; ++d) sm_acc[wave][h][8 * vc + d] = acc[h][d];
+            }
+        }
         if (lane == 0) {
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
                 sm_m[wave][h] = m[h];
                 sm_l[wave][h] = lpart[h];
             }
-        }
-        if (lane < 16) {
-#pragma unroll
-            for (int h = 0; h < 4; ++h)
-#pragma unroll
-                for (int d = 0; d < 8; ++d) sm_acc[wave][h][8 * vc + d] = acc[h][d];
         }
         __syncthreads();
 
