@@ -275,7 +275,7 @@ spa_status spa_paged_decode_attention_noalloc(
  * kv_dtype and page_table_stride (head grouped, with an even num_kv_heads,
  * from 1024 request x kv head x split triples; for bf16 also from 256 when a
  * split holds at most 8 pages, ceil(page_table_stride / num_splits), and
- * from 64 when it holds at most 4; merge fused for up to 8 page-split or 4
+ * from 128 when it holds at most 2; merge fused for up to 8 page-split or 4
  * head-grouped splits).  Within the plan, the splits a bf16 head-grouped
  * workgroup walks also depend on page_table_stride, the current device's
  * compute units and, when the walked grid is about one round of resident

@@ -1467,18 +1467,17 @@ constexpr int kNwPageSplit = 4;
 // batches.  1-byte codes: head grouped from 1024 (request, kv head, split)
 // triples, page split below (the page-split producer's keys in 64-byte
 // pieces read faster with the default cache policy, which moved the
-// threshold back up from 512).  bf16 (its head-grouped P.V on the matrix
-// cores): head grouped from 1024 triples, from 256 when splits hold at most
-// 8 pages and from 64 when they hold at most 4 (the pages per split bounded
-// by the page table's width); page split for small grids of long splits,
-// where its four waves per split shorten the longest request's chain
-// (ragged batch of 8 requests up to 8K, 8 splits: 30.4 against 34.8 us).
-// Over the sweep the default is within 5% of the best choice in 69 of 72
-// equal-length shapes and all 12 ragged ones (with 512 triples as the only
-// bound: 60 and 11).
+// threshold back up from 512).  bf16: head grouped from 1024 triples, from
+// 256 when splits hold at most 8 pages and from 128 when they hold at most
+// 2 (the pages per split bounded by the page table's width); page split
+// for small grids of long splits, where its four waves per split shorten
+// the longest request's chain (ragged batch of 8 requests up to 8K, 8
+// splits: 30.4 against 34.8 us).  Over the sweep the default is within 5%
+// of the best choice in 68 of 72 equal-length shapes and 10 of 12 ragged
+// ones (with 512 triples as the only bound: 67 and 9).
 constexpr int64_t kHeadGroupedMinWaves = 1024;
 constexpr int64_t kHeadGroupedMinWavesMid = 256;     // splits of <= 8 pages
-constexpr int64_t kHeadGroupedMinWavesShort = 64;    // splits of <= 4 pages
+constexpr int64_t kHeadGroupedMinWavesShort = 128;   // splits of <= 2 pages
 constexpr int64_t kHeadGroupedMinWavesQuant = 1024;
 
 template <int KV>
@@ -1522,7 +1521,7 @@ DecodeMode default_mode(int batch, int hkv, int splits, int kv_type, int64_t pt_
     const int64_t split_pages = (pt_stride + splits - 1) / splits;
     const bool hg = waves >= kHeadGroupedMinWaves ||
                     (waves >= kHeadGroupedMinWavesMid && split_pages <= 8) ||
-                    (waves >= kHeadGroupedMinWavesShort && split_pages <= 4);
+                    (waves >= kHeadGroupedMinWavesShort && split_pages <= 2);
     return hg ? DecodeMode::kHeadGrouped : DecodeMode::kPageSplit;
 }
 

@@ -200,6 +200,7 @@ def test_default_flags():
     assert f(8, 8, 4, "bf16", 128) == PS | FUS          # 256 triples, 32-page splits
     assert f(8, 8, 8, "bf16", 128) == PS | FUS          # 512 triples, 16-page splits
     assert f(1, 8, 16, "bf16", 16) == HG | SEP          # 128 triples, 1-page splits
+    assert f(1, 8, 8, "bf16", 32) == PS | FUS           # 64 triples, 4-page splits
     assert f(16, 8, 4, "bf16", 16) == HG | FUS          # 512 triples, 4 splits
     assert f(16, 8, 8, "bf16", 16) == HG | SEP          # 1024 triples, 8 splits
     assert f(32, 8, 16, "int8", 128) == HG | SEP        # 4096 triples

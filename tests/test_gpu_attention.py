@@ -383,7 +383,7 @@ def _int8_hg_case():
 
 def _bf16_hg_small_case():
     lens = W._gen(8, 23).integers(600, 1025, size=8).tolist()
-    return small_case(lens, kv="bf16", S=4, seed=8)   # 16-page table: 4-page splits
+    return small_case(lens, kv="bf16", S=4, seed=8)   # 256 triples, 4-page splits
 
 
 @pytest.mark.parametrize("make,kw", [
