@@ -249,6 +249,22 @@ def test_verify_split_walk(S):
     assert torch.equal(lse2[keep], lse[keep])
 
 
+def test_verify_large_grid_walks_whatever_the_lengths():
+    """1024 ragged bf16 requests with 1-4 query rows, 8 splits: the walked
+    grid spans several rounds of resident workgroups, so the kernel walks
+    without looking at the lengths.  Against the oracle on every output."""
+    rng = W._gen(1024, 41)
+    lens = rng.integers(4, 321, size=1024)
+    lens[:3] = [4, 64, 320]
+    qlens = np.minimum(rng.integers(1, 5, size=1024), lens).tolist()
+    c = small_case(lens.tolist(), kv="bf16", S=8, seed=1024)
+    q_rows, cu = W.verify_queries(c, qlens)
+    print("[case] verify walked grid of several rounds, batch 1024 ragged", flush=True)
+    out, lse = run_verify(c, q_rows, cu)
+    o_ref, l_ref = oracle_verify(c, q_rows, cu)
+    compare_attention(out, lse, o_ref, l_ref, label="verify batch 1024 walked")
+
+
 def test_verify_graph_replay_matches_eager():
     """Captured once, replayed with the query rows changed in place: every
     replay equals an eager call on the same inputs, bit for bit."""
