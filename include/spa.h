@@ -276,8 +276,9 @@ spa_status spa_paged_decode_attention_noalloc(
  * from 1024 request x kv head x split triples; for bf16 also from 256 when a
  * split holds at most 8 pages, ceil(page_table_stride / num_splits), and
  * from 128 when it holds at most 2; merge fused for up to 8 page-split or 4
- * head-grouped splits).  Within the plan, the splits a bf16 head-grouped
- * workgroup walks also depend on page_table_stride, the current device's
+ * head-grouped splits).  Within the plan, the splits a bf16 or fp8
+ * head-grouped workgroup walks (fp8: at most 2) also depend on
+ * page_table_stride, the current device's
  * compute units and, when the walked grid is about one round of resident
  * workgroups, per call on seq_lens (a walk is then taken only when the
  * longest request has at most 6/5 of the mean number of pages).  0 for sizes

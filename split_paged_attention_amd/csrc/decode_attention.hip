@@ -268,8 +268,8 @@ void decode_kernel(DecodeParams p,
     // Lane i holds request i's length (the walk choice and, for batches of
     // up to 64, the request ranking below read it).
     const int Li = lane < p.batch ? seq_lens[lane] : INT32_MIN;
-    // A head-grouped bf16 workgroup may walk `walk` consecutive splits (S a
-    // multiple of it), one page pipeline across the split boundaries, the
+    // A head-grouped bf16 or e4m3 workgroup may walk `walk` consecutive
+    // splits (S a multiple of it), one page pipeline across the split boundaries, the
     // states of all but its last split kept in LDS until the walk ends: grids
     // larger than the GPU's resident workgroups then run in one round, and
     // the later splits skip the workgroup start (request ranking, page-id
@@ -286,7 +286,7 @@ void decode_kernel(DecodeParams p,
     // walked grid of several rounds always walks (walk_checked = 0, grid
     // cut): the dispatcher evens out the workgroups' lengths.
     int walk = 1;
-    if constexpr (HG && !QUANT) {
+    if constexpr (HG && !I8) {
         if (p.split_walk > 1 &&
             (!p.walk_checked || pages_balanced(seq_lens, p.batch, Li, p.pt_stride * P, P, lane)))
             walk = p.split_walk;
@@ -1155,12 +1155,30 @@ void decode_kernel(DecodeParams p,
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (QUANT) vsc_tok = vsc_next * (I8 ? 1.f : kF8ValueScale);
         if constexpr (HG) {
-            // (the vector-ALU head-grouped producer serves e4m3 codes, which
-            // walk one split, so its split ends where the workgroup's does)
             if (pg + 1 == split_end) {
-                // split jcur complete: write its state, start the next one
+                // split jcur complete: write its state (a split before the
+                // walk's last goes to the LDS stash, written out after the
+                // loop), start the next one
                 reduce_state();
-                {
+                if (pg + 1 < pg1) {
+                    float *st = stash + (wave * (walk - 1) + nstash) * kStashFloats;
+                    float v8[8];
+#pragma unroll
+                    for (int d = 0; d < 8; ++d)
+                        v8[d] = vr == 0 ? acc[0][d] : vr == 1 ? acc[1][d] : vr == 2 ? acc[2][d] : acc[3][d];
+                    *reinterpret_cast<float4 *>(st + vr * D + 8 * vc) =
+                        make_float4(v8[0], v8[1], v8[2], v8[3]);
+                    *reinterpret_cast<float4 *>(st + vr * D + 8 * vc + 4) =
+                        make_float4(v8[4], v8[5], v8[6], v8[7]);
+                    if (lane == 0) {
+#pragma unroll
+                        for (int h = 0; h < 4; ++h) {
+                            st[4 * D + h] = m[h];
+                            st[4 * D + 4 + h] = lpart[h];
+                        }
+                    }
+                    ++nstash;
+                } else {
                     const int jw = jcur;
                     // One wave = one kv head: write its split state straight from
                     // registers.  After the butterfly every lane holds the reduced sums
@@ -1359,7 +1377,11 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t *__restrict__ p
 template <int KV, int NW, bool HG>
 hipError_t launch_nw(const DecodeParams &p_in, bool fused, hipStream_t stream) {
     DecodeParams p = p_in;
-    p.split_walk = HG ? split_walk_for(p, KV != 0, NW) : 1;
+    p.split_walk = HG ? split_walk_for(p, KV == kKvInt8, NW) : 1;
+    // e4m3 codes walk at most 2 splits: the stash of 2 keeps 3 workgroups
+    // per CU (batch 32 / 8K producer 94.8 -> 92.4 us; a ragged batch, which
+    // does not walk, 1% slower for the length check)
+    if (KV == kKvFp8 && p.split_walk > 2) p.split_walk = 2;
     if (p.split_walk > 1) {
         // the stash must fit beside the kernel's static LDS
         auto lds_of = [](const void *f) {
@@ -1422,9 +1444,10 @@ size_t max_lds_per_block() {
 // workgroup per CU (batch 32 / 8K / 16 splits: 187 us with one split per
 // workgroup, 168 us walking 8); shorter splits stop at one round, their
 // boundaries costing more than the longer streams save.  1-byte codes walk
-// one split: their waves move half the bytes per page and lose with fewer
-// of them (a ragged fp8 batch 21% slower walking 4; equal lengths at most
-// 4% faster).
+// one split (int8) or at most 2 (e4m3, see launch_nw): their waves move
+// half the bytes per page and lose with fewer of them (fp8 walking 4: a
+// ragged batch 21% slower, its stash costing occupancy; equal lengths at
+// most 4% faster).
 constexpr int kMaxSplitWalk = 8;
 constexpr int kLongSplitPages = 4;
 // A walked grid of at least kWalkRounds rounds of kWalkRoundWgsPerCu

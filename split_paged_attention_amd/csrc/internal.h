@@ -48,7 +48,7 @@ struct DecodeParams {
     int64_t pt_stride;
     const int32_t *seq_lens;   // [B]
     int32_t batch, hq, hkv, splits;
-    int32_t split_walk;        // head-grouped bf16: splits per workgroup (divides splits)
+    int32_t split_walk;        // head-grouped bf16 / e4m3: splits per workgroup (divides splits)
     int32_t walk_checked;      // 1: walk only if the batch's page counts are balanced (grid
                                // of a workgroup per split); 0: always (grid cut to match)
     int32_t num_pages;         // pool size: page ids outside [0, num_pages) load nothing

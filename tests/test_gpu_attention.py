@@ -526,9 +526,10 @@ def test_large_ragged_batches(batch, producer, kv):
     compare_attention(out, lse, o_ref, l_ref, label=f"batch {batch} {kv} {producer}")
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
 @pytest.mark.parametrize("S", [16, 8])
-def test_split_walk(S):
-    """bf16 head-grouped grids large enough that a workgroup walks several
+def test_split_walk(S, kv):
+    """bf16 and e4m3 head-grouped grids large enough that a workgroup walks several
     consecutive splits (states of all but the last kept in LDS until the
     workgroup ends), on a batch balanced enough to walk: empty and one-token
     requests, exact page multiples and splits past the context inside a
@@ -539,12 +540,12 @@ def test_split_walk(S):
     cutting other requests to one token, and four requests alone (a grid
     too small to walk)."""
     lens = balanced_walk_lens(64, 7)
-    c = small_case(lens.tolist(), kv="bf16", S=S, seed=64 + S)
-    print(f"[case] split walk S={S} batch 64 balanced", flush=True)
+    c = small_case(lens.tolist(), kv=kv, S=S, seed=64 + S)
+    print(f"[case] split walk S={S} {kv} batch 64 balanced", flush=True)
     d = DevCase(c)
     o_ref, l_ref = oracle.case_attention(c)
     o1, l1 = d.attention(producer="head_grouped", merge="separate")
-    compare_attention(o1, l1, o_ref, l_ref, label=f"walk S={S}")
+    compare_attention(o1, l1, o_ref, l_ref, label=f"walk S={S} {kv}")
     o2, l2 = d.attention(producer="head_grouped", merge="fused")
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
@@ -555,7 +556,8 @@ def test_split_walk(S):
     keep = list(range(8)) + list(range(40, 64))
     for merge in ("separate", "fused"):
         o3, l3 = spa.paged_decode_attention(d.q, d.k, d.v, d.page_list, sl, S, float(c.scale),
-                                            kv_dtype="bf16", producer="head_grouped", merge=merge)
+                                            kv_dtype=kv, k_scales=d.ks, v_scales=d.vs,
+                                            producer="head_grouped", merge=merge)
         torch.cuda.synchronize()
         assert torch.equal(o3[keep].view(torch.int16), o1[keep].view(torch.int16)), merge
         assert torch.equal(l3[keep], l1[keep]), merge
@@ -564,8 +566,8 @@ def test_split_walk(S):
     rows = slice(4, 8)
     o3, l3 = spa.paged_decode_attention(d.q[rows].contiguous(), d.k, d.v,
                                         d.page_list[rows].contiguous(), d.seq_lens[rows].contiguous(),
-                                        S, float(c.scale), kv_dtype="bf16",
-                                        producer="head_grouped", merge="separate")
+                                        S, float(c.scale), kv_dtype=kv, k_scales=d.ks,
+                                        v_scales=d.vs, producer="head_grouped", merge="separate")
     torch.cuda.synchronize()
     assert torch.equal(o3.view(torch.int16), o1[rows].view(torch.int16))
     assert torch.equal(l3, l1[rows])
