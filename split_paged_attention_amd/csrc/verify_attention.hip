@@ -91,8 +91,8 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
     // Lane i holds request i's length (the walk choice and, for batches of
     // up to 64, the request ranking below read it).
     const int Li = lane < p.batch ? seq_lens[lane] : INT32_MIN;
-    // bf16: a workgroup may walk `walk` consecutive splits (S a multiple of
-    // it) with one page pipeline, as the one-token decode does: the states
+    // bf16 and e4m3: a workgroup may walk `walk` consecutive splits (S a
+    // multiple of it) with one page pipeline, as the one-token decode does: the states
     // of all but the last wait in dynamic LDS until the workgroup ends, each
     // split's arithmetic unchanged.  As there, a walked grid of about one
     // round walks only a batch whose requests have about the same number of
@@ -100,7 +100,7 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
     // chunk, and when the batch walks, those past the walked part of each
     // chunk exit at once.
     int walk = 1;
-    if constexpr (!QUANT) {
+    if constexpr (!I8) {
         if (p.split_walk > 1 &&
             (!p.walk_checked || pages_balanced(seq_lens, p.batch, Li, p.pt_stride * P, P, lane)))
             walk = p.split_walk;
@@ -552,7 +552,7 @@ void verify_kernel(DecodeParams p, const int32_t *__restrict__ page_table,
         }
         // the next page's V overwrites the tile only after these reads
         __asm__ volatile("" ::: "memory");
-        if (!QUANT && pg + 1 == split_end && pg + 1 < pg1) {
+        if (!I8 && pg + 1 == split_end && pg + 1 < pg1) {
             // split jcur complete and not this workgroup's last: its state
             // into the LDS stash, then start the next one
             float *st = vstash + (wave * (walk - 1) + nstash) * STASH;
@@ -610,7 +610,11 @@ template <int KV, int RB, int NW>
 hipError_t launch_verify_kv(const DecodeParams &p_in, hipStream_t stream) {
     constexpr int STASH = verify_stash_floats<RB>();
     DecodeParams p = p_in;
-    p.split_walk = split_walk_for(p, KV != 0, NW);
+    p.split_walk = split_walk_for(p, KV == kKvInt8, NW);
+    // e4m3 codes walk at most 2 splits, whose stash keeps 2 workgroups per
+    // CU (batch 32 / 8K, 4 tokens: 110.5 -> 108.4 us per call; int8 codes,
+    // walking too, cost the ragged batch 2%)
+    if (KV == kKvFp8 && p.split_walk > 2) p.split_walk = 2;
     if (p.split_walk > 1) {
         // the stash must fit beside the kernel's static LDS
         static const size_t static_lds = [] {

@@ -213,11 +213,12 @@ def test_verify_large_batches(batch, kv):
     compare_attention(out, lse, o_ref, l_ref, label=f"verify batch {batch} {kv}")
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
 @pytest.mark.parametrize("S", [16, 8])
-def test_verify_split_walk(S):
-    """bf16 grids large enough that a workgroup walks several consecutive
-    splits (states of all but the last held in LDS until the workgroup
-    ends), on 64 requests balanced enough to walk, with 0-4 query rows, an
+def test_verify_split_walk(S, kv):
+    """bf16 and e4m3 grids large enough that a workgroup walks several
+    consecutive splits (states of all but the last held in LDS until the
+    workgroup ends), on 64 requests balanced enough to walk, with 0-4 query rows, an
     empty context, exact page multiples and splits past the context inside
     a walk; then the same queries over a ragged batch (other requests cut
     short), which takes one split per workgroup: the rows of the requests
@@ -228,19 +229,20 @@ def test_verify_split_walk(S):
     qlens = rng.integers(0, 5, size=64)
     qlens[:4] = [4, 0, 1, 4]
     qlens = np.minimum(qlens, lens).tolist()
-    c = small_case(lens.tolist(), kv="bf16", S=S, seed=80 + S)
+    c = small_case(lens.tolist(), kv=kv, S=S, seed=80 + S)
     q_rows, cu = W.verify_queries(c, qlens)
-    print(f"[case] verify split walk S={S} batch 64 balanced", flush=True)
+    print(f"[case] verify split walk S={S} {kv} batch 64 balanced", flush=True)
     out, lse = run_verify(c, q_rows, cu)
     o_ref, l_ref = oracle_verify(c, q_rows, cu)
-    compare_attention(out, lse, o_ref, l_ref, label=f"verify walk S={S}")
+    compare_attention(out, lse, o_ref, l_ref, label=f"verify walk S={S} {kv}")
     ragged = lens.copy()
     ragged[8:40] = np.maximum(np.asarray(qlens[8:40]), 1)
     assert not walks_balanced(ragged)
     d = DevCase(c)
     out2, lse2 = spa.paged_verify_attention(
         bf16_dev(q_rows), d.k, d.v, d.page_list, torch.tensor(ragged, dtype=torch.int32).cuda(),
-        torch.from_numpy(cu).cuda(), S, float(c.scale), max_q_len=4, kv_dtype="bf16")
+        torch.from_numpy(cu).cuda(), S, float(c.scale), max_q_len=4, kv_dtype=kv,
+        k_scales=d.ks, v_scales=d.vs)
     torch.cuda.synchronize()
     cu_h = np.asarray(cu)
     keep = np.concatenate([np.arange(cu_h[b], cu_h[b + 1]) for b in list(range(8)) + list(range(40, 64))])
