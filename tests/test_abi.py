@@ -211,6 +211,19 @@ def test_default_flags():
     assert f(8, 8, 4, "fp8", 128) == PS | FUS           # 256 triples
     assert f(2, 8, 16, "int8", 16) == PS | SEP          # 256 triples, 16 splits
     assert f(32, 3, 16, "bf16", 128) == PS | SEP        # odd kv heads: page split only
+    # the producer rule at its edges (triples = batch x kv heads x splits;
+    # split pages = ceil(page-table stride / splits))
+    prod = lambda *a: f(*a) & (HG | PS)
+    assert prod(16, 8, 1, "bf16", 2) == HG              # 128 triples, 2-page splits
+    assert prod(15, 8, 1, "bf16", 2) == PS              # 120 triples
+    assert prod(16, 8, 1, "bf16", 3) == PS              # 128 triples, 3-page splits
+    assert prod(4, 8, 8, "bf16", 64) == HG              # 256 triples, 8-page splits
+    assert prod(4, 8, 8, "bf16", 65) == PS              # 256 triples, 9-page splits
+    assert prod(31, 8, 1, "bf16", 8) == PS              # 248 triples
+    assert prod(128, 8, 1, "bf16", 4096) == HG          # 1024 triples, any split length
+    assert prod(127, 8, 1, "bf16", 4096) == PS          # 1016 triples, long splits
+    assert prod(128, 8, 1, "int8", 4096) == HG          # 1-byte codes: 1024 triples only
+    assert prod(127, 8, 1, "fp8", 1) == PS              # 1016 triples, even 1-page splits
     # every result is exactly one producer and one merge flag
     for args in [(1, 8, 1, "bf16", 1), (64, 8, 8, "int8", 32), (4, 2, 1024, "fp8", 128)]:
         v = f(*args)
